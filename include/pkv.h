@@ -1,0 +1,197 @@
+/*
+ * pkv.h -- C ABI of libpkv.so: paged KV-cache decode attention on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What is computed comes from three web pages on paged KV caches:
+ *  [ttlab]  "Basics of LLM Inference and vLLM Internals: KV Cache,
+ *           PagedAttention, and Scheduler" -- section 2 (sizing formula,
+ *           MQA/GQA, fp8 KV) and section 4 (16-token blocks, per-request
+ *           block table, physical block pool, shared prefix blocks,
+ *           reserved null block 0).
+ *  [redhat] drpranayjha, "How PagedAttention pages the KV cache" (fixed
+ *           16-token blocks, block table to non-adjacent physical blocks,
+ *           waste only in the last block, shared prefixes).
+ *  [tarun]  tarundecipher, "The Memory Trick Behind Fast LLM Serving" --
+ *           "PagedAttention changes the shape of the problem" and "Batching
+ *           does not merge the conversations" (a flattened batch whose
+ *           metadata keeps each sequence's context private).
+ *
+ * Conventions (all entry points)
+ *  - Every function returns an int status: PKV_OK or a negative PKV_ERR_*.
+ *    pkv_status_string() names it.
+ *  - All buffers are caller-owned, contiguous, row-major device memory
+ *    unless a parameter says "host". The library allocates nothing, keeps no
+ *    state between calls and is safe to call from several host threads.
+ *  - Work is enqueued on the given HIP stream (NULL = the null stream) and
+ *    never synchronised: results are visible after the stream reaches the
+ *    point of the call.
+ *  - Argument errors that the host can see (null pointers, sizes, dtypes)
+ *    return before any HIP call; launch failures return PKV_ERR_HIP.
+ *  - Values in device memory (block ids, slots, lengths) are not read by the
+ *    host. Out-of-range ones never cause an out-of-bounds access: the
+ *    kernels skip such slots and turn such sequences into NaN rows, as
+ *    documented per call.
+ *
+ * KV cache layout (one tensor each for K and V, same shape):
+ *     cache[num_blocks][num_kv_heads][16][head_dim]
+ * element (blk, g, off, j) at ((blk * num_kv_heads + g) * 16 + off) * head_dim
+ * + j. One (block, KV head) tile is 16 * head_dim elements, contiguous.
+ * Token position t of a sequence lives in physical block
+ * block_tables[s][t / 16], row t % 16 ([ttlab] section 4: logical block ->
+ * physical block through the request's block table). A slot is the flat row
+ * index phys_block * 16 + row.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same definition as HIP's own, so the header needs no HIP include. */
+typedef struct ihipStream_t *hipStream_t;
+
+/* Status codes. */
+#define PKV_OK 0
+#define PKV_ERR_INVALID_ARG (-1) /* null pointer, non-positive size, bad ratio */
+#define PKV_ERR_UNSUPPORTED (-2) /* valid but not built: dtype pair, head_dim, group */
+#define PKV_ERR_WORKSPACE (-3)   /* workspace missing or smaller than required */
+#define PKV_ERR_HIP (-4)         /* a HIP launch reported an error */
+
+/* Element types. PKV_FP8_E4M3 is OCP E4M3FN: 1 sign, 4 exponent bits
+ * (bias 7), 3 mantissa bits, no infinities, NaN = 0x7F / 0xFF, largest
+ * finite 448 ([ttlab] sections 2 and 7: an fp8 KV cache, b = 1). An fp8
+ * element's value is code * scale with one float scale per tensor. */
+typedef enum {
+    PKV_F32 = 0,
+    PKV_F16 = 1,
+    PKV_BF16 = 2,
+    PKV_FP8_E4M3 = 3
+} pkv_dtype;
+
+/* The tokens of one physical block ([ttlab] section 4, [redhat]). The only
+ * block size this library accepts. */
+#define PKV_BLOCK_SIZE 16
+
+/* Describes both k_cache and v_cache (see the layout above).
+ *  num_blocks    physical blocks in the pool (> 0)
+ *  block_size    must be PKV_BLOCK_SIZE
+ *  num_kv_heads  H_kv (> 0)
+ *  head_dim      d: 64 or 128
+ *  dtype         element type of both caches
+ *  k_scale, v_scale  per-tensor scales for PKV_FP8_E4M3 (ignored otherwise) */
+typedef struct {
+    int32_t num_blocks;
+    int32_t block_size;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t dtype; /* a pkv_dtype */
+    float k_scale;
+    float v_scale;
+} pkv_cache_desc;
+
+/* Text for a status code (static storage, never NULL). */
+const char *pkv_status_string(int status);
+
+/* KV bytes per token over the whole model: 2 (K and V) * num_layers *
+ * num_kv_heads * head_dim * element bytes ([ttlab] section 2, the sizing
+ * formula; [redhat] "How PagedAttention pages the KV cache", the 40-layer
+ * example). Returns 0 for a non-positive size or an unknown dtype. */
+size_t pkv_kv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t dtype);
+
+/* Bytes of ONE cache tensor (K or V) described by *cache:
+ * num_blocks * num_kv_heads * 16 * head_dim * element bytes. 0 if invalid. */
+size_t pkv_cache_tensor_bytes(const pkv_cache_desc *cache);
+
+/* Slot-mapped append: write each new token's K and V rows into its block.
+ * ([ttlab] section 4: physical blocks are filled one token row at a time as
+ * a request grows; the block-table figure shows a last block 6/16 full.)
+ *
+ *  k, v          [num_tokens][num_kv_heads][head_dim] in kv_dtype (device)
+ *  kv_dtype      must equal cache->dtype: the rows are copied byte for byte
+ *  slot_mapping  int64 [num_tokens] (device). Token i goes to block
+ *                slot / 16, row slot % 16, for every KV head. A negative
+ *                slot skips the token; a slot >= num_blocks * 16 is also
+ *                skipped (precondition violation, never written).
+ *  num_tokens    >= 0 (0 is a no-op that still validates)
+ *  k_cache, v_cache  the pool tensors (device), updated in place
+ * Two tokens with the same slot in one call race (precondition: distinct).
+ * Errors: INVALID_ARG (null pointer with num_tokens > 0, bad desc),
+ * UNSUPPORTED (block size, head_dim, dtype, kv_dtype != cache dtype), HIP. */
+int pkv_kv_append(const void *k, const void *v, int32_t kv_dtype, const int64_t *slot_mapping,
+                  int32_t num_tokens, void *k_cache, void *v_cache, const pkv_cache_desc *cache,
+                  hipStream_t stream);
+
+/* Workspace bytes pkv_paged_attention_decode needs for a split-KV launch:
+ * Pn = ceil(max_blocks_per_seq * 16 / P) partitions per sequence, and when
+ * Pn > 1, num_seqs * num_q_heads * Pn * (head_dim + 2) * 4 bytes (float
+ * partial outputs, maxima and sums). 0 when Pn == 1 (no workspace needed).
+ * partition_size 0 means the library default (512); it must otherwise be a
+ * positive multiple of 16. Returns 0 for invalid arguments. */
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t max_blocks_per_seq, int32_t partition_size);
+
+/* Library default tokens per split-KV partition. */
+#define PKV_DEFAULT_PARTITION 512
+
+/* Paged decode attention: one new query token per sequence attends over its
+ * own cached tokens, read through its block table.
+ * ([ttlab] section 4 and [redhat]: block table lookup into a shared pool;
+ *  [ttlab] section 2: query head h of H_q shares KV head h / (H_q / H_kv)
+ *  (GQA, MQA when H_kv = 1); [tarun] "Batching does not merge the
+ *  conversations": sequences in one batch never see each other's blocks.)
+ *
+ * For sequence s with n = context_lens[s] and query head h, g = h / G:
+ *     x_t = scale * (q[s][h] . K_t),  t in [0, n),  K_t = k_cache row of t
+ *     out[s][h] = sum_t exp(x_t - max_u x_u) * V_t / sum_t exp(x_t - max_u x_u)
+ * with fp8 elements read as code * k_scale / code * v_scale. n counts the
+ * query's own token, whose K/V must already be appended. n <= 0 gives a zero
+ * row. Arithmetic is float32; the result is rounded to nearest-even into
+ * q_dtype.
+ *
+ *  q             [num_seqs][num_q_heads][head_dim] in q_dtype (device)
+ *  q_dtype       (q, cache) pairs: (F32, F32), (F16, F16), (BF16, BF16),
+ *                (F16 or BF16, FP8_E4M3)
+ *  num_q_heads   H_q, a multiple of cache->num_kv_heads with G = H_q / H_kv
+ *                at most 8
+ *  block_tables  int32 [num_seqs][max_blocks_per_seq] (device); only the
+ *                first ceil(n / 16) entries of a row are read
+ *  context_lens  int32 [num_seqs] (device)
+ *  scale         softmax scale applied to q . k (typically 1/sqrt(head_dim))
+ *  partition_size  tokens per split-KV partition (multiple of 16, 0 = default)
+ *  workspace, workspace_bytes  at least pkv_decode_workspace_bytes(...) of
+ *                device memory when that is > 0 (may be NULL when it is 0);
+ *                contents on entry do not matter
+ *  out           [num_seqs][num_q_heads][head_dim] in q_dtype (device); must
+ *                not alias any input or the workspace
+ * A sequence whose length exceeds max_blocks_per_seq * 16, or whose needed
+ * block ids fall outside [0, num_blocks), gets a NaN row (no out-of-range
+ * read happens). Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP. */
+int pkv_paged_attention_decode(const void *q, int32_t q_dtype, int32_t num_seqs,
+                               int32_t num_q_heads, const void *k_cache, const void *v_cache,
+                               const pkv_cache_desc *cache, const int32_t *block_tables,
+                               int32_t max_blocks_per_seq, const int32_t *context_lens,
+                               float scale, int32_t partition_size, void *workspace,
+                               size_t workspace_bytes, void *out, hipStream_t stream);
+
+/* Gather through the block tables (the same device addressing code as the
+ * decode kernel), for checking indexing byte for byte:
+ *     k_out[s][g][t][:] = K row of position t of sequence s, KV head g
+ * for t < min(context_lens[s], max_ctx); other rows of k_out/v_out are left
+ * untouched. k_out, v_out: [num_seqs][num_kv_heads][max_ctx][head_dim] in
+ * the cache dtype (device). Sequences with invalid lengths or block ids are
+ * skipped entirely. Errors: INVALID_ARG, UNSUPPORTED, HIP. */
+int pkv_debug_gather(const void *k_cache, const void *v_cache, const pkv_cache_desc *cache,
+                     const int32_t *block_tables, int32_t max_blocks_per_seq,
+                     const int32_t *context_lens, int32_t num_seqs, int32_t max_ctx, void *k_out,
+                     void *v_out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */
