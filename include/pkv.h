@@ -131,12 +131,14 @@ int pkv_kv_append(const void *k, const void *v, int32_t kv_dtype, const int64_t 
  * Pn > 1, num_seqs * num_q_heads * Pn * (head_dim + 2) * 4 bytes (float
  * partial outputs, maxima and sums). 0 when Pn == 1 (no workspace needed).
  * partition_size 0 means the library default (512); it must otherwise be a
- * positive multiple of 16. Returns 0 for invalid arguments. */
+ * positive multiple of 16 no larger than PKV_MAX_PARTITION. Returns 0 for
+ * invalid arguments. */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_blocks_per_seq, int32_t partition_size);
 
-/* Library default tokens per split-KV partition. */
+/* Library default and largest tokens per split-KV partition. */
 #define PKV_DEFAULT_PARTITION 512
+#define PKV_MAX_PARTITION 1024
 
 /* Paged decode attention: one new query token per sequence attends over its
  * own cached tokens, read through its block table.
@@ -162,10 +164,17 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *                first ceil(n / 16) entries of a row are read
  *  context_lens  int32 [num_seqs] (device)
  *  scale         softmax scale applied to q . k (typically 1/sqrt(head_dim))
- *  partition_size  tokens per split-KV partition (multiple of 16, 0 = default)
+ *  partition_size  tokens per split-KV partition: a multiple of 16 up to
+ *                PKV_MAX_PARTITION (UNSUPPORTED above), 0 = the default
  *  workspace, workspace_bytes  at least pkv_decode_workspace_bytes(...) of
- *                device memory when that is > 0 (may be NULL when it is 0);
- *                contents on entry do not matter
+ *                16-byte aligned device memory when that is > 0 (may be NULL
+ *                when it is 0); contents on entry do not matter. On return
+ *                it holds, for R = num_seqs * num_q_heads rows and Pn
+ *                partitions: float o[R][Pn][head_dim] (each partition's own
+ *                normalised output), then float m[R][Pn] (its max score,
+ *                natural-log units), then float l[R][Pn] (its sum of
+ *                exp(score - m)); entries of partitions past a sequence's
+ *                length are unspecified
  *  out           [num_seqs][num_q_heads][head_dim] in q_dtype (device); must
  *                not alias any input or the workspace
  * A sequence whose length exceeds max_blocks_per_seq * 16, or whose needed

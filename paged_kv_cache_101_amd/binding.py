@@ -1,0 +1,207 @@
+"""Thin ctypes binding of libpkv.so (include/pkv.h).
+
+Argument marshalling only: torch tensors in, raw device pointers, dtype codes
+and sizes out to the C entry points of the same names; every step of the
+computation runs in the HIP kernels behind them. Shapes, dtypes and
+contiguity are checked here so that a wrong call fails with a Python error
+before reaching the library. Without a built library every call raises: there
+is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpkv.so")
+
+PKV_OK = 0
+PKV_ERR_INVALID_ARG = -1
+PKV_ERR_UNSUPPORTED = -2
+PKV_ERR_WORKSPACE = -3
+PKV_ERR_HIP = -4
+
+PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2, 3
+PKV_BLOCK_SIZE = 16
+PKV_DEFAULT_PARTITION = 512
+PKV_MAX_PARTITION = 1024
+
+DTYPE_CODES = {"f32": PKV_F32, "f16": PKV_F16, "bf16": PKV_BF16, "fp8": PKV_FP8_E4M3}
+_TORCH_CODES = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
+
+EXPORTS = ("pkv_status_string", "pkv_kv_bytes_per_token", "pkv_cache_tensor_bytes",
+           "pkv_kv_append", "pkv_decode_workspace_bytes", "pkv_paged_attention_decode",
+           "pkv_debug_gather")
+
+
+class PkvError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status_string(status)} ({status})")
+        self.status = status
+
+
+class pkv_cache_desc(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("k_scale", ctypes.c_float),
+                ("v_scale", ctypes.c_float)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libpkv.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libpkv.so not found at {LIB_PATH}: build it first "
+                               "(python -c 'import __graft_entry__ as g; g.build()')")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz, f32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                 ctypes.c_size_t, ctypes.c_float)
+        descp = ctypes.POINTER(pkv_cache_desc)
+        L.pkv_status_string.argtypes = [ctypes.c_int]
+        L.pkv_status_string.restype = ctypes.c_char_p
+        L.pkv_kv_bytes_per_token.argtypes = [i32, i32, i32, i32]
+        L.pkv_kv_bytes_per_token.restype = sz
+        L.pkv_cache_tensor_bytes.argtypes = [descp]
+        L.pkv_cache_tensor_bytes.restype = sz
+        L.pkv_kv_append.argtypes = [vp, vp, i32, vp, i32, vp, vp, descp, vp]
+        L.pkv_kv_append.restype = ctypes.c_int
+        L.pkv_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+        L.pkv_decode_workspace_bytes.restype = sz
+        L.pkv_paged_attention_decode.argtypes = [vp, i32, i32, i32, vp, vp, descp, vp, i32, vp,
+                                                 f32, i32, vp, sz, vp, vp]
+        L.pkv_paged_attention_decode.restype = ctypes.c_int
+        L.pkv_debug_gather.argtypes = [vp, vp, descp, vp, i32, vp, i32, i32, vp, vp, vp]
+        L.pkv_debug_gather.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().pkv_status_string(status).decode()
+
+
+def _check(fn: str, rc: int):
+    if rc != PKV_OK:
+        raise PkvError(fn, rc)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def cache_desc(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: str,
+               k_scale: float = 1.0, v_scale: float = 1.0) -> pkv_cache_desc:
+    return pkv_cache_desc(num_blocks, PKV_BLOCK_SIZE, num_kv_heads, head_dim, DTYPE_CODES[dtype],
+                          k_scale, v_scale)
+
+
+def desc_for(k_cache: torch.Tensor, dtype: str, k_scale=1.0, v_scale=1.0) -> pkv_cache_desc:
+    nb, H, bs, d = k_cache.shape
+    _need(bs == PKV_BLOCK_SIZE, "cache must be [num_blocks][H_kv][16][head_dim]")
+    return cache_desc(nb, H, d, dtype, k_scale, v_scale)
+
+
+def _dtype_of(t: torch.Tensor, declared: Optional[str] = None) -> int:
+    if t.dtype == torch.uint8:
+        _need(declared in (None, "fp8"), "uint8 tensors hold fp8 E4M3 codes")
+        return PKV_FP8_E4M3
+    if t.dtype == torch.float8_e4m3fn:
+        return PKV_FP8_E4M3
+    return _TORCH_CODES[t.dtype]
+
+
+# ---- entry points (same names as the C ABI) --------------------------------
+
+def pkv_kv_bytes_per_token(num_layers: int, num_kv_heads: int, head_dim: int, dtype: str) -> int:
+    return int(lib().pkv_kv_bytes_per_token(num_layers, num_kv_heads, head_dim,
+                                            DTYPE_CODES[dtype]))
+
+
+def pkv_cache_tensor_bytes(desc: pkv_cache_desc) -> int:
+    return int(lib().pkv_cache_tensor_bytes(ctypes.byref(desc)))
+
+
+def pkv_decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
+                               max_blocks_per_seq: int, partition_size: int = 0) -> int:
+    return int(lib().pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
+                                                max_blocks_per_seq, partition_size))
+
+
+def pkv_kv_append(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                  k_cache: torch.Tensor, v_cache: torch.Tensor, desc: pkv_cache_desc,
+                  stream=None) -> None:
+    """k, v: [T][H_kv][d] in the cache dtype; slot_mapping: int64 [T]."""
+    T = k.shape[0]
+    _need(k.shape == v.shape and k.dim() == 3, "k and v must be [T][H_kv][d]")
+    _need(slot_mapping.dtype == torch.int64 and slot_mapping.numel() == T,
+          "slot_mapping must be int64 [T]")
+    for t in (k, v, slot_mapping, k_cache, v_cache):
+        _need(t.is_contiguous() and t.is_cuda, "all tensors must be contiguous device tensors")
+    _need(k.dtype == k_cache.dtype == v_cache.dtype == v.dtype, "k/v/cache dtypes differ")
+    rc = lib().pkv_kv_append(_ptr(k), _ptr(v), _dtype_of(k), _ptr(slot_mapping), T,
+                             _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc), _stream(stream))
+    _check("pkv_kv_append", rc)
+
+
+def pkv_paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                               desc: pkv_cache_desc, block_tables: torch.Tensor,
+                               context_lens: torch.Tensor, scale: float, out: torch.Tensor,
+                               partition_size: int = 0,
+                               workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """q, out: [S][H_q][d]; block_tables: int32 [S][max_blocks]; context_lens: int32 [S].
+    A workspace of pkv_decode_workspace_bytes() bytes is allocated from torch
+    when none is given."""
+    S, Hq, d = q.shape
+    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+          and block_tables.shape[0] == S, "block_tables must be int32 [S][max_blocks]")
+    _need(context_lens.dtype == torch.int32 and context_lens.numel() == S,
+          "context_lens must be int32 [S]")
+    for t in (q, k_cache, v_cache, block_tables, context_lens, out):
+        _need(t.is_contiguous() and t.is_cuda, "all tensors must be contiguous device tensors")
+    mb = block_tables.shape[1]
+    need = pkv_decode_workspace_bytes(S, Hq, d, mb, partition_size)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().pkv_paged_attention_decode(
+        _ptr(q), _dtype_of(q), S, Hq, _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
+        _ptr(block_tables), mb, _ptr(context_lens), float(scale), partition_size,
+        _ptr(workspace), ws_bytes, _ptr(out), _stream(stream))
+    _check("pkv_paged_attention_decode", rc)
+
+
+def pkv_debug_gather(k_cache: torch.Tensor, v_cache: torch.Tensor, desc: pkv_cache_desc,
+                     block_tables: torch.Tensor, context_lens: torch.Tensor, max_ctx: int,
+                     k_out: torch.Tensor, v_out: torch.Tensor, stream=None) -> None:
+    """k_out, v_out: [S][H_kv][max_ctx][d] in the cache dtype."""
+    S = context_lens.numel()
+    for t in (k_cache, v_cache, block_tables, context_lens, k_out, v_out):
+        _need(t.is_contiguous() and t.is_cuda, "all tensors must be contiguous device tensors")
+    rc = lib().pkv_debug_gather(_ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
+                                _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+                                S, max_ctx, _ptr(k_out), _ptr(v_out), _stream(stream))
+    _check("pkv_debug_gather", rc)
+
+
+# Names as the pages' problem statement gives them.
+kv_append = pkv_kv_append
+paged_attention_decode = pkv_paged_attention_decode

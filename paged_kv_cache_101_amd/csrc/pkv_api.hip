@@ -1,0 +1,195 @@
+// pkv_api.hip -- the extern "C" entry points of libpkv.so (declared and
+// documented in include/pkv.h). Every argument the host can check is checked
+// here, before any HIP call; the launchers in the kernel files only see
+// validated arguments.
+#include <stdint.h>
+
+#include "pkv.h"
+#include "pkv_internal.h"
+
+#define PKV_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+int elem_bytes(int dtype) {
+    switch (dtype) {
+    case PKV_F32: return 4;
+    case PKV_F16: return 2;
+    case PKV_BF16: return 2;
+    case PKV_FP8_E4M3: return 1;
+    default: return 0;
+    }
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Common checks of a cache descriptor.
+int check_cache(const pkv_cache_desc* c) {
+    if (c == nullptr) return PKV_ERR_INVALID_ARG;
+    if (c->num_blocks <= 0 || c->num_kv_heads <= 0 || c->head_dim <= 0) return PKV_ERR_INVALID_ARG;
+    if (c->block_size != PKV_BLOCK_SIZE) return PKV_ERR_UNSUPPORTED;
+    if (c->head_dim != 64 && c->head_dim != 128) return PKV_ERR_UNSUPPORTED;
+    if (elem_bytes(c->dtype) == 0) return PKV_ERR_UNSUPPORTED;
+    if (c->dtype == PKV_FP8_E4M3 && !(c->k_scale > 0.f && c->v_scale > 0.f))
+        return PKV_ERR_INVALID_ARG;
+    return PKV_OK;
+}
+
+int32_t resolve_partition(int32_t partition_size) {
+    return partition_size == 0 ? PKV_DEFAULT_PARTITION : partition_size;
+}
+
+bool partition_ok(int32_t p) {
+    return p > 0 && p % PKV_BLOCK_SIZE == 0 && p <= pkv::kMaxPartition;
+}
+
+int64_t num_partitions(int32_t max_blocks_per_seq, int32_t p) {
+    return ((int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE + p - 1) / p;
+}
+
+}  // namespace
+
+PKV_EXPORT const char* pkv_status_string(int status) {
+    switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID_ARG: return "invalid argument";
+    case PKV_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+    }
+}
+
+PKV_EXPORT size_t pkv_kv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t dtype) {
+    const int b = elem_bytes(dtype);
+    if (num_layers <= 0 || num_kv_heads <= 0 || head_dim <= 0 || b == 0) return 0;
+    return (size_t)2 * num_layers * num_kv_heads * head_dim * b;
+}
+
+PKV_EXPORT size_t pkv_cache_tensor_bytes(const pkv_cache_desc* cache) {
+    if (check_cache(cache) != PKV_OK) return 0;
+    return (size_t)cache->num_blocks * cache->num_kv_heads * PKV_BLOCK_SIZE * cache->head_dim *
+           elem_bytes(cache->dtype);
+}
+
+PKV_EXPORT int pkv_kv_append(const void* k, const void* v, int32_t kv_dtype,
+                             const int64_t* slot_mapping, int32_t num_tokens, void* k_cache,
+                             void* v_cache, const pkv_cache_desc* cache, hipStream_t stream) {
+    int rc = check_cache(cache);
+    if (rc != PKV_OK) return rc;
+    if (num_tokens < 0) return PKV_ERR_INVALID_ARG;
+    if (kv_dtype != cache->dtype) return PKV_ERR_UNSUPPORTED;
+    if (k_cache == nullptr || v_cache == nullptr) return PKV_ERR_INVALID_ARG;
+    if (num_tokens > 0 && (k == nullptr || v == nullptr || slot_mapping == nullptr))
+        return PKV_ERR_INVALID_ARG;
+    if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
+        return PKV_ERR_INVALID_ARG;
+    if (num_tokens == 0) return PKV_OK;
+    hipError_t err = pkv::launch_kv_append(k, v, elem_bytes(cache->dtype), slot_mapping,
+                                           num_tokens, k_cache, v_cache, cache->num_blocks,
+                                           cache->num_kv_heads, cache->head_dim, stream);
+    return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+PKV_EXPORT size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                             int32_t head_dim, int32_t max_blocks_per_seq,
+                                             int32_t partition_size) {
+    const int32_t p = resolve_partition(partition_size);
+    if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0 ||
+        !partition_ok(p))
+        return 0;
+    const int64_t pn = num_partitions(max_blocks_per_seq, p);
+    if (pn <= 1) return 0;
+    return (size_t)num_seqs * num_q_heads * pn * (head_dim + 2) * sizeof(float);
+}
+
+PKV_EXPORT int pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t num_seqs,
+                                          int32_t num_q_heads, const void* k_cache,
+                                          const void* v_cache, const pkv_cache_desc* cache,
+                                          const int32_t* block_tables,
+                                          int32_t max_blocks_per_seq,
+                                          const int32_t* context_lens, float scale,
+                                          int32_t partition_size, void* workspace,
+                                          size_t workspace_bytes, void* out,
+                                          hipStream_t stream) {
+    int rc = check_cache(cache);
+    if (rc != PKV_OK) return rc;
+    if (num_seqs <= 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0)
+        return PKV_ERR_INVALID_ARG;
+    if (num_q_heads % cache->num_kv_heads != 0) return PKV_ERR_INVALID_ARG;
+    const int group = num_q_heads / cache->num_kv_heads;
+    if (group > 8) return PKV_ERR_UNSUPPORTED;
+    const int kv = cache->dtype;
+    const bool pair_ok = (kv == PKV_F32 && q_dtype == PKV_F32) ||
+                         (kv == PKV_F16 && q_dtype == PKV_F16) ||
+                         (kv == PKV_BF16 && q_dtype == PKV_BF16) ||
+                         (kv == PKV_FP8_E4M3 && (q_dtype == PKV_F16 || q_dtype == PKV_BF16));
+    if (!pair_ok) return PKV_ERR_UNSUPPORTED;
+    if (q == nullptr || k_cache == nullptr || v_cache == nullptr || block_tables == nullptr ||
+        context_lens == nullptr || out == nullptr)
+        return PKV_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+        return PKV_ERR_INVALID_ARG;
+    if (!(scale == scale)) return PKV_ERR_INVALID_ARG;
+    const int32_t p = resolve_partition(partition_size);
+    if (p <= 0 || p % PKV_BLOCK_SIZE != 0) return PKV_ERR_INVALID_ARG;
+    if (p > pkv::kMaxPartition) return PKV_ERR_UNSUPPORTED;
+    const int64_t pn = num_partitions(max_blocks_per_seq, p);
+    if (pn > 65535) return PKV_ERR_UNSUPPORTED;  // grid x limit for one launch
+
+    pkv::DecodeArgs a{};
+    a.q = q;
+    a.q_dtype = q_dtype;
+    a.kv_dtype = kv;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = cache->num_kv_heads;
+    a.group = group;
+    a.head_dim = cache->head_dim;
+    a.num_blocks = cache->num_blocks;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.context_lens = context_lens;
+    a.scale = scale;
+    a.k_scale = cache->k_scale;
+    a.v_scale = cache->v_scale;
+    a.partition_size = p;
+    a.num_partitions = (int)pn;
+    a.out = out;
+    a.stream = stream;
+    if (pn > 1) {
+        const size_t need = pkv_decode_workspace_bytes(num_seqs, num_q_heads, cache->head_dim,
+                                                       max_blocks_per_seq, p);
+        if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))
+            return PKV_ERR_WORKSPACE;
+        const size_t rows = (size_t)num_seqs * num_q_heads * pn;
+        a.ws_o = static_cast<float*>(workspace);
+        a.ws_m = a.ws_o + rows * cache->head_dim;
+        a.ws_l = a.ws_m + rows;
+    }
+    hipError_t err = pkv::launch_paged_decode(a);
+    return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+PKV_EXPORT int pkv_debug_gather(const void* k_cache, const void* v_cache,
+                                const pkv_cache_desc* cache, const int32_t* block_tables,
+                                int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                int32_t num_seqs, int32_t max_ctx, void* k_out, void* v_out,
+                                hipStream_t stream) {
+    int rc = check_cache(cache);
+    if (rc != PKV_OK) return rc;
+    if (num_seqs <= 0 || max_ctx < 0 || max_blocks_per_seq <= 0) return PKV_ERR_INVALID_ARG;
+    if (k_cache == nullptr || v_cache == nullptr || block_tables == nullptr ||
+        context_lens == nullptr || k_out == nullptr || v_out == nullptr)
+        return PKV_ERR_INVALID_ARG;
+    if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_out) || !aligned16(v_out))
+        return PKV_ERR_INVALID_ARG;
+    hipError_t err = pkv::launch_gather(k_cache, v_cache, elem_bytes(cache->dtype),
+                                        cache->num_blocks, cache->num_kv_heads, cache->head_dim,
+                                        block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                                        max_ctx, k_out, v_out, stream);
+    return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}

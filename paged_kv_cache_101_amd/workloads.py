@@ -171,13 +171,14 @@ def make_batch(name: str, case_id: int, context_lens: Sequence[int], num_q_heads
                pool_factor: float = 1.0, shared_prefix_blocks: int = 0,
                max_blocks: Optional[int] = None, canary: bool = False,
                append_last: bool = False, partition_size: int = 512,
-               scale: Optional[float] = None) -> DecodeBatch:
+               scale: Optional[float] = None, structure_layer: Optional[int] = None) -> DecodeBatch:
     """Build one decode batch.
 
     ``append_last`` holds back the K/V row at position n-1 of every sequence
     with n > 0: its slot is left as NaN (canary) or random, and the row to
     write comes back in ``new_k``/``new_v``/``slot_mapping`` for an append
-    call made before decode."""
+    call made before decode. ``structure_layer`` (default: ``layer``) seeds the
+    block permutation, so several layers can share one block table."""
     ctx = np.asarray(context_lens, dtype=np.int64)
     S = ctx.shape[0]
     bps = [(max(int(n), 0) + BLOCK - 1) // BLOCK for n in ctx]
@@ -185,7 +186,7 @@ def make_batch(name: str, case_id: int, context_lens: Sequence[int], num_q_heads
     need = shared_prefix_blocks + sum(max(0, b - shared_prefix_blocks) for b in bps)
     if num_blocks is None:
         num_blocks = int(math.ceil(pool_factor * need)) + 1
-    rng = np.random.default_rng([case_id, 1, layer])
+    rng = np.random.default_rng([case_id, 1, layer if structure_layer is None else structure_layer])
     bt = assign_blocks(bps, num_blocks, rng, shared_prefix_blocks, mb)
 
     H, d = num_kv_heads, head_dim
@@ -268,11 +269,13 @@ def qwen_layer(device="cpu", canary=False, num_seqs=64, lo=128, hi=4096) -> Deco
                       pool_factor=1.5, canary=canary, append_last=True)
 
 
-def gqa40_layer(device="cpu", layer=0, num_seqs=40, ctx=8192, canary=False) -> DecodeBatch:
+def gqa40_layer(device="cpu", layer=0, num_seqs=40, ctx=8192, canary=False,
+                append_last=False) -> DecodeBatch:
     """One layer of the 40-layer GQA shape: 32 query / 8 KV heads, d 128,
-    fp16 KV, 40 sequences of 8192 tokens, shuffled blocks."""
+    fp16 KV, 40 sequences of 8192 tokens, shuffled blocks. Every layer has its
+    own caches and queries; all layers share one block table."""
     return make_batch("gqa40-8k", 3, [ctx] * num_seqs, 32, 8, 128, "f16", "f16", device=device,
-                      layer=layer, canary=canary)
+                      layer=layer, canary=canary, append_last=append_last, structure_layer=0)
 
 
 def prefix_shared_lengths(num_seqs=256, prefix=2048, lo=64, hi=512, case_id=4):

@@ -1,0 +1,135 @@
+"""Host-side checks of libpkv.so that need no GPU: it loads, exports every
+entry point include/pkv.h declares, computes the sizing numbers the pages
+print, and rejects every bad argument before any HIP call (so these calls
+return on a machine without a GPU)."""
+import ctypes
+import json
+import os
+import re
+import subprocess
+
+import pytest
+
+from paged_kv_cache_101_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLD = json.load(open(os.path.join(ROOT, "tests", "golden", "sizing.json")))
+FAKE = 0x10000  # an aligned non-null address; never dereferenced by these calls
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "pkv.h")).read()
+    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) == set(B.EXPORTS)
+    L = B.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert exported == set(names)  # nothing else leaks out of the library
+
+
+def test_sizing_matches_pages():
+    g = GOLD["qwen2_5_1_5b"]
+    assert B.pkv_kv_bytes_per_token(28, 2, 128, "bf16") == g["bytes_per_token"]
+    g = GOLD["qwen2_5_7b"]
+    assert B.pkv_kv_bytes_per_token(28, 4, 128, "bf16") == g["kib_per_token"] * 1024
+    assert B.pkv_kv_bytes_per_token(28, 28, 128, "bf16") == g["mha_kib_per_token"] * 1024
+    g = GOLD["gqa40_fp16"]
+    assert B.pkv_kv_bytes_per_token(40, 8, 128, "f16") == g["kib_per_token"] * 1024
+    assert B.pkv_kv_bytes_per_token(40, 8, 128, "fp8") == g["kib_per_token"] * 512
+    assert B.pkv_kv_bytes_per_token(0, 8, 128, "f16") == 0
+
+
+def test_cache_tensor_bytes():
+    d = B.cache_desc(20481, 8, 128, "f16")
+    assert B.pkv_cache_tensor_bytes(d) == 20481 * 8 * 16 * 128 * 2
+    d = B.cache_desc(10, 8, 96, "f16")
+    assert B.pkv_cache_tensor_bytes(d) == 0
+
+
+def test_workspace_bytes_formula():
+    # 40 sequences x 32 heads x 16 partitions x (128 + 2) floats
+    assert B.pkv_decode_workspace_bytes(40, 32, 128, 512, 512) == 40 * 32 * 16 * 130 * 4
+    assert B.pkv_decode_workspace_bytes(40, 32, 128, 512, 0) == 40 * 32 * 16 * 130 * 4
+    assert B.pkv_decode_workspace_bytes(16, 64, 128, 2048, 512) == 16 * 64 * 64 * 130 * 4
+    assert B.pkv_decode_workspace_bytes(4, 4, 64, 3, 512) == 0      # one partition
+    assert B.pkv_decode_workspace_bytes(4, 4, 64, 3, 24) == 0       # not a multiple of 16
+    assert B.pkv_decode_workspace_bytes(4, 4, 64, 3, 2048) == 0     # above the maximum
+
+
+def _decode(**kw):
+    a = dict(q=FAKE, q_dtype=B.PKV_F16, S=4, Hq=8, k=FAKE, v=FAKE,
+             desc=B.cache_desc(16, 2, 128, "f16"), bt=FAKE, mb=64, cl=FAKE, scale=0.1, P=512,
+             ws=None, ws_bytes=0, out=FAKE)
+    a.update(kw)
+    return B.lib().pkv_paged_attention_decode(
+        a["q"], a["q_dtype"], a["S"], a["Hq"], a["k"], a["v"], ctypes.byref(a["desc"]), a["bt"],
+        a["mb"], a["cl"], a["scale"], a["P"], a["ws"], a["ws_bytes"], a["out"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), B.PKV_ERR_INVALID_ARG),
+    (dict(out=None), B.PKV_ERR_INVALID_ARG),
+    (dict(bt=None), B.PKV_ERR_INVALID_ARG),
+    (dict(cl=None), B.PKV_ERR_INVALID_ARG),
+    (dict(S=0), B.PKV_ERR_INVALID_ARG),
+    (dict(Hq=7), B.PKV_ERR_INVALID_ARG),                      # 7 % 2 != 0
+    (dict(Hq=18), B.PKV_ERR_UNSUPPORTED),                     # G = 9 > 8
+    (dict(desc=B.pkv_cache_desc(16, 32, 2, 128, B.PKV_F16, 1, 1)), B.PKV_ERR_UNSUPPORTED),
+    (dict(desc=B.cache_desc(16, 2, 96, "f16")), B.PKV_ERR_UNSUPPORTED),
+    (dict(desc=B.cache_desc(0, 2, 128, "f16")), B.PKV_ERR_INVALID_ARG),
+    (dict(q_dtype=B.PKV_BF16), B.PKV_ERR_UNSUPPORTED),        # bf16 q over f16 cache
+    (dict(desc=B.cache_desc(16, 2, 128, "fp8", 0.0, 1.0), q_dtype=B.PKV_BF16),
+     B.PKV_ERR_INVALID_ARG),                                  # fp8 needs positive scales
+    (dict(q_dtype=7), B.PKV_ERR_UNSUPPORTED),
+    (dict(P=24), B.PKV_ERR_INVALID_ARG),
+    (dict(P=2048), B.PKV_ERR_UNSUPPORTED),
+    (dict(ws=None, ws_bytes=0), B.PKV_ERR_WORKSPACE),         # 2 partitions need one
+    (dict(ws=FAKE, ws_bytes=100), B.PKV_ERR_WORKSPACE),
+    (dict(q=FAKE + 4), B.PKV_ERR_INVALID_ARG),                # misaligned
+    (dict(scale=float("nan")), B.PKV_ERR_INVALID_ARG),
+])
+def test_decode_rejects_before_any_hip_call(kw, status):
+    assert _decode(**kw) == status
+
+
+def _append(**kw):
+    a = dict(k=FAKE, v=FAKE, dt=B.PKV_F16, slots=FAKE, T=4, kc=FAKE, vc=FAKE,
+             desc=B.cache_desc(16, 2, 128, "f16"))
+    a.update(kw)
+    return B.lib().pkv_kv_append(a["k"], a["v"], a["dt"], a["slots"], a["T"], a["kc"], a["vc"],
+                                 ctypes.byref(a["desc"]), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=None), B.PKV_ERR_INVALID_ARG),
+    (dict(slots=None), B.PKV_ERR_INVALID_ARG),
+    (dict(kc=None), B.PKV_ERR_INVALID_ARG),
+    (dict(T=-1), B.PKV_ERR_INVALID_ARG),
+    (dict(dt=B.PKV_BF16), B.PKV_ERR_UNSUPPORTED),             # not the cache dtype
+    (dict(desc=B.pkv_cache_desc(16, 8, 2, 128, B.PKV_F16, 1, 1)), B.PKV_ERR_UNSUPPORTED),
+    (dict(v=FAKE + 8), B.PKV_ERR_INVALID_ARG),
+    (dict(T=0, k=None, v=None, slots=None), B.PKV_OK),        # empty append is a no-op
+])
+def test_append_rejects_before_any_hip_call(kw, status):
+    assert _append(**kw) == status
+
+
+def test_gather_rejects_bad_args():
+    L = B.lib()
+    d = B.cache_desc(16, 2, 128, "f16")
+    assert L.pkv_debug_gather(FAKE, FAKE, ctypes.byref(d), FAKE, 4, FAKE, 0, 8, FAKE, FAKE,
+                              None) == B.PKV_ERR_INVALID_ARG
+    assert L.pkv_debug_gather(FAKE, FAKE, ctypes.byref(d), None, 4, FAKE, 2, 8, FAKE, FAKE,
+                              None) == B.PKV_ERR_INVALID_ARG
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, 99):
+        assert B.status_string(s)

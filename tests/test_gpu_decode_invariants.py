@@ -1,0 +1,86 @@
+"""GPU: invariants of paged decode that hold bit for bit on the device.
+
+The kernel's arithmetic depends only on each sequence's logical token order,
+never on where the blocks sit in the pool, so permuting physical blocks,
+sharing vs copying a prefix and repeating a run must give identical bytes.
+Changing the partition size reorders the float32 sums, so it is checked
+against the oracle's tolerance instead."""
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_101_amd import workloads as W
+from tests.helpers import assert_close, gpu_decode, oracle_decode, out_to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _same_bytes(a: torch.Tensor, b: torch.Tensor) -> bool:
+    return W.to_numpy(a).tobytes() == W.to_numpy(b).tobytes()
+
+
+@pytest.mark.parametrize("P", [64, 512])
+def test_block_permutation_is_bitwise_invariant(gpu, P):
+    b = W.make_batch("perm", 81, [1, 16, 33, 700, 2049], 12, 2, 128, "bf16", "bf16", device=gpu,
+                     pool_factor=2.0, canary=True)
+    base = gpu_decode(b, P)
+    perm = torch.from_numpy(np.random.default_rng(5).permutation(b.num_blocks)).to(gpu)
+    kc = torch.empty_like(b.k_cache)
+    vc = torch.empty_like(b.v_cache)
+    kc[perm] = b.k_cache
+    vc[perm] = b.v_cache
+    moved = W.DecodeBatch(**{**b.__dict__, "k_cache": kc, "v_cache": vc,
+                             "block_tables": perm[b.block_tables.long()].to(torch.int32)})
+    out = gpu_decode(moved, P)
+    torch.cuda.synchronize()
+    assert _same_bytes(base, out)
+
+
+def test_shared_prefix_equals_private_copies(gpu):
+    ctx = W.prefix_shared_lengths(16, 256)
+    b = W.make_batch("shared", 82, ctx, 32, 8, 128, "bf16", "bf16", device=gpu,
+                     shared_prefix_blocks=16)
+    bt = b.block_tables.cpu().numpy()
+    assert (bt[:, :16] == bt[0, :16]).all()
+    # give every sequence its own copy of the 16 prefix blocks
+    extra = 16 * (b.num_seqs - 1)
+    kc = torch.cat([b.k_cache, torch.empty((extra,) + b.k_cache.shape[1:], dtype=b.k_cache.dtype,
+                                           device=gpu)])
+    vc = torch.cat([b.v_cache, torch.empty_like(kc[b.num_blocks:])])
+    bt2 = bt.copy()
+    nxt = b.num_blocks
+    for s in range(1, b.num_seqs):
+        for i in range(16):
+            kc[nxt] = b.k_cache[bt[0, i]]
+            vc[nxt] = b.v_cache[bt[0, i]]
+            bt2[s, i] = nxt
+            nxt += 1
+    copied = W.DecodeBatch(**{**b.__dict__, "k_cache": kc, "v_cache": vc,
+                              "num_blocks": kc.shape[0],
+                              "block_tables": torch.from_numpy(bt2).to(gpu)})
+    for P in (64, 512):
+        assert _same_bytes(gpu_decode(b, P), gpu_decode(copied, P))
+
+
+def test_repeat_runs_are_bitwise_identical(gpu):
+    b = W.gqa40_layer(device=gpu, num_seqs=8, ctx=4100)
+    first = gpu_decode(b)
+    for _ in range(3):
+        assert _same_bytes(first, gpu_decode(b))
+
+
+def test_batch_order_permutes_rows(gpu):
+    b = W.make_batch("order", 83, [5, 900, 64, 1500, 17], 8, 1, 128, "f16", "f16", device=gpu)
+    base = gpu_decode(b)
+    p = torch.tensor([3, 0, 4, 1, 2], device=gpu)
+    pb = W.DecodeBatch(**{**b.__dict__, "q": b.q[p].contiguous(),
+                          "block_tables": b.block_tables[p].contiguous(),
+                          "context_lens": b.context_lens[p].contiguous()})
+    assert _same_bytes(gpu_decode(pb), base[p].contiguous())
+
+
+def test_partition_size_changes_only_rounding(gpu):
+    b = W.make_batch("parts", 84, [3000, 4096, 77], 32, 8, 128, "f16", "f16", device=gpu)
+    ref = oracle_decode(b)
+    for P in (16, 48, 128, 512, 1024):
+        assert_close(out_to_f64(gpu_decode(b, P)), ref, "f16", f"P={P}")
