@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Benchmark: paged decode attention on one MI355X.
+
+A step is one pass of the whole hot path over the 40-layer GQA workload
+(40 sequences of 8192 tokens, 32 query / 8 KV heads, d 128, fp16 KV in
+16-token blocks, one block table shared by all layers): for each of the 40
+layers, append the new token's K/V rows through the slot mapping, then run
+paged decode (one launch: the batch's tiles split evenly over the device's
+worker waves, split segments merged by log-sum-exp inside it). Every layer
+has its own 1.25 GiB of cache, so nothing is served from a cache level across
+layers; all inputs are resident in HBM before timing starts.
+
+Printed (one JSON line, last): value = algorithmic KV bytes read per second
+(GB/s, 1e9), decode sequences per second, and the roofline of the dominant
+kernel (the decode kernel, one launch per layer) timed with HIP events on the
+stream it runs on, plus the CPU oracle timed on a bounded sample of the same
+workload on this host's cores.
+
+Other workloads (--workload qwen|prefix|fp8|tiny) time the decode call alone
+and print the same fields; they are for profiling, not the headline line.
+"""
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gqa40", choices=["gqa40", "qwen", "prefix", "fp8", "tiny"])
+    ap.add_argument("--workers", type=int, default=0, help="worker waves (0 = fill the device)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of this many MiB (for counter scaling)")
+    return ap.parse_args()
+
+
+def kernel_hash() -> str:
+    """Hash of the decode kernel sources: counter figures are valid only for
+    the build they were taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("paged_decode.hip", "pkv_device.h"):
+        with open(os.path.join(ROOT, "paged_kv_cache_101_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM traffic per decode launch from the committed counter summary, or
+    None if it was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    rec = None
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("{"):
+                rec = json.loads(line)
+    if rec is None or rec.get("kernel_hash") != kernel_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def copy_calibration(mib: int):
+    import torch
+    n = mib * 2**20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+
+
+def build_layers(workload: str, device):
+    from paged_kv_cache_101_amd import workloads as W
+    if workload == "gqa40":
+        layers = [W.gqa40_layer(device=device, layer=l, append_last=True) for l in range(40)]
+    elif workload == "qwen":
+        layers = [W.qwen_layer(device=device)]
+    elif workload == "prefix":
+        layers = [W.prefix_shared(device=device)]
+    elif workload == "fp8":
+        layers = [W.fp8_long(device=device)]
+    else:
+        layers = [W.tiny(device=device)]
+    return layers
+
+
+def describe(workload: str, layers, workers: int) -> dict:
+    b = layers[0]
+    return {
+        "workload": {
+            "gqa40": "40-layer GQA decode step: 40 layers x 40 seqs x 8192 ctx",
+            "qwen": "Qwen2.5-1.5B-shaped layer decode: 64 seqs, ctx U[128,4096]",
+            "prefix": "prefix sharing decode: 256 seqs, 2048 shared + U[64,512] ctx",
+            "fp8": "long-context fp8 decode: 16 seqs x 32768 ctx",
+            "tiny": "tiny MQA decode: 4 seqs, ctx {1,15,16,33}",
+        }[workload],
+        "layers": len(layers), "num_seqs": b.num_seqs, "q_heads": b.num_q_heads,
+        "kv_heads": b.num_kv_heads, "head_dim": b.head_dim, "kv_dtype": b.kv_dtype,
+        "block_size": 16, "workers": workers or "device default",
+    }
+
+
+def cpu_baseline(layer, target_s: float):
+    """The oracle (as it stands) on a bounded sample: the first k sequences of
+    one layer, all their heads; k grows until about target_s of CPU work."""
+    import numpy as np
+    import oracle
+    from paged_kv_cache_101_amd import workloads as W
+
+    h = dict(q=W.to_numpy(layer.q), k=W.to_numpy(layer.k_cache), v=W.to_numpy(layer.v_cache),
+             bt=layer.block_tables.cpu().numpy(), ctx=layer.context_lens.cpu().numpy())
+    bpt = 2 * layer.num_kv_heads * layer.head_dim * W.STORAGE[layer.kv_dtype][1]
+
+    def run(k):
+        t0 = time.perf_counter()
+        oracle.paged_decode(np.ascontiguousarray(h["q"][:k]), h["k"], h["v"],
+                            np.ascontiguousarray(h["bt"][:k]), np.ascontiguousarray(h["ctx"][:k]),
+                            layer.scale, layer.k_scale, layer.v_scale)
+        return time.perf_counter() - t0
+
+    k, el = 1, run(1)
+    S = layer.num_seqs
+    if el < target_s:
+        k = max(1, min(S, int(target_s / max(el, 1e-3))))
+        if k > 1:
+            el = run(k)
+    tokens = int(h["ctx"][:k].clip(min=0).sum())
+    return {
+        "value": round(tokens * bpt / el / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"layer 0, sequences 0..{k - 1} of {S} (all {layer.num_q_heads} query heads), "
+                  f"{tokens} tokens, {tokens * bpt} KV bytes, {el:.2f} s",
+        "seqs_per_s": round(k / el, 4),
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "paged decode shards over sequences or KV heads with no exchange, and this build "
+              "measures the single-GPU share.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from paged_kv_cache_101_amd import binding as B
+    from paged_kv_cache_101_amd import workloads as W
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+    B.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    layers = build_layers(args.workload, dev)
+    descs = [B.desc_for(b.k_cache, b.kv_dtype, b.k_scale, b.v_scale) for b in layers]
+    outs = [torch.empty_like(b.q) for b in layers]
+    b0 = layers[0]
+    ws = B.decode_workspace(b0.num_seqs, b0.num_q_heads, b0.num_kv_heads, b0.head_dim,
+                            args.workers, dev)
+    do_append = args.workload == "gqa40"
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    def step(evs=None):
+        for i, b in enumerate(layers):
+            if do_append:
+                B.pkv_kv_append(b.new_k, b.new_v, b.slot_mapping, b.k_cache, b.v_cache, descs[i])
+            if evs is not None:
+                evs[i][0].record(stream)
+            B.pkv_paged_attention_decode(b.q, b.k_cache, b.v_cache, descs[i], b.block_tables,
+                                         b.context_lens, b.scale, outs[i],
+                                         num_workers=args.workers, workspace=ws)
+            if evs is not None:
+                evs[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in layers] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for s in range(args.steps):
+        step(evs[s])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    decode_ms = [a.elapsed_time(b) for st in evs for (a, b) in st]
+    decode_avg_ms = statistics.fmean(decode_ms)
+    kv_bytes_step = sum(b.kv_bytes() for b in layers)
+    kv_bytes_launch = b0.kv_bytes()
+    seqs = b0.num_seqs
+    value = kv_bytes_step / (ms_step * 1e-3) / 1e9
+    achieved = kv_bytes_launch / (decode_avg_ms * 1e-3) / 1e9
+    traffic = load_traffic(args.workload)
+    roofline = {
+        "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+        "kernel": "paged_decode_kernel (one launch per pkv_paged_attention_decode call)",
+        "algorithmic_bytes_per_launch": kv_bytes_launch,
+        "launch_avg_us": round(decode_avg_ms * 1e3, 2),
+        "launch_p10_us": round(sorted(decode_ms)[len(decode_ms) // 10] * 1e3, 2),
+        "launch_p90_us": round(sorted(decode_ms)[(9 * len(decode_ms)) // 10] * 1e3, 2),
+    }
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(b0, args.cpu_seconds)
+    line = {
+        "metric": "paged decode attention: achieved HBM GB/s (% of peak) + decode seqs/sec",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": b0.kv_dtype, "data": "synthetic",
+        "config": describe(args.workload, layers, args.workers),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "decode_seqs_per_s": round(seqs / (ms_step * 1e-3), 1),
+        "kv_bytes_per_step": kv_bytes_step,
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

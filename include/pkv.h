@@ -126,19 +126,19 @@ int pkv_kv_append(const void *k, const void *v, int32_t kv_dtype, const int64_t 
                   int32_t num_tokens, void *k_cache, void *v_cache, const pkv_cache_desc *cache,
                   hipStream_t stream);
 
-/* Workspace bytes pkv_paged_attention_decode needs for a split-KV launch:
- * Pn = ceil(max_blocks_per_seq * 16 / P) partitions per sequence, and when
- * Pn > 1, num_seqs * num_q_heads * Pn * (head_dim + 2) * 4 bytes (float
- * partial outputs, maxima and sums). 0 when Pn == 1 (no workspace needed).
- * partition_size 0 means the library default (512); it must otherwise be a
- * positive multiple of 16 no larger than PKV_MAX_PARTITION. Returns 0 for
- * invalid arguments. */
-size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                  int32_t max_blocks_per_seq, int32_t partition_size);
+/* Largest number of worker waves one decode launch uses. */
+#define PKV_MAX_WORKERS 4096
 
-/* Library default and largest tokens per split-KV partition. */
-#define PKV_DEFAULT_PARTITION 512
-#define PKV_MAX_PARTITION 1024
+/* Workspace bytes pkv_paged_attention_decode needs for this batch shape and
+ * worker count (num_workers 0 = the device default, sized for
+ * PKV_MAX_WORKERS): int32 counters [num_seqs][num_kv_heads] rounded up to 256
+ * bytes, then 2 * workers float partial slots of Gp * head_dim + pad(2 * Gp)
+ * floats each, Gp being G = num_q_heads / num_kv_heads rounded up to 1, 2, 4,
+ * 6 or 8 and pad() rounding up to a multiple of 4. Returns 0 for invalid
+ * arguments (non-positive sizes, G not a whole number or above 8,
+ * num_workers < 0 or > PKV_MAX_WORKERS). */
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t num_workers);
 
 /* Paged decode attention: one new query token per sequence attends over its
  * own cached tokens, read through its block table.
@@ -155,6 +155,13 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  * row. Arithmetic is float32; the result is rounded to nearest-even into
  * q_dtype.
  *
+ * Split-KV: the (sequence, KV head, 16-token block) tiles of the whole batch
+ * are split evenly over num_workers waves, so a long (sequence, KV head) may
+ * be shared by several waves; each leaves a partial (max, sum, accumulator)
+ * and the last one to finish merges them by the log-sum-exp rule. Results
+ * depend on num_workers only through float32 rounding, and are bit-for-bit
+ * repeatable for a fixed num_workers and device.
+ *
  *  q             [num_seqs][num_q_heads][head_dim] in q_dtype (device)
  *  q_dtype       (q, cache) pairs: (F32, F32), (F16, F16), (BF16, BF16),
  *                (F16 or BF16, FP8_E4M3)
@@ -164,17 +171,14 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *                first ceil(n / 16) entries of a row are read
  *  context_lens  int32 [num_seqs] (device)
  *  scale         softmax scale applied to q . k (typically 1/sqrt(head_dim))
- *  partition_size  tokens per split-KV partition: a multiple of 16 up to
- *                PKV_MAX_PARTITION (UNSUPPORTED above), 0 = the default
+ *  num_workers   waves sharing the work: 0 = enough to fill the device,
+ *                otherwise 1..PKV_MAX_WORKERS
  *  workspace, workspace_bytes  at least pkv_decode_workspace_bytes(...) of
- *                16-byte aligned device memory when that is > 0 (may be NULL
- *                when it is 0); contents on entry do not matter. On return
- *                it holds, for R = num_seqs * num_q_heads rows and Pn
- *                partitions: float o[R][Pn][head_dim] (each partition's own
- *                normalised output), then float m[R][Pn] (its max score,
- *                natural-log units), then float l[R][Pn] (its sum of
- *                exp(score - m)); entries of partitions past a sequence's
- *                length are unspecified
+ *                device memory, 256-byte aligned. Its counter region (the
+ *                first num_seqs * num_kv_heads int32, rounded up to 256
+ *                bytes) must be all zero before the first call that uses it;
+ *                every call leaves it zero again. Two calls must not use one
+ *                workspace at the same time.
  *  out           [num_seqs][num_q_heads][head_dim] in q_dtype (device); must
  *                not alias any input or the workspace
  * A sequence whose length exceeds max_blocks_per_seq * 16, or whose needed
@@ -184,7 +188,7 @@ int pkv_paged_attention_decode(const void *q, int32_t q_dtype, int32_t num_seqs,
                                int32_t num_q_heads, const void *k_cache, const void *v_cache,
                                const pkv_cache_desc *cache, const int32_t *block_tables,
                                int32_t max_blocks_per_seq, const int32_t *context_lens,
-                               float scale, int32_t partition_size, void *workspace,
+                               float scale, int32_t num_workers, void *workspace,
                                size_t workspace_bytes, void *out, hipStream_t stream);
 
 /* Gather through the block tables (the same device addressing code as the

@@ -30,6 +30,8 @@ def lib():
             _build.build()
         L = ctypes.CDLL(_build.LIB)
         c_i64, c_int, c_dbl, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_void_p
+        L.oracle_num_threads.argtypes = []
+        L.oracle_num_threads.restype = c_int
         L.oracle_f16_to_double.argtypes = [ctypes.c_uint16]
         L.oracle_f16_to_double.restype = c_dbl
         L.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
@@ -61,7 +63,7 @@ def _ptr(a: np.ndarray):
     return a.ctypes.data_as(ctypes.c_void_p)
 
 
-def _dtype_code(a: np.ndarray, fp8: bool = False) -> int:
+def _dtype_code(a: np.ndarray) -> int:
     if a.dtype == np.float32:
         return F32
     if a.dtype == np.float16:
@@ -71,6 +73,11 @@ def _dtype_code(a: np.ndarray, fp8: bool = False) -> int:
     if a.dtype == np.uint8:
         return FP8
     raise TypeError(f"oracle: unsupported storage dtype {a.dtype}")
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(lib().oracle_num_threads())
 
 
 # ---- element codecs --------------------------------------------------------

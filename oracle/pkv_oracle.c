@@ -36,6 +36,7 @@
  * (blk, g, off, j) sits at ((blk * H_kv + g) * 16 + off) * d + j.
  */
 #include <math.h>
+#include <omp.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <string.h>
@@ -58,6 +59,12 @@ static int elem_size(int dt)
     case OR_FP8: return 1;
     default: return 0;
     }
+}
+
+/* Threads the OpenMP loops below will use. */
+int oracle_num_threads(void)
+{
+    return omp_get_max_threads();
 }
 
 /* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 mantissa bits. */

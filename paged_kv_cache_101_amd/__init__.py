@@ -8,6 +8,7 @@ opened on first use and a missing library raises.
 from .binding import (  # noqa: F401
     PkvError,
     cache_desc,
+    decode_workspace,
     desc_for,
     kv_append,
     paged_attention_decode,

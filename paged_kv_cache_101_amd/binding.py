@@ -26,8 +26,7 @@ PKV_ERR_HIP = -4
 
 PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2, 3
 PKV_BLOCK_SIZE = 16
-PKV_DEFAULT_PARTITION = 512
-PKV_MAX_PARTITION = 1024
+PKV_MAX_WORKERS = 4096
 
 DTYPE_CODES = {"f32": PKV_F32, "f16": PKV_F16, "bf16": PKV_BF16, "fp8": PKV_FP8_E4M3}
 _TORCH_CODES = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
@@ -139,10 +138,19 @@ def pkv_cache_tensor_bytes(desc: pkv_cache_desc) -> int:
     return int(lib().pkv_cache_tensor_bytes(ctypes.byref(desc)))
 
 
-def pkv_decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
-                               max_blocks_per_seq: int, partition_size: int = 0) -> int:
-    return int(lib().pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
-                                                max_blocks_per_seq, partition_size))
+def pkv_decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                               head_dim: int, num_workers: int = 0) -> int:
+    return int(lib().pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                num_workers))
+
+
+def decode_workspace(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                     num_workers: int = 0, device=None) -> torch.Tensor:
+    """A zero-filled decode workspace (its counters must start at zero; every
+    decode call leaves them zero, so it can be reused call after call)."""
+    n = pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, num_workers)
+    _need(n > 0, "invalid decode shape")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
 def pkv_kv_append(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
@@ -164,11 +172,11 @@ def pkv_kv_append(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
 def pkv_paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                                desc: pkv_cache_desc, block_tables: torch.Tensor,
                                context_lens: torch.Tensor, scale: float, out: torch.Tensor,
-                               partition_size: int = 0,
+                               num_workers: int = 0,
                                workspace: Optional[torch.Tensor] = None, stream=None) -> None:
     """q, out: [S][H_q][d]; block_tables: int32 [S][max_blocks]; context_lens: int32 [S].
-    A workspace of pkv_decode_workspace_bytes() bytes is allocated from torch
-    when none is given."""
+    A zero-filled workspace (decode_workspace) is allocated from torch when
+    none is given."""
     S, Hq, d = q.shape
     _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
     _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
@@ -178,13 +186,13 @@ def pkv_paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: 
     for t in (q, k_cache, v_cache, block_tables, context_lens, out):
         _need(t.is_contiguous() and t.is_cuda, "all tensors must be contiguous device tensors")
     mb = block_tables.shape[1]
-    need = pkv_decode_workspace_bytes(S, Hq, d, mb, partition_size)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if workspace is None:
+        workspace = decode_workspace(S, Hq, desc.num_kv_heads, d, num_workers, q.device)
+    _need(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a device tensor")
+    ws_bytes = workspace.numel() * workspace.element_size()
     rc = lib().pkv_paged_attention_decode(
         _ptr(q), _dtype_of(q), S, Hq, _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
-        _ptr(block_tables), mb, _ptr(context_lens), float(scale), partition_size,
+        _ptr(block_tables), mb, _ptr(context_lens), float(scale), num_workers,
         _ptr(workspace), ws_bytes, _ptr(out), _stream(stream))
     _check("pkv_paged_attention_decode", rc)
 

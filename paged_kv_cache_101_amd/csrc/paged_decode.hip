@@ -1,4 +1,4 @@
-// paged_decode.hip -- split-KV paged decode attention for gfx950 (CDNA4).
+// paged_decode.hip -- paged decode attention for gfx950 (CDNA4), one launch.
 //
 // What is computed (ttlab page, sections 2 and 4; drpranayjha page, "How
 // PagedAttention pages the KV cache"; tarundecipher page, "Batching does not
@@ -6,26 +6,33 @@
 // sequence's own K/V rows, found through its block table in a shared pool of
 // 16-token physical blocks; a group of G query heads shares one KV head.
 //
-// Decomposition
-//   * One workgroup (4 waves) owns (sequence s, KV head g, partition j): the
-//     positions [j*P, min((j+1)*P, n)). It reads each K and V tile of that
-//     range once and serves all G query heads of the group from it.
-//   * Tiles are 16 rows x D elements, contiguous. A lane owns 8 consecutive
-//     elements of a row, so D/8 lanes cover a row and one wave instruction
-//     covers 64*8 contiguous elements: every global load is fully coalesced
-//     and goes straight to registers (no LDS staging: each byte is used by
-//     exactly the lanes that loaded it).
+// Work decomposition: a persistent, evenly split tile stream
+//   * A "tile" is one (sequence s, KV head g, logical block b): 16 K rows and
+//     16 V rows of D elements, contiguous in the pool. All tiles of the batch
+//     are numbered s-major, then g, then b. Each worker wave takes an equal
+//     contiguous slice of that numbering (within one tile of every other
+//     wave), whatever the mix of sequence lengths.
+//   * A wave streams its slice: the K and V tiles of the next tile are in
+//     flight while the current one is computed (K of the next is issued as
+//     soon as the current QK is done, V after the current P.V).
+//   * A slice covers whole (s, g) segments and at most two partial ones. A
+//     segment finished by one wave is written out directly. A segment split
+//     over several waves (the split-KV case) leaves one partial (running max
+//     m, sum l, unnormalised accumulator) per wave in the workspace; the last
+//     wave to finish the segment, found with a device-scope counter, merges
+//     them with the log-sum-exp rule and writes the output.
+//   * Tiles are 16 rows x D elements. A lane owns 8 consecutive elements of a
+//     row, so D/8 lanes cover a row and one wave instruction covers 64*8
+//     contiguous elements: every load is coalesced and goes straight to
+//     registers; cache tiles use nontemporal loads (read once).
 //   * QK: per-lane dot products (dot2 instructions for 16-bit data), then a
-//     DPP sum across the D/8 lanes of the row. Scores go to LDS.
-//   * Softmax inside the partition is exact (max over the partition's scores,
-//     then exp2), so no running rescale is needed.
-//   * PV: each lane accumulates p * V for its 8 elements; the rows a wave
-//     covered are summed across lanes, then across waves through LDS.
-//   * Several partitions: (m_j, l_j, o_j) go to the workspace and
-//     lse_reduce_kernel merges them; one partition: the output is written
-//     directly.
-// Positions >= n inside the last block are excluded by select (score -inf,
-// V row zero), never by arithmetic, so garbage or NaN there cannot leak.
+//     DPP sum across the D/8 lanes of the row. Online softmax in log2 units
+//     with a lazily moved maximum; P.V accumulates in float32.
+// Positions >= n inside a sequence's last block are excluded by select
+// (score -inf, V row zero), never by arithmetic, so garbage or NaN there
+// cannot leak.
+#include <atomic>
+
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -37,37 +44,30 @@ struct DecodeParams {
     const uint8_t* v_cache;
     const int32_t* block_tables;
     const int32_t* context_lens;
+    int num_seqs;
     int num_q_heads;
     int num_kv_heads;
     int group;
     int num_blocks;
     int max_blocks_per_seq;
-    int partition_size;
-    int num_partitions;
+    int num_workers;      // waves sharing the tile stream
     float qk_scale_log2;  // scale * k_scale * log2(e)
     float v_scale;
-    float* ws_m;
-    float* ws_l;
-    float* ws_o;
+    int* counters;        // [S][H_kv], zero on entry and on exit
+    float* slots;         // [2 * num_workers][GM * (D + 2)]
     void* out;
 };
 
-constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr int kWavesPerGroup = 4;
 constexpr int kThreads = kWavesPerGroup * kWave;
+constexpr int kPrefetch = 2;  // tiles whose K and V a wave has in flight
 
-template <int KT, int D, int GM>
+template <int KT, int D>
 struct DecodeShape {
     static constexpr int kLanesPerRow = D / kElemsPerLane;          // 16 (D=128) or 8 (D=64)
     static constexpr int kRowsPerInst = kWave / kLanesPerRow;        // 4 or 8
     static constexpr int kInstPerTile = kBlock / kRowsPerInst;       // 4 or 2
-    static constexpr int kTileBytes = kBlock * D * Elem<KT>::bytes;
-    // Tiles a wave holds in registers at once: 32 KiB per wave for up to 4
-    // query heads, 16 KiB above that (the accumulators grow with G).
-    static constexpr int kBudget = (GM <= 4 ? 32768 : 16384);
-    static constexpr int kBlocksPerWave = kBudget / kTileBytes > 0 ? kBudget / kTileBytes : 1;
-    static constexpr int kChunkBlocks = kWavesPerGroup * kBlocksPerWave;
 };
 
 // Query registers: 8 elements per head, kept packed for the dot2 paths.
@@ -119,372 +119,593 @@ struct QRegs<PKV_BF16, PKV_BF16> {
     }
 };
 
-// float32 query (f32 caches, and 16-bit queries over fp8 caches).
-template <int QT, int KT>
-struct QRegsF32 {
+// float32 query over float32 caches.
+template <>
+struct QRegs<PKV_F32, PKV_F32> {
     float v[8];
     __device__ __forceinline__ void load(const uint8_t* p) {
-        Chunk<QT> c = load_chunk<QT>(p);
-        chunk_to_f32<QT>(c, v);
+        Chunk<PKV_F32> c = load_chunk<PKV_F32>(p);
+        chunk_to_f32<PKV_F32>(c, v);
     }
     __device__ __forceinline__ void zero() {
         for (int i = 0; i < 8; ++i) v[i] = 0.f;
     }
-    __device__ __forceinline__ float dot(const Chunk<KT>& k) const {
-        float f[8];
-        chunk_to_f32<KT>(k, f);
+    __device__ __forceinline__ float dot(const Chunk<PKV_F32>& k) const {
         float acc = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc = fmaf(v[i], f[i], acc);
+        for (int i = 0; i < 8; ++i) acc = fmaf(v[i], __builtin_bit_cast(float, k.w[i]), acc);
         return acc;
     }
 };
+
+// 16-bit query over an fp8 cache: the 8 codes of a chunk are widened to the
+// query's type (exact: every E4M3 value is a bf16 and an f16 value; the
+// scaled conversions run with scale 1), then the same dot2 path.
 template <>
-struct QRegs<PKV_F32, PKV_F32> : QRegsF32<PKV_F32, PKV_F32> {};
+struct QRegs<PKV_BF16, PKV_FP8_E4M3> : QRegs<PKV_BF16, PKV_BF16> {
+    __device__ __forceinline__ float dot(const Chunk<PKV_FP8_E4M3>& k) const {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const bf162_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(k.w[i], 1.0f, false);
+            const bf162_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(k.w[i], 1.0f, true);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(lo, v[2 * i], acc, false);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(hi, v[2 * i + 1], acc, false);
+        }
+        return acc;
+    }
+};
+
 template <>
-struct QRegs<PKV_F16, PKV_FP8_E4M3> : QRegsF32<PKV_F16, PKV_FP8_E4M3> {};
-template <>
-struct QRegs<PKV_BF16, PKV_FP8_E4M3> : QRegsF32<PKV_BF16, PKV_FP8_E4M3> {};
-
-template <int KT, int QT, int D, int GM>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
-void paged_decode_partition_kernel(DecodeParams p) {
-    using S = DecodeShape<KT, D, GM>;
-    constexpr int LPR = S::kLanesPerRow;
-    constexpr int RPI = S::kRowsPerInst;
-    constexpr int NI = S::kInstPerTile;
-    constexpr int BPW = S::kBlocksPerWave;
-    constexpr int CHB = S::kChunkBlocks;
-    constexpr int KB = Elem<KT>::bytes;
-    constexpr int QB = Elem<QT>::bytes;
-    constexpr int ROW_BYTES = D * KB;
-
-    extern __shared__ float smem[];
-    float* s_scores = smem;                                   // [P][GM]
-    float* s_acc = smem + (size_t)p.partition_size * GM;      // [waves][GM][D]
-    float* s_ml = s_acc + kWavesPerGroup * GM * D;            // m[GM], l[GM]
-
-    const int j = blockIdx.x;
-    const int g = blockIdx.y;
-    const int s = blockIdx.z;
-    const int lane = lane_id();
-    const int wave = wave_id();
-    const int P = p.partition_size;
-    const int Hq = p.num_q_heads;
-    const int G = p.group;
-    const bool direct = p.num_partitions == 1;
-
-    const int n = p.context_lens[s];
-    const int start = j * P;
-    const bool bad_len = n > p.max_blocks_per_seq * kBlock;
-    if (n <= 0 || bad_len || start >= n) {
-        // Nothing to attend to here. Only a single-partition launch owns the
-        // output row; with several partitions the reduce writes it.
-        if (direct) {
-            const float fill = bad_len ? __builtin_nanf("") : 0.f;
-            for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-                const int h = idx / D, e = idx % D;
-                store_f32_as<QT>(p.out, ((size_t)s * Hq + g * G + h) * D + e, fill);
-            }
+struct QRegs<PKV_F16, PKV_FP8_E4M3> : QRegs<PKV_F16, PKV_F16> {
+    __device__ __forceinline__ float dot(const Chunk<PKV_FP8_E4M3>& k) const {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const half2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(k.w[i], 1.0f, false);
+            const half2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(k.w[i], 1.0f, true);
+            acc = __builtin_amdgcn_fdot2(lo, v[2 * i], acc, false);
+            acc = __builtin_amdgcn_fdot2(hi, v[2 * i + 1], acc, false);
         }
-        return;
+        return acc;
     }
-    const int n_p = min(P, n - start);                 // positions in this partition
-    const int nb = (n_p + kBlock - 1) / kBlock;        // blocks in this partition
-    const int lb0 = start / kBlock;                    // first logical block
-    const int32_t* bt_row = p.block_tables + (size_t)s * p.max_blocks_per_seq + lb0;
+};
 
-    const int row_in_inst = lane / LPR;                // which of the RPI rows
-    const int col = (lane % LPR) * kElemsPerLane;      // first element this lane owns
+// Scores are kept in log2 units; a wave only rescales its running sums when a
+// new score exceeds its running max by more than kLazyRescale (2^8 headroom
+// for the unnormalised weights, far inside float32 range). The result is the
+// same softmax: every weight is exp2(x - m) against one common m per wave.
+constexpr float kLazyRescale = 8.0f;
 
-    // q for the GM heads of this group (heads past G read as zero).
-    QRegs<QT, KT> qr[GM];
+__device__ __forceinline__ int tiles_of(int n, int max_ctx) {
+    return (n > 0 && n <= max_ctx) ? (n + kBlock - 1) / kBlock : 0;
+}
+
+// Sum over the wave, returned as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_sum_int(int v) {
 #pragma unroll
-    for (int h = 0; h < GM; ++h) {
-        if (h < G)
-            qr[h].load(p.q + (((size_t)s * Hq + g * G + h) * D + col) * QB);
-        else
-            qr[h].zero();
+    for (int sh = 1; sh < kWave; sh <<= 1) v += __shfl_xor(v, sh, kWave);
+    return __builtin_amdgcn_readfirstlane(v);
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int u = __shfl_up(v, d, kWave);
+        if (lane >= d) v += u;
     }
+    return v;
+}
 
-    const uint8_t* kbase = p.k_cache + (size_t)(lane / LPR) * ROW_BYTES + col * KB;
-    const uint8_t* vbase = p.v_cache + (size_t)(lane / LPR) * ROW_BYTES + col * KB;
-    const int nchunks = (nb + CHB - 1) / CHB;
-    int bad_block = 0;
-
-    Chunk<KT> reg[BPW][NI];
-    int64_t phys[BPW];
-
-    // ---- phase 1: scores ---------------------------------------------------
-    for (int c = 0; c < nchunks; ++c) {
-        const int b0 = c * CHB + wave * BPW;
+// 8 float32 values rounded into the output type, one 16- or 32-byte store.
+template <int OT>
+__device__ __forceinline__ void store8(void* base, size_t idx, const float* f) {
+    if constexpr (OT == PKV_F32) {
+        float4* d = reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + idx);
+        d[0] = make_float4(f[0], f[1], f[2], f[3]);
+        d[1] = make_float4(f[4], f[5], f[6], f[7]);
+    } else {
+        uint32_t w[4];
 #pragma unroll
-        for (int i = 0; i < BPW; ++i) {
-            const int b = b0 + i;
-            int64_t id = 0;
-            if (b < nb) {
-                id = bt_row[b];
-                if (id < 0 || id >= p.num_blocks) {
-                    bad_block = 1;
-                    id = 0;
-                }
+        for (int i = 0; i < 4; ++i) {
+            uint16_t lo, hi;
+            if constexpr (OT == PKV_F16) {
+                lo = __builtin_bit_cast(uint16_t, (_Float16)f[2 * i]);
+                hi = __builtin_bit_cast(uint16_t, (_Float16)f[2 * i + 1]);
+            } else {
+                lo = f32_to_bf16_rne(f[2 * i]);
+                hi = f32_to_bf16_rne(f[2 * i + 1]);
             }
-            phys[i] = id;
-            if (b < nb) {
-                const uint8_t* t = kbase + cache_row_offset(id, g, 0, p.num_kv_heads, ROW_BYTES);
-#pragma unroll
-                for (int r = 0; r < NI; ++r) reg[i][r] = load_chunk<KT>(t + r * RPI * ROW_BYTES);
-            }
+            w[i] = (uint32_t)lo | ((uint32_t)hi << 16);
         }
-#pragma unroll
-        for (int i = 0; i < BPW; ++i) {
-            const int b = b0 + i;
-            if (b >= nb) break;
-#pragma unroll
-            for (int r = 0; r < NI; ++r) {
-                float part[GM];
-#pragma unroll
-                for (int h = 0; h < GM; ++h) part[h] = group_sum<LPR>(qr[h].dot(reg[i][r]));
-                const int t = b * kBlock + r * RPI + row_in_inst;
-                if (lane % LPR == 0) {
-                    const bool live = t < n_p;
-#pragma unroll
-                    for (int h = 0; h < GM; ++h)
-                        s_scores[t * GM + h] = live ? part[h] * p.qk_scale_log2 : -INFINITY;
-                }
-            }
-        }
-    }
-
-    // Start streaming the first V chunk while the softmax runs.
-    {
-        const int b0 = wave * BPW;
-#pragma unroll
-        for (int i = 0; i < BPW; ++i) {
-            const int b = b0 + i;
-            if (b < nb) {
-                if (nchunks > 1) {
-                    int64_t id = bt_row[b];
-                    phys[i] = (id < 0 || id >= p.num_blocks) ? 0 : id;
-                }
-                const uint8_t* t =
-                    vbase + cache_row_offset(phys[i], g, 0, p.num_kv_heads, ROW_BYTES);
-#pragma unroll
-                for (int r = 0; r < NI; ++r) reg[i][r] = load_chunk<KT>(t + r * RPI * ROW_BYTES);
-            }
-        }
-    }
-
-    bad_block = __syncthreads_or(bad_block);
-
-    // ---- phase 2: softmax of each head over the partition -------------------
-    const int ntok = nb * kBlock;
-    for (int h = wave; h < G; h += kWavesPerGroup) {
-        float mx = -INFINITY;
-        for (int t = lane; t < ntok; t += kWave) mx = fmaxf(mx, s_scores[t * GM + h]);
-        mx = wave_max(mx);
-        float sum = 0.f;
-        for (int t = lane; t < ntok; t += kWave) {
-            const float e = __builtin_amdgcn_exp2f(s_scores[t * GM + h] - mx);
-            s_scores[t * GM + h] = e;
-            sum += e;
-        }
-        sum = wave_sum(sum);
-        if (lane == 0) {
-            s_ml[h] = mx;
-            s_ml[GM + h] = sum;
-        }
-    }
-    __syncthreads();
-
-    // ---- phase 3: P . V ------------------------------------------------------
-    float acc[GM][kElemsPerLane];
-#pragma unroll
-    for (int h = 0; h < GM; ++h)
-#pragma unroll
-        for (int e = 0; e < kElemsPerLane; ++e) acc[h][e] = 0.f;
-
-    for (int c = 0; c < nchunks; ++c) {
-        const int b0 = c * CHB + wave * BPW;
-        if (c > 0) {
-#pragma unroll
-            for (int i = 0; i < BPW; ++i) {
-                const int b = b0 + i;
-                if (b < nb) {
-                    int64_t id = bt_row[b];
-                    id = (id < 0 || id >= p.num_blocks) ? 0 : id;
-                    const uint8_t* t =
-                        vbase + cache_row_offset(id, g, 0, p.num_kv_heads, ROW_BYTES);
-#pragma unroll
-                    for (int r = 0; r < NI; ++r)
-                        reg[i][r] = load_chunk<KT>(t + r * RPI * ROW_BYTES);
-                }
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < BPW; ++i) {
-            const int b = b0 + i;
-            if (b >= nb) break;
-            const bool partial = (b + 1) * kBlock > n_p;
-#pragma unroll
-            for (int r = 0; r < NI; ++r) {
-                const int t = b * kBlock + r * RPI + row_in_inst;
-                float pr[GM];
-#pragma unroll
-                for (int h = 0; h < GM; ++h) pr[h] = s_scores[t * GM + h];
-                float vf[kElemsPerLane];
-                chunk_to_f32<KT>(reg[i][r], vf);
-                if (partial) {
-                    const bool live = t < n_p;
-#pragma unroll
-                    for (int e = 0; e < kElemsPerLane; ++e) vf[e] = live ? vf[e] : 0.f;
-                }
-#pragma unroll
-                for (int h = 0; h < GM; ++h)
-#pragma unroll
-                    for (int e = 0; e < kElemsPerLane; ++e) acc[h][e] = fmaf(pr[h], vf[e], acc[h][e]);
-            }
-        }
-    }
-
-    // Sum the RPI rows of each wave (lanes with equal `col`), then the waves.
-#pragma unroll
-    for (int h = 0; h < GM; ++h)
-#pragma unroll
-        for (int e = 0; e < kElemsPerLane; ++e) {
-            float v = acc[h][e];
-#pragma unroll
-            for (int sh = LPR; sh < kWave; sh <<= 1) v += __shfl_xor(v, sh, kWave);
-            acc[h][e] = v;
-        }
-    if (lane < LPR) {
-#pragma unroll
-        for (int h = 0; h < GM; ++h)
-#pragma unroll
-            for (int e = 0; e < kElemsPerLane; ++e)
-                s_acc[(wave * GM + h) * D + col + e] = acc[h][e];
-    }
-    __syncthreads();
-
-    const float nan = __builtin_nanf("");
-    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-        const int h = idx / D, e = idx % D;
-        float o = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWavesPerGroup; ++w) o += s_acc[(w * GM + h) * D + e];
-        const float l = s_ml[GM + h];
-        o = bad_block ? nan : o * (p.v_scale / l);
-        const size_t row = (size_t)s * Hq + g * G + h;
-        if (direct) {
-            store_f32_as<QT>(p.out, row * D + e, o);
-        } else {
-            p.ws_o[(row * p.num_partitions + j) * D + e] = o;
-            if (e == 0) {
-                p.ws_m[row * p.num_partitions + j] = bad_block ? nan : s_ml[h] * kLn2;
-                p.ws_l[row * p.num_partitions + j] = bad_block ? nan : l;
-            }
-        }
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(base) + idx) =
+            make_uint4(w[0], w[1], w[2], w[3]);
     }
 }
 
-// Merge the partitions of one (sequence, query head):
-//   M = max_j m_j,  w_j = l_j * exp(m_j - M),  out = sum_j w_j o_j / sum_j w_j
-// over the partitions that hold positions (j * P < n).
-template <int OT>
-__global__ __launch_bounds__(128) void lse_reduce_kernel(
-    const float* __restrict__ ws_m, const float* __restrict__ ws_l,
-    const float* __restrict__ ws_o, const int32_t* __restrict__ context_lens, int num_q_heads,
-    int head_dim, int num_partitions, int partition_size, int max_ctx, void* __restrict__ out) {
-    constexpr int kChunk = 512;
-    __shared__ float s_w[kChunk];
-    __shared__ float s_red[2];
-    const int h = blockIdx.x;
-    const int s = blockIdx.y;
-    const int tid = threadIdx.x;
-    const size_t row = (size_t)s * num_q_heads + h;
-    const int n = context_lens[s];
-    if (n <= 0 || n > max_ctx) {
-        const float fill = n <= 0 ? 0.f : __builtin_nanf("");
-        for (int e = tid; e < head_dim; e += blockDim.x) store_f32_as<OT>(out, row * head_dim + e, fill);
-        return;
-    }
-    const int pv = (n + partition_size - 1) / partition_size;
-    const float* m = ws_m + row * num_partitions;
-    const float* l = ws_l + row * num_partitions;
-    const float* o = ws_o + row * num_partitions * head_dim;
+// Partials cross between waves on different XCDs (each XCD has its own L2).
+// They are written and read with agent-scope atomic (write-through, coherent)
+// accesses, and the writer waits for its stores to complete before it bumps
+// the segment counter; no cache writeback or invalidate of a whole L2 (what a
+// device-scope fence costs on this chip) is needed.
+__device__ __forceinline__ void coherent_store(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_load(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
-    float mx = -INFINITY;
-    for (int jj = tid; jj < pv; jj += blockDim.x) mx = fmaxf(mx, m[jj]);
-    mx = wave_max(mx);
-    if ((tid & (kWave - 1)) == 0) s_red[tid / kWave] = mx;
-    __syncthreads();
-    mx = blockDim.x > kWave ? fmaxf(s_red[0], s_red[1]) : s_red[0];
+// The worker wave whose slice [a_w, a_{w+1}) holds tile f, a_w = floor(w*T/NW).
+__device__ __forceinline__ int worker_of(int64_t f, int64_t total, int nw) {
+    return (int)(((f + 1) * nw - 1) / total);
+}
 
-    float acc0 = 0.f, acc1 = 0.f, wsum = 0.f;
-    for (int j0 = 0; j0 < pv; j0 += kChunk) {
-        const int cnt = min(kChunk, pv - j0);
-        __syncthreads();
-        for (int jj = tid; jj < cnt; jj += blockDim.x)
-            s_w[jj] = l[j0 + jj] * __expf(m[j0 + jj] - mx);
-        __syncthreads();
-        for (int jj = 0; jj < cnt; ++jj) {
-            const float w = s_w[jj];
-            wsum += w;
-            const float* oj = o + (size_t)(j0 + jj) * head_dim;
-            if (tid < head_dim) acc0 = fmaf(w, oj[tid], acc0);
-            if (tid + (int)blockDim.x < head_dim) acc1 = fmaf(w, oj[tid + blockDim.x], acc1);
+// Merge the partials of one split segment, left by workers w0..w1 (worker w0
+// in its slot k0, the others in slot 0), into the output rows orow..orow+G-1:
+//   M = max_j m_j,  out = sum_j 2^(m_j - M) acc_j / sum_j 2^(m_j - M) l_j.
+// Lane j reads partial j's maxima and sums; the accumulators of 8 partials
+// are in flight at a time.
+template <int QT, int D, int GM>
+__device__ __forceinline__ void merge_segment(const DecodeParams& p, int w0, int w1,
+                                                        int k0, int G, size_t orow, int lane) {
+    constexpr int SLOT = decode_slot_floats(GM, D);
+    constexpr int PER_LANE = (GM * D + kWave - 1) / kWave;  // accumulator elements per lane
+    const int nparts = w1 - w0 + 1;
+    auto slot_of = [&](int j) {
+        return p.slots + (size_t)(2 * (w0 + j) + (j == 0 ? k0 : 0)) * SLOT;
+    };
+    float mx[GM];
+#pragma unroll
+    for (int h = 0; h < GM; ++h) mx[h] = -INFINITY;
+    for (int j0 = 0; j0 < nparts; j0 += kWave) {
+        const int j = j0 + lane;
+#pragma unroll
+        for (int h = 0; h < GM; ++h) {
+            const float v = j < nparts ? coherent_load(slot_of(j) + GM * D + h) : -INFINITY;
+            mx[h] = fmaxf(mx[h], wave_max(v));
         }
     }
-    if (tid < head_dim) store_f32_as<OT>(out, row * head_dim + tid, acc0 / wsum);
-    if (tid + (int)blockDim.x < head_dim)
-        store_f32_as<OT>(out, row * head_dim + tid + blockDim.x, acc1 / wsum);
+    float lsum[GM], o[PER_LANE];
+#pragma unroll
+    for (int h = 0; h < GM; ++h) lsum[h] = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i) o[i] = 0.f;
+    for (int j0 = 0; j0 < nparts; j0 += kWave) {
+        const int j = j0 + lane;
+        float c[GM];
+#pragma unroll
+        for (int h = 0; h < GM; ++h) {
+            const float* sl = slot_of(min(j, nparts - 1));
+            c[h] = j < nparts ? __builtin_amdgcn_exp2f(coherent_load(sl + GM * D + h) - mx[h]) : 0.f;
+            lsum[h] += wave_sum(j < nparts ? coherent_load(sl + GM * D + GM + h) * c[h] : 0.f);
+        }
+        const int cnt = min(kWave, nparts - j0);
+#pragma unroll 8
+        for (int jj = 0; jj < cnt; ++jj) {
+            const float* sl = slot_of(j0 + jj);
+#pragma unroll
+            for (int i = 0; i < PER_LANE; ++i) {
+                const int idx = i * kWave + lane;       // h * D + e
+                if (idx < GM * D) {
+                    const int cj = __builtin_amdgcn_readlane(
+                        __builtin_bit_cast(int, c[idx / D]), jj);
+                    o[i] = fmaf(__builtin_bit_cast(float, cj), coherent_load(sl + idx), o[i]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i) {
+        const int idx = i * kWave + lane;
+        const int h = idx / D, e = idx % D;
+        if (idx < GM * D && h < G) store_f32_as<QT>(p.out, (orow + h) * D + e, o[i] * (p.v_scale / lsum[h]));
+    }
+}
+
+template <int KT, int QT, int D, int GM>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void paged_decode_kernel(DecodeParams p) {
+    using Shape = DecodeShape<KT, D>;
+    constexpr int LPR = Shape::kLanesPerRow;
+    constexpr int RPI = Shape::kRowsPerInst;
+    constexpr int NI = Shape::kInstPerTile;
+    constexpr int KB = Elem<KT>::bytes;
+    constexpr int QB = Elem<QT>::bytes;
+    constexpr int ROW_BYTES = D * KB;
+    constexpr int SLOT = decode_slot_floats(GM, D);
+
+    const int lane = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kWavesPerGroup) + wave_id());
+    const int nw_launch = p.num_workers;
+    if (w >= nw_launch) return;
+    const int S = p.num_seqs, H = p.num_kv_heads, G = p.group, Hq = p.num_q_heads;
+    const int mb = p.max_blocks_per_seq;
+    const int max_ctx = mb * kBlock;
+    const float nan = __builtin_nanf("");
+
+    // Sequences with no tiles: a zero row (n <= 0) or a NaN row (n longer than
+    // the block-table row). One wave writes each.
+    for (int s = w; s < S; s += nw_launch) {
+        const int n = p.context_lens[s];
+        if (n > 0 && n <= max_ctx) continue;
+        const float fill = n <= 0 ? 0.f : nan;
+        for (int idx = lane; idx < Hq * D; idx += kWave)
+            store_f32_as<QT>(p.out, (size_t)s * Hq * D + idx, fill);
+    }
+
+    // Total tiles T and this wave's slice.
+    int64_t total = 0;
+    for (int base = 0; base < S; base += kWave) {
+        const int s = base + lane;
+        total += wave_sum_int(s < S ? tiles_of(p.context_lens[s], max_ctx) : 0);
+    }
+    total *= H;
+    if (total == 0) return;
+    const int nw = (int)min((int64_t)nw_launch, total);  // every slice non-empty
+    if (w >= nw) return;
+    const int64_t a = (int64_t)w * total / nw;
+    const int64_t b = (int64_t)(w + 1) * total / nw;
+
+    // The sequence holding tile a, and the number of tiles before it.
+    int cs = 0;
+    int64_t seq_base = 0;
+    {
+        int64_t before = 0;
+        for (int base = 0; base < S; base += kWave) {
+            const int s = base + lane;
+            const int t = s < S ? tiles_of(p.context_lens[s], max_ctx) * H : 0;
+            const int incl = wave_inclusive_scan(t, lane);
+            const int64_t lo = before + incl - t;
+            const unsigned long long hit = __ballot(t > 0 && lo <= a && a < before + incl);
+            if (hit) {
+                const int L = __ffsll(hit) - 1;
+                cs = base + L;
+                seq_base = before + __builtin_amdgcn_readlane(incl - t, L);
+                break;
+            }
+            before += __builtin_amdgcn_readlane(incl, kWave - 1);
+        }
+    }
+
+    // A position in the tile stream: segment (s, g) of sequence length n and
+    // nb tiles whose first tile has index seg; block bi; the wave's slice of
+    // the segment ends at block hi. All fields are wave-uniform.
+    struct Cursor {
+        int s, g, n, nb, bi, hi;
+        int64_t seg;
+    };
+    // Move c to the first block of the next segment (order s, then g) inside
+    // the slice; false when the slice has no more tiles.
+    auto next_segment = [&](Cursor& c) -> bool {
+        const int64_t seg = c.seg + c.nb;
+        if (seg >= b) return false;
+        if (c.g + 1 < H) {
+            ++c.g;
+        } else {
+            int s = c.s + 1, n = 0, nb = 0;
+            for (; s < S; ++s) {
+                n = p.context_lens[s];
+                nb = tiles_of(n, max_ctx);
+                if (nb > 0) break;
+            }
+            if (s >= S) return false;  // cannot happen: tiles after seg exist
+            c.s = s;
+            c.g = 0;
+            c.n = n;
+            c.nb = nb;
+        }
+        c.seg = seg;
+        c.bi = 0;
+        c.hi = (int)min((int64_t)c.nb, b - seg);
+        return true;
+    };
+
+    Cursor cc;  // the tile being computed
+    cc.s = cs;
+    cc.n = p.context_lens[cs];
+    cc.nb = tiles_of(cc.n, max_ctx);
+    if (cc.nb == 0) return;  // cannot happen: tile a lies in a non-empty sequence
+    cc.g = (int)((a - seq_base) / cc.nb);
+    cc.bi = (int)((a - seq_base) % cc.nb);
+    cc.seg = seq_base + (int64_t)cc.g * cc.nb;
+    cc.hi = (int)min((int64_t)cc.nb, cc.bi + (b - a));
+    int clo = cc.bi;           // first block of the computed piece
+    bool first_piece = true;   // the piece holding tile a (partial slot 0)
+    bool piece_bad = false;
+
+    Cursor ic = cc;  // the next tile to load (kPrefetch tiles ahead of cc)
+    bool ic_valid = true;
+    // Block id of ic's tile, read with a wave-uniform (scalar) load one tile
+    // before it is needed; -1 marks an id outside the pool. Scalar loads keep
+    // the tile loads' wait counter free of anything but tile data.
+    auto read_id = [&](const Cursor& c) -> int {
+        const int id = p.block_tables[(size_t)c.s * mb + c.bi];
+        return (id < 0 || id >= p.num_blocks) ? -1 : id;
+    };
+    int ic_id = read_id(ic);
+    auto ic_advance = [&]() {
+        if (!ic_valid) return;
+        if (++ic.bi == ic.hi) ic_valid = next_segment(ic);
+        if (ic_valid) ic_id = read_id(ic);
+    };
+
+    const int row = lane / LPR;                        // which of the RPI rows
+    const int col = (lane % LPR) * kElemsPerLane;      // first element this lane owns
+
+    QRegs<QT, KT> qr[GM];
+    auto load_q = [&](int s, int g) {
+#pragma unroll
+        for (int h = 0; h < GM; ++h) {
+            if (h < G)
+                qr[h].load(p.q + (((size_t)s * Hq + g * G + h) * D + col) * QB);
+            else
+                qr[h].zero();
+        }
+    };
+
+    // tile base (wave-uniform, scalar registers) + this lane's byte offset
+    const uint32_t lane_off = (uint32_t)(row * ROW_BYTES + col * KB);
+    Chunk<KT> kr[kPrefetch][NI], vr[kPrefetch][NI];
+    bool slot_bad[kPrefetch];
+    size_t last_off = 0;
+    // Where ic's tile lives; once the slice is exhausted the last tile is
+    // read again, so that every iteration issues the same loads (this keeps
+    // the compiler's memory waits exact).
+    auto ic_offset = [&](bool& bad_tile) -> size_t {
+        bad_tile = false;
+        if (ic_valid) {
+            bad_tile = ic_id < 0;
+            last_off = cache_row_offset(ic_id < 0 ? 0 : ic_id, ic.g, 0, H, ROW_BYTES);
+        }
+        return last_off;
+    };
+    // Each tile is read through its own buffer resource (base = the tile,
+    // 16 rows), nontemporal: every cache byte is used once per call. The
+    // scheduling barriers keep a refill after the last read of the slot it
+    // overwrites, so the ring registers stay put from one pass to the next
+    // (no copies of data still in flight).
+    auto issue_k = [&](int slot, size_t off) {
+        const __amdgpu_buffer_rsrc_t t = make_rsrc(p.k_cache + off, kBlock * ROW_BYTES);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = 0; r < NI; ++r)
+            kr[slot][r] = load_chunk_stream<KT>(t, lane_off + r * RPI * ROW_BYTES);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto issue_v = [&](int slot, size_t off) {
+        const __amdgpu_buffer_rsrc_t t = make_rsrc(p.v_cache + off, kBlock * ROW_BYTES);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = 0; r < NI; ++r)
+            vr[slot][r] = load_chunk_stream<KT>(t, lane_off + r * RPI * ROW_BYTES);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+#pragma unroll
+    for (int slot = 0; slot < kPrefetch; ++slot) {
+        const size_t off = ic_offset(slot_bad[slot]);
+        issue_k(slot, off);
+        issue_v(slot, off);
+        ic_advance();
+    }
+    load_q(cc.s, cc.g);
+
+    float m[GM], l[GM], acc[GM][kElemsPerLane];
+#pragma unroll
+    for (int h = 0; h < GM; ++h) {
+        m[h] = -INFINITY;
+        l[h] = 0.f;
+#pragma unroll
+        for (int e = 0; e < kElemsPerLane; ++e) acc[h][e] = 0.f;
+    }
+    const float qk_scale = p.qk_scale_log2;
+    bool active = true;  // cc holds a tile still to compute
+
+    // Every pass of the loop computes one tile per ring slot and issues the
+    // loads that refill the slot, unconditionally: a pass after the last
+    // tile only re-reads and computes on data nobody keeps. Only the piece
+    // bookkeeping depends on `active`. One back edge with the same loads on
+    // every path lets the compiler wait for exactly the tile it needs.
+    while (active) {
+#pragma unroll
+        for (int slot = 0; slot < kPrefetch; ++slot) {
+            piece_bad |= slot_bad[slot];
+            bool next_bad;
+            const size_t nxt_off = ic_offset(next_bad);
+
+            // ---- one row instruction at a time: QK, online softmax, P.V ----
+            // The next K goes out once the last QK has read this slot's K, the
+            // next V once the last P.V has read this slot's V.
+            const int live_rows = cc.n - cc.bi * kBlock;   // rows < live_rows hold positions < n
+#pragma unroll
+            for (int r = 0; r < NI; ++r) {
+                const bool live = r * RPI + row < live_rows;
+                float x[GM];
+#pragma unroll
+                for (int h = 0; h < GM; ++h) {
+                    x[h] = group_sum<LPR>(qr[h].dot(kr[slot][r])) * qk_scale;
+                    x[h] = live ? x[h] : -INFINITY;
+                }
+                if (r == NI - 1) issue_k(slot, nxt_off);
+#pragma unroll
+                for (int h = 0; h < GM; ++h) {
+                    if (__any(x[h] > m[h] + kLazyRescale)) {
+                        float bm = x[h];
+#pragma unroll
+                        for (int sh = LPR; sh < kWave; sh <<= 1) bm = fmaxf(bm, __shfl_xor(bm, sh, kWave));
+                        const float mn = fmaxf(m[h], bm);
+                        const float c = __builtin_amdgcn_exp2f(m[h] - mn);
+                        l[h] *= c;
+#pragma unroll
+                        for (int e = 0; e < kElemsPerLane; ++e) acc[h][e] *= c;
+                        m[h] = mn;
+                    }
+                }
+                float vf[kElemsPerLane];
+                chunk_to_f32<KT>(vr[slot][r], vf);
+#pragma unroll
+                for (int e = 0; e < kElemsPerLane; ++e) vf[e] = live ? vf[e] : 0.f;
+#pragma unroll
+                for (int h = 0; h < GM; ++h) {
+                    const float pr = __builtin_amdgcn_exp2f(x[h] - m[h]);
+                    l[h] += pr;
+#pragma unroll
+                    for (int e = 0; e < kElemsPerLane; ++e) acc[h][e] = fmaf(pr, vf[e], acc[h][e]);
+                }
+            }
+            issue_v(slot, nxt_off);
+            slot_bad[slot] = next_bad;
+            ic_advance();
+
+            if (!active) continue;
+            if (cc.bi + 1 < cc.hi) {
+                ++cc.bi;
+                continue;
+            }
+
+            // ---- the piece is done: write it out, or leave a partial ----
+            // Sum the rows of the wave (lanes with equal `col` hold different rows).
+#pragma unroll
+            for (int h = 0; h < GM; ++h) {
+#pragma unroll
+                for (int sh = LPR; sh < kWave; sh <<= 1) l[h] += __shfl_xor(l[h], sh, kWave);
+#pragma unroll
+                for (int e = 0; e < kElemsPerLane; ++e) {
+                    float v = acc[h][e];
+#pragma unroll
+                    for (int sh = LPR; sh < kWave; sh <<= 1) v += __shfl_xor(v, sh, kWave);
+                    acc[h][e] = v;
+                }
+            }
+            const size_t orow = (size_t)cc.s * Hq + (size_t)cc.g * G;  // first output row
+            if (clo == 0 && cc.hi == cc.nb) {
+                // the whole segment: normalise and store
+                if (lane < LPR) {
+#pragma unroll
+                    for (int h = 0; h < GM; ++h) {
+                        if (h >= G) break;
+                        float o[kElemsPerLane];
+                        const float sc = p.v_scale / l[h];
+#pragma unroll
+                        for (int e = 0; e < kElemsPerLane; ++e) o[e] = piece_bad ? nan : acc[h][e] * sc;
+                        store8<QT>(p.out, (orow + h) * D + col, o);
+                    }
+                }
+            } else {
+                // partial of a split segment: unnormalised accumulator, max, sum
+                float* slotp = p.slots + (size_t)(2 * w + (first_piece ? 0 : 1)) * SLOT;
+                if (lane < LPR) {
+#pragma unroll
+                    for (int h = 0; h < GM; ++h)
+#pragma unroll
+                        for (int e = 0; e < kElemsPerLane; ++e)
+                            coherent_store(slotp + h * D + col + e, acc[h][e]);
+                }
+                if (lane == 0) {
+#pragma unroll
+                    for (int h = 0; h < GM; ++h) {
+                        coherent_store(slotp + GM * D + h, piece_bad ? nan : m[h]);
+                        coherent_store(slotp + GM * D + GM + h, piece_bad ? nan : l[h]);
+                    }
+                }
+                __builtin_amdgcn_s_waitcnt(0);  // the partial has landed before it is announced
+                int* counter = p.counters + (size_t)cc.s * H + cc.g;
+                int old = 0;
+                if (lane == 0)
+                    old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                old = __builtin_amdgcn_readfirstlane(old);
+                const int w0 = worker_of(cc.seg, total, nw);
+                const int w1 = worker_of(cc.seg + cc.nb - 1, total, nw);
+                if (old == w1 - w0) {
+                    // every partial of the segment is in: merge them (log-sum-exp)
+                    merge_segment<QT, D, GM>(p, w0, w1, (int64_t)w0 * total / nw < cc.seg ? 1 : 0,
+                                             G, orow, lane);
+                    if (lane == 0)  // ready for the next call
+                        __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+
+            // ---- next piece (its first tiles are already in flight) ----
+            if (!next_segment(cc)) {
+                active = false;
+                continue;
+            }
+            clo = 0;
+            first_piece = false;
+            piece_bad = false;
+            load_q(cc.s, cc.g);
+#pragma unroll
+            for (int h = 0; h < GM; ++h) {
+                m[h] = -INFINITY;
+                l[h] = 0.f;
+#pragma unroll
+                for (int e = 0; e < kElemsPerLane; ++e) acc[h][e] = 0.f;
+            }
+        }
+    }
 }
 
 // ---- dispatch ------------------------------------------------------------------
 
 template <int KT, int QT, int D, int GM>
 static hipError_t launch_typed(const DecodeArgs& a) {
+    auto kernel = paged_decode_kernel<KT, QT, D, GM>;
+    int nw = a.num_workers;
+    if (nw == 0) {
+        // fill the device: resident workgroups per CU x CUs x 4 waves
+        static std::atomic<int> per_cu_cache{0};
+        int per_cu = per_cu_cache.load(std::memory_order_relaxed);
+        if (per_cu == 0) {
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) !=
+                    hipSuccess ||
+                per_cu <= 0)
+                per_cu = 1;
+            per_cu_cache.store(per_cu, std::memory_order_relaxed);
+        }
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return hipErrorInvalidDevice;
+        nw = per_cu * cus * kWavesPerGroup;
+        if (nw > kMaxWorkers) nw = kMaxWorkers;
+    }
+    // never more workers than tiles could exist
+    const int64_t tile_bound = (int64_t)a.num_seqs * a.num_kv_heads * a.max_blocks_per_seq;
+    if (nw > tile_bound) nw = (int)tile_bound;
+    if (nw < 1) nw = 1;
+
     DecodeParams p;
     p.q = static_cast<const uint8_t*>(a.q);
     p.k_cache = static_cast<const uint8_t*>(a.k_cache);
     p.v_cache = static_cast<const uint8_t*>(a.v_cache);
     p.block_tables = a.block_tables;
     p.context_lens = a.context_lens;
+    p.num_seqs = a.num_seqs;
     p.num_q_heads = a.num_q_heads;
     p.num_kv_heads = a.num_kv_heads;
     p.group = a.group;
     p.num_blocks = a.num_blocks;
     p.max_blocks_per_seq = a.max_blocks_per_seq;
-    p.partition_size = a.partition_size;
-    p.num_partitions = a.num_partitions;
+    p.num_workers = nw;
     p.qk_scale_log2 = a.scale * (KT == PKV_FP8_E4M3 ? a.k_scale : 1.f) * kLog2e;
     p.v_scale = KT == PKV_FP8_E4M3 ? a.v_scale : 1.f;
-    p.ws_m = a.ws_m;
-    p.ws_l = a.ws_l;
-    p.ws_o = a.ws_o;
+    p.counters = a.counters;
+    p.slots = a.slots;
     p.out = a.out;
-    const size_t smem =
-        ((size_t)a.partition_size * GM + kWavesPerGroup * GM * D + 2 * GM) * sizeof(float);
-    dim3 grid(a.num_partitions, a.num_kv_heads, a.num_seqs);
-    hipLaunchKernelGGL((paged_decode_partition_kernel<KT, QT, D, GM>), grid, dim3(kThreads), smem,
-                       a.stream, p);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess || a.num_partitions == 1) return err;
-    dim3 rgrid(a.num_q_heads, a.num_seqs);
-    hipLaunchKernelGGL((lse_reduce_kernel<QT>), rgrid, dim3(a.head_dim > 64 ? 128 : 64), 0,
-                       a.stream, a.ws_m, a.ws_l, a.ws_o, a.context_lens, a.num_q_heads,
-                       a.head_dim, a.num_partitions, a.partition_size,
-                       a.max_blocks_per_seq * kBlock, a.out);
+    const int grid = (nw + kWavesPerGroup - 1) / kWavesPerGroup;
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, a.stream, p);
     return hipGetLastError();
 }
 
 template <int KT, int QT, int D>
 static hipError_t launch_group(const DecodeArgs& a) {
-    if (a.group <= 1) return launch_typed<KT, QT, D, 1>(a);
-    if (a.group <= 2) return launch_typed<KT, QT, D, 2>(a);
-    if (a.group <= 4) return launch_typed<KT, QT, D, 4>(a);
-    if (a.group <= 6) return launch_typed<KT, QT, D, 6>(a);
-    return launch_typed<KT, QT, D, 8>(a);
+    switch (padded_group(a.group)) {
+    case 1: return launch_typed<KT, QT, D, 1>(a);
+    case 2: return launch_typed<KT, QT, D, 2>(a);
+    case 4: return launch_typed<KT, QT, D, 4>(a);
+    case 6: return launch_typed<KT, QT, D, 6>(a);
+    default: return launch_typed<KT, QT, D, 8>(a);
+    }
 }
 
 template <int KT, int QT>

@@ -35,18 +35,6 @@ int check_cache(const pkv_cache_desc* c) {
     return PKV_OK;
 }
 
-int32_t resolve_partition(int32_t partition_size) {
-    return partition_size == 0 ? PKV_DEFAULT_PARTITION : partition_size;
-}
-
-bool partition_ok(int32_t p) {
-    return p > 0 && p % PKV_BLOCK_SIZE == 0 && p <= pkv::kMaxPartition;
-}
-
-int64_t num_partitions(int32_t max_blocks_per_seq, int32_t p) {
-    return ((int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE + p - 1) / p;
-}
-
 }  // namespace
 
 PKV_EXPORT const char* pkv_status_string(int status) {
@@ -93,15 +81,14 @@ PKV_EXPORT int pkv_kv_append(const void* k, const void* v, int32_t kv_dtype,
 }
 
 PKV_EXPORT size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
-                                             int32_t head_dim, int32_t max_blocks_per_seq,
-                                             int32_t partition_size) {
-    const int32_t p = resolve_partition(partition_size);
-    if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0 ||
-        !partition_ok(p))
+                                             int32_t num_kv_heads, int32_t head_dim,
+                                             int32_t num_workers) {
+    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > 8 || num_workers < 0 ||
+        num_workers > pkv::kMaxWorkers)
         return 0;
-    const int64_t pn = num_partitions(max_blocks_per_seq, p);
-    if (pn <= 1) return 0;
-    return (size_t)num_seqs * num_q_heads * pn * (head_dim + 2) * sizeof(float);
+    return pkv::decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                       num_workers == 0 ? pkv::kMaxWorkers : num_workers);
 }
 
 PKV_EXPORT int pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t num_seqs,
@@ -110,13 +97,14 @@ PKV_EXPORT int pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_
                                           const int32_t* block_tables,
                                           int32_t max_blocks_per_seq,
                                           const int32_t* context_lens, float scale,
-                                          int32_t partition_size, void* workspace,
+                                          int32_t num_workers, void* workspace,
                                           size_t workspace_bytes, void* out,
                                           hipStream_t stream) {
     int rc = check_cache(cache);
     if (rc != PKV_OK) return rc;
     if (num_seqs <= 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0)
         return PKV_ERR_INVALID_ARG;
+    if ((int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE > INT32_MAX) return PKV_ERR_UNSUPPORTED;
     if (num_q_heads % cache->num_kv_heads != 0) return PKV_ERR_INVALID_ARG;
     const int group = num_q_heads / cache->num_kv_heads;
     if (group > 8) return PKV_ERR_UNSUPPORTED;
@@ -132,11 +120,12 @@ PKV_EXPORT int pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
         return PKV_ERR_INVALID_ARG;
     if (!(scale == scale)) return PKV_ERR_INVALID_ARG;
-    const int32_t p = resolve_partition(partition_size);
-    if (p <= 0 || p % PKV_BLOCK_SIZE != 0) return PKV_ERR_INVALID_ARG;
-    if (p > pkv::kMaxPartition) return PKV_ERR_UNSUPPORTED;
-    const int64_t pn = num_partitions(max_blocks_per_seq, p);
-    if (pn > 65535) return PKV_ERR_UNSUPPORTED;  // grid x limit for one launch
+    if (num_workers < 0) return PKV_ERR_INVALID_ARG;
+    if (num_workers > pkv::kMaxWorkers) return PKV_ERR_UNSUPPORTED;
+    const size_t need = pkv_decode_workspace_bytes(num_seqs, num_q_heads, cache->num_kv_heads,
+                                                   cache->head_dim, num_workers);
+    if (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
+        return PKV_ERR_WORKSPACE;
 
     pkv::DecodeArgs a{};
     a.q = q;
@@ -156,20 +145,12 @@ PKV_EXPORT int pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_
     a.scale = scale;
     a.k_scale = cache->k_scale;
     a.v_scale = cache->v_scale;
-    a.partition_size = p;
-    a.num_partitions = (int)pn;
+    a.num_workers = num_workers;
+    a.counters = static_cast<int*>(workspace);
+    a.slots = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                       pkv::decode_counter_bytes(num_seqs, cache->num_kv_heads));
     a.out = out;
     a.stream = stream;
-    if (pn > 1) {
-        const size_t need = pkv_decode_workspace_bytes(num_seqs, num_q_heads, cache->head_dim,
-                                                       max_blocks_per_seq, p);
-        if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))
-            return PKV_ERR_WORKSPACE;
-        const size_t rows = (size_t)num_seqs * num_q_heads * pn;
-        a.ws_o = static_cast<float*>(workspace);
-        a.ws_m = a.ws_o + rows * cache->head_dim;
-        a.ws_l = a.ws_m + rows;
-    }
     hipError_t err = pkv::launch_paged_decode(a);
     return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }

@@ -15,6 +15,8 @@ constexpr int kWave = 64;               // CDNA wavefront width
 constexpr int kElemsPerLane = 8;        // cache elements a lane owns per row chunk
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
 
 template <int DT>
@@ -51,20 +53,65 @@ struct Chunk {
     uint32_t w[dwords];
 };
 
-template <int DT>
+// Loads of 8 elements through a plain pointer (optionally nontemporal).
+template <typename V>
+__device__ __forceinline__ V load_vec(const uint8_t* p, bool stream) {
+    const V* q = reinterpret_cast<const V*>(p);
+    return stream ? __builtin_nontemporal_load(q) : *q;
+}
+
+template <int DT, bool STREAM = false>
 __device__ __forceinline__ Chunk<DT> load_chunk(const uint8_t* p) {
     Chunk<DT> c;
     if constexpr (Chunk<DT>::dwords == 8) {
-        uint4 a = *reinterpret_cast<const uint4*>(p);
-        uint4 b = *reinterpret_cast<const uint4*>(p + 16);
-        c.w[0] = a.x; c.w[1] = a.y; c.w[2] = a.z; c.w[3] = a.w;
-        c.w[4] = b.x; c.w[5] = b.y; c.w[6] = b.z; c.w[7] = b.w;
+        u32x4_t a = load_vec<u32x4_t>(p, STREAM);
+        u32x4_t b = load_vec<u32x4_t>(p + 16, STREAM);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            c.w[i] = a[i];
+            c.w[4 + i] = b[i];
+        }
     } else if constexpr (Chunk<DT>::dwords == 4) {
-        uint4 a = *reinterpret_cast<const uint4*>(p);
-        c.w[0] = a.x; c.w[1] = a.y; c.w[2] = a.z; c.w[3] = a.w;
+        u32x4_t a = load_vec<u32x4_t>(p, STREAM);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c.w[i] = a[i];
     } else {
-        uint2 a = *reinterpret_cast<const uint2*>(p);
-        c.w[0] = a.x; c.w[1] = a.y;
+        u32x2_t a = load_vec<u32x2_t>(p, STREAM);
+        c.w[0] = a[0];
+        c.w[1] = a[1];
+    }
+    return c;
+}
+
+// Buffer resource for `bytes` bytes at `base` (raw, untyped dwords). Loads
+// through it outside [0, bytes) return zero instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// 8 elements at byte `voff` of a buffer, nontemporal (streamed past the
+// caches). The address lives in one 32-bit VGPR plus the scalar resource.
+template <int DT>
+__device__ __forceinline__ Chunk<DT> load_chunk_stream(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    constexpr int kNontemporal = 2;
+    Chunk<DT> c;
+    if constexpr (Chunk<DT>::dwords == 8) {
+        u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kNontemporal);
+        u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, 0, kNontemporal);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            c.w[i] = a[i];
+            c.w[4 + i] = b[i];
+        }
+    } else if constexpr (Chunk<DT>::dwords == 4) {
+        u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kNontemporal);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c.w[i] = a[i];
+    } else {
+        u32x2_t a = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, kNontemporal);
+        c.w[0] = a[0];
+        c.w[1] = a[1];
     }
     return c;
 }

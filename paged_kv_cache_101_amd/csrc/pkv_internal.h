@@ -9,8 +9,27 @@
 
 namespace pkv {
 
-// Tokens of one partition are scored into LDS, so a partition is bounded.
-constexpr int kMaxPartition = PKV_MAX_PARTITION;
+// Worker waves of one decode launch (the device default fills every CU).
+constexpr int kMaxWorkers = PKV_MAX_WORKERS;
+
+// Query heads per KV head are handled in register groups of 1, 2, 4, 6 or 8.
+constexpr int padded_group(int g) { return g <= 1 ? 1 : g <= 2 ? 2 : g <= 4 ? 4 : g <= 6 ? 6 : 8; }
+
+// One partial in the decode workspace: the unnormalised accumulator of GM
+// heads x D, then GM maxima and GM sums, padded to a multiple of 4 floats.
+constexpr int decode_slot_floats(int gm, int d) { return gm * d + ((2 * gm + 3) & ~3); }
+
+// Decode workspace: int32 counters [S][H_kv] (rounded up to 256 bytes), then
+// 2 * workers partial slots.
+inline size_t decode_counter_bytes(int num_seqs, int num_kv_heads) {
+    return (((size_t)num_seqs * num_kv_heads * sizeof(int32_t)) + 255) & ~(size_t)255;
+}
+inline size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
+                                     int head_dim, int workers) {
+    const int gm = padded_group(num_q_heads / num_kv_heads);
+    return decode_counter_bytes(num_seqs, num_kv_heads) +
+           (size_t)2 * workers * decode_slot_floats(gm, head_dim) * sizeof(float);
+}
 
 struct DecodeArgs {
     const void* q;
@@ -30,11 +49,9 @@ struct DecodeArgs {
     float scale;
     float k_scale;
     float v_scale;
-    int partition_size;
-    int num_partitions;
-    float* ws_m;  // [S][H_q][Pn] (natural-log units), only when Pn > 1
-    float* ws_l;  // [S][H_q][Pn]
-    float* ws_o;  // [S][H_q][Pn][D]
+    int num_workers;  // 0 = fill the device
+    int* counters;    // [S][H_kv], zero on entry
+    float* slots;     // partial slots
     void* out;
     hipStream_t stream;
 };

@@ -96,7 +96,6 @@ class DecodeBatch:
     scale: float
     k_scale: float = 1.0
     v_scale: float = 1.0
-    partition_size: int = 512
     new_k: Optional[torch.Tensor] = None   # [T][H_kv][d]
     new_v: Optional[torch.Tensor] = None
     slot_mapping: Optional[torch.Tensor] = None  # int64 [T]
@@ -170,7 +169,7 @@ def make_batch(name: str, case_id: int, context_lens: Sequence[int], num_q_heads
                device="cpu", layer: int = 0, num_blocks: Optional[int] = None,
                pool_factor: float = 1.0, shared_prefix_blocks: int = 0,
                max_blocks: Optional[int] = None, canary: bool = False,
-               append_last: bool = False, partition_size: int = 512,
+               append_last: bool = False,
                scale: Optional[float] = None, structure_layer: Optional[int] = None) -> DecodeBatch:
     """Build one decode batch.
 
@@ -241,7 +240,7 @@ def make_batch(name: str, case_id: int, context_lens: Sequence[int], num_q_heads
         context_lens=torch.from_numpy(ctx.astype(np.int32)).to(device),
         block_tables=torch.from_numpy(bt).to(device), q=q, k_cache=k_cache, v_cache=v_cache,
         scale=scale if scale is not None else 1.0 / math.sqrt(head_dim),
-        k_scale=k_scale, v_scale=v_scale, partition_size=partition_size,
+        k_scale=k_scale, v_scale=v_scale,
         new_k=new_k, new_v=new_v, slot_mapping=slot_mapping,
         meta={"case_id": case_id, "layer": layer, "shared_prefix_blocks": shared_prefix_blocks})
 
@@ -299,6 +298,6 @@ def prefix_shared(device="cpu", canary=False, num_seqs=256, prefix=2048) -> Deco
 
 def fp8_long(device="cpu", canary=False, num_seqs=16, ctx=32768) -> DecodeBatch:
     """16 sequences of 32768 tokens, 64 query / 8 KV heads, d 128, fp8 E4M3FN
-    KV with one scale per tensor, bf16 q/out, 512-token partitions."""
+    KV with one scale per tensor, bf16 q/out."""
     return make_batch("fp8-long", 5, [ctx] * num_seqs, 64, 8, 128, "fp8", "bf16", device=device,
                       canary=canary)

@@ -37,12 +37,12 @@ def gpu_append(b: W.DecodeBatch):
     B.pkv_kv_append(b.new_k, b.new_v, b.slot_mapping, b.k_cache, b.v_cache, desc(b))
 
 
-def gpu_decode(b: W.DecodeBatch, partition_size=None, out=None) -> torch.Tensor:
+def gpu_decode(b: W.DecodeBatch, num_workers=0, out=None, workspace=None) -> torch.Tensor:
     if out is None:
         out = torch.empty_like(b.q)
-    P = b.partition_size if partition_size is None else partition_size
     B.pkv_paged_attention_decode(b.q, b.k_cache, b.v_cache, desc(b), b.block_tables,
-                                 b.context_lens, b.scale, out, partition_size=P)
+                                 b.context_lens, b.scale, out, num_workers=num_workers,
+                                 workspace=workspace)
     return out
 
 

@@ -53,19 +53,29 @@ def test_cache_tensor_bytes():
     assert B.pkv_cache_tensor_bytes(d) == 0
 
 
+def _slot_floats(gp, d):
+    return gp * d + ((2 * gp + 3) // 4) * 4
+
+
 def test_workspace_bytes_formula():
-    # 40 sequences x 32 heads x 16 partitions x (128 + 2) floats
-    assert B.pkv_decode_workspace_bytes(40, 32, 128, 512, 512) == 40 * 32 * 16 * 130 * 4
-    assert B.pkv_decode_workspace_bytes(40, 32, 128, 512, 0) == 40 * 32 * 16 * 130 * 4
-    assert B.pkv_decode_workspace_bytes(16, 64, 128, 2048, 512) == 16 * 64 * 64 * 130 * 4
-    assert B.pkv_decode_workspace_bytes(4, 4, 64, 3, 512) == 0      # one partition
-    assert B.pkv_decode_workspace_bytes(4, 4, 64, 3, 24) == 0       # not a multiple of 16
-    assert B.pkv_decode_workspace_bytes(4, 4, 64, 3, 2048) == 0     # above the maximum
+    # counters [S][H_kv] int32 rounded up to 256 B, then 2 slots per worker
+    ctr = -(-40 * 8 * 4 // 256) * 256
+    assert B.pkv_decode_workspace_bytes(40, 32, 8, 128, 2048) == ctr + 2 * 2048 * _slot_floats(4, 128) * 4
+    assert B.pkv_decode_workspace_bytes(40, 32, 8, 128, 0) == ctr + 2 * 4096 * _slot_floats(4, 128) * 4
+    # G = 6 and G = 5 use 6-head slots, G = 3 uses 4, G = 7 uses 8
+    assert B.pkv_decode_workspace_bytes(64, 12, 2, 128, 10) == 512 + 20 * _slot_floats(6, 128) * 4
+    assert B.pkv_decode_workspace_bytes(1, 5, 1, 64, 1) == 256 + 2 * _slot_floats(6, 64) * 4
+    assert B.pkv_decode_workspace_bytes(1, 3, 1, 64, 1) == 256 + 2 * _slot_floats(4, 64) * 4
+    assert B.pkv_decode_workspace_bytes(1, 7, 1, 64, 1) == 256 + 2 * _slot_floats(8, 64) * 4
+    assert B.pkv_decode_workspace_bytes(4, 4, 3, 64, 1) == 0        # 4 % 3 != 0
+    assert B.pkv_decode_workspace_bytes(4, 18, 2, 64, 1) == 0       # G = 9
+    assert B.pkv_decode_workspace_bytes(4, 4, 1, 64, -1) == 0
+    assert B.pkv_decode_workspace_bytes(4, 4, 1, 64, B.PKV_MAX_WORKERS + 1) == 0
 
 
 def _decode(**kw):
     a = dict(q=FAKE, q_dtype=B.PKV_F16, S=4, Hq=8, k=FAKE, v=FAKE,
-             desc=B.cache_desc(16, 2, 128, "f16"), bt=FAKE, mb=64, cl=FAKE, scale=0.1, P=512,
+             desc=B.cache_desc(16, 2, 128, "f16"), bt=FAKE, mb=64, cl=FAKE, scale=0.1, P=0,
              ws=None, ws_bytes=0, out=FAKE)
     a.update(kw)
     return B.lib().pkv_paged_attention_decode(
@@ -88,10 +98,11 @@ def _decode(**kw):
     (dict(desc=B.cache_desc(16, 2, 128, "fp8", 0.0, 1.0), q_dtype=B.PKV_BF16),
      B.PKV_ERR_INVALID_ARG),                                  # fp8 needs positive scales
     (dict(q_dtype=7), B.PKV_ERR_UNSUPPORTED),
-    (dict(P=24), B.PKV_ERR_INVALID_ARG),
-    (dict(P=2048), B.PKV_ERR_UNSUPPORTED),
-    (dict(ws=None, ws_bytes=0), B.PKV_ERR_WORKSPACE),         # 2 partitions need one
+    (dict(P=-1), B.PKV_ERR_INVALID_ARG),                      # negative worker count
+    (dict(P=B.PKV_MAX_WORKERS + 1), B.PKV_ERR_UNSUPPORTED),
+    (dict(ws=None, ws_bytes=0), B.PKV_ERR_WORKSPACE),         # a workspace is always needed
     (dict(ws=FAKE, ws_bytes=100), B.PKV_ERR_WORKSPACE),
+    (dict(ws=FAKE + 16, ws_bytes=1 << 30), B.PKV_ERR_WORKSPACE),  # not 256-byte aligned
     (dict(q=FAKE + 4), B.PKV_ERR_INVALID_ARG),                # misaligned
     (dict(scale=float("nan")), B.PKV_ERR_INVALID_ARG),
 ])

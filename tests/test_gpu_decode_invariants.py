@@ -3,8 +3,8 @@
 The kernel's arithmetic depends only on each sequence's logical token order,
 never on where the blocks sit in the pool, so permuting physical blocks,
 sharing vs copying a prefix and repeating a run must give identical bytes.
-Changing the partition size reorders the float32 sums, so it is checked
-against the oracle's tolerance instead."""
+Changing the number of workers moves the split points and so reorders the
+float32 sums; it is checked against the oracle's tolerance instead."""
 import numpy as np
 import pytest
 import torch
@@ -19,11 +19,11 @@ def _same_bytes(a: torch.Tensor, b: torch.Tensor) -> bool:
     return W.to_numpy(a).tobytes() == W.to_numpy(b).tobytes()
 
 
-@pytest.mark.parametrize("P", [64, 512])
-def test_block_permutation_is_bitwise_invariant(gpu, P):
+@pytest.mark.parametrize("nw", [0, 9])
+def test_block_permutation_is_bitwise_invariant(gpu, nw):
     b = W.make_batch("perm", 81, [1, 16, 33, 700, 2049], 12, 2, 128, "bf16", "bf16", device=gpu,
                      pool_factor=2.0, canary=True)
-    base = gpu_decode(b, P)
+    base = gpu_decode(b, nw)
     perm = torch.from_numpy(np.random.default_rng(5).permutation(b.num_blocks)).to(gpu)
     kc = torch.empty_like(b.k_cache)
     vc = torch.empty_like(b.v_cache)
@@ -31,7 +31,7 @@ def test_block_permutation_is_bitwise_invariant(gpu, P):
     vc[perm] = b.v_cache
     moved = W.DecodeBatch(**{**b.__dict__, "k_cache": kc, "v_cache": vc,
                              "block_tables": perm[b.block_tables.long()].to(torch.int32)})
-    out = gpu_decode(moved, P)
+    out = gpu_decode(moved, nw)
     torch.cuda.synchronize()
     assert _same_bytes(base, out)
 
@@ -58,8 +58,8 @@ def test_shared_prefix_equals_private_copies(gpu):
     copied = W.DecodeBatch(**{**b.__dict__, "k_cache": kc, "v_cache": vc,
                               "num_blocks": kc.shape[0],
                               "block_tables": torch.from_numpy(bt2).to(gpu)})
-    for P in (64, 512):
-        assert _same_bytes(gpu_decode(b, P), gpu_decode(copied, P))
+    for nw in (0, 13):
+        assert _same_bytes(gpu_decode(b, nw), gpu_decode(copied, nw))
 
 
 def test_repeat_runs_are_bitwise_identical(gpu):
@@ -71,16 +71,20 @@ def test_repeat_runs_are_bitwise_identical(gpu):
 
 def test_batch_order_permutes_rows(gpu):
     b = W.make_batch("order", 83, [5, 900, 64, 1500, 17], 8, 1, 128, "f16", "f16", device=gpu)
-    base = gpu_decode(b)
     p = torch.tensor([3, 0, 4, 1, 2], device=gpu)
     pb = W.DecodeBatch(**{**b.__dict__, "q": b.q[p].contiguous(),
                           "block_tables": b.block_tables[p].contiguous(),
                           "context_lens": b.context_lens[p].contiguous()})
-    assert _same_bytes(gpu_decode(pb), base[p].contiguous())
+    # one worker never splits a sequence, so the arithmetic of every row is
+    # the same whatever the order: identical bytes
+    assert _same_bytes(gpu_decode(pb, 1), gpu_decode(b, 1)[p].contiguous())
+    # with the default split the rows move and stay within tolerance
+    ref = oracle_decode(b)
+    assert_close(out_to_f64(gpu_decode(pb)), ref[p.cpu().numpy()], "f16", "permuted batch")
 
 
-def test_partition_size_changes_only_rounding(gpu):
+def test_worker_count_changes_only_rounding(gpu):
     b = W.make_batch("parts", 84, [3000, 4096, 77], 32, 8, 128, "f16", "f16", device=gpu)
     ref = oracle_decode(b)
-    for P in (16, 48, 128, 512, 1024):
-        assert_close(out_to_f64(gpu_decode(b, P)), ref, "f16", f"P={P}")
+    for nw in (1, 2, 3, 48, 128, 1000, 0):
+        assert_close(out_to_f64(gpu_decode(b, nw)), ref, "f16", f"workers={nw}")

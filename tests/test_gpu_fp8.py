@@ -15,7 +15,7 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("q_dtype,v_scale", [("bf16", 1.0), ("bf16", 0.25), ("f16", 2.0 ** -3)])
-@pytest.mark.parametrize("P", [16, 512])
+@pytest.mark.parametrize("P", [0, 3])
 def test_single_token_returns_every_code_exactly(gpu, q_dtype, v_scale, P):
     finite = [c for c in range(256) if c not in (0x7F, 0xFF)]
     assert len(finite) == 254
@@ -28,13 +28,13 @@ def test_single_token_returns_every_code_exactly(gpu, q_dtype, v_scale, P):
     vc[2, 0, 0] = torch.from_numpy(codes[0]).to(gpu)
     vc[2, 1, 0] = torch.from_numpy(codes[1]).to(gpu)
     kc[2, :, 0] = 0x38  # 1.0
-    bt = torch.tensor([[2, 1, 3]], dtype=torch.int32, device=gpu)  # P = 16: 3 partitions, 2 empty
+    bt = torch.tensor([[2, 1, 3]], dtype=torch.int32, device=gpu)
     cl = torch.tensor([1], dtype=torch.int32, device=gpu)
     tdt = torch.bfloat16 if q_dtype == "bf16" else torch.float16
     q = torch.randn((1, Hq, d), device=gpu).to(tdt)
     out = torch.empty_like(q)
     desc = B.cache_desc(nb, H, d, "fp8", 0.5, v_scale)
-    B.pkv_paged_attention_decode(q, kc, vc, desc, bt, cl, 0.1, out, partition_size=P)
+    B.pkv_paged_attention_decode(q, kc, vc, desc, bt, cl, 0.1, out, num_workers=P)
     torch.cuda.synchronize()
     got = out.to(torch.float64).cpu().numpy()
     for h in range(Hq):
