@@ -73,7 +73,7 @@ def load_traffic(workload: str):
                 rec = json.loads(line)
     if rec is None or rec.get("kernel_hash") != kernel_hash():
         return None
-    return rec.get("traffic_bytes_per_launch")
+    return rec.get("traffic_bytes_per_launch", {}).get("total")
 
 
 def copy_calibration(mib: int):
