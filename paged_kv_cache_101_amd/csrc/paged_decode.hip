@@ -61,7 +61,7 @@ struct DecodeParams {
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr int kWavesPerGroup = 4;
 constexpr int kThreads = kWavesPerGroup * kWave;
-constexpr int kPrefetch = 2;  // tiles whose K and V a wave has in flight
+constexpr int kPrefetch = 1;  // tiles whose K and V a wave has in flight
 
 template <int KT, int D>
 struct DecodeShape {
@@ -235,6 +235,23 @@ __device__ __forceinline__ float coherent_load(const float* p) {
     return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// A wave-uniform read of an input table the kernel never writes (block
+// tables, context lengths): through the constant address space it becomes a
+// scalar load, which leaves the vector-memory wait counter to the tile data.
+__device__ __forceinline__ int32_t uniform_read(const int32_t* base, size_t i) {
+    return ((const __attribute__((address_space(4))) int32_t*)base)[i];
+}
+
+// Everything that computes v[] happens before this point, and no memory
+// access moves across it. Placed between the last read of a ring slot and the
+// loads that refill it, it keeps the old and the new contents of the slot from
+// being live at once, so the refill can land in the same registers.
+template <int N>
+__device__ __forceinline__ void settle(float (&v)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]) : : "memory");
+}
+
 // The worker wave whose slice [a_w, a_{w+1}) holds tile f, a_w = floor(w*T/NW).
 __device__ __forceinline__ int worker_of(int64_t f, int64_t total, int nw) {
     return (int)(((f + 1) * nw - 1) / total);
@@ -249,7 +266,8 @@ template <int QT, int D, int GM>
 __device__ __forceinline__ void merge_segment(const DecodeParams& p, int w0, int w1,
                                                         int k0, int G, size_t orow, int lane) {
     constexpr int SLOT = decode_slot_floats(GM, D);
-    constexpr int PER_LANE = (GM * D + kWave - 1) / kWave;  // accumulator elements per lane
+    static_assert(D % kWave == 0, "head size must be a multiple of the wave width");
+    constexpr int PER_LANE = GM * D / kWave;  // accumulator elements per lane
     const int nparts = w1 - w0 + 1;
     auto slot_of = [&](int j) {
         return p.slots + (size_t)(2 * (w0 + j) + (j == 0 ? k0 : 0)) * SLOT;
@@ -287,8 +305,10 @@ __device__ __forceinline__ void merge_segment(const DecodeParams& p, int w0, int
             for (int i = 0; i < PER_LANE; ++i) {
                 const int idx = i * kWave + lane;       // h * D + e
                 if (idx < GM * D) {
+                    // D is a multiple of the wave width, so the head of
+                    // element idx is (i * kWave) / D: known at compile time
                     const int cj = __builtin_amdgcn_readlane(
-                        __builtin_bit_cast(int, c[idx / D]), jj);
+                        __builtin_bit_cast(int, c[(i * kWave) / D]), jj);
                     o[i] = fmaf(__builtin_bit_cast(float, cj), coherent_load(sl + idx), o[i]);
                 }
             }
@@ -297,7 +317,7 @@ __device__ __forceinline__ void merge_segment(const DecodeParams& p, int w0, int
 #pragma unroll
     for (int i = 0; i < PER_LANE; ++i) {
         const int idx = i * kWave + lane;
-        const int h = idx / D, e = idx % D;
+        const int h = (i * kWave) / D, e = idx % D;
         if (idx < GM * D && h < G) store_f32_as<QT>(p.out, (orow + h) * D + e, o[i] * (p.v_scale / lsum[h]));
     }
 }
@@ -384,7 +404,7 @@ void paged_decode_kernel(DecodeParams p) {
         } else {
             int s = c.s + 1, n = 0, nb = 0;
             for (; s < S; ++s) {
-                n = p.context_lens[s];
+                n = uniform_read(p.context_lens, s);
                 nb = tiles_of(n, max_ctx);
                 if (nb > 0) break;
             }
@@ -402,7 +422,7 @@ void paged_decode_kernel(DecodeParams p) {
 
     Cursor cc;  // the tile being computed
     cc.s = cs;
-    cc.n = p.context_lens[cs];
+    cc.n = uniform_read(p.context_lens, cs);
     cc.nb = tiles_of(cc.n, max_ctx);
     if (cc.nb == 0) return;  // cannot happen: tile a lies in a non-empty sequence
     cc.g = (int)((a - seq_base) / cc.nb);
@@ -419,7 +439,7 @@ void paged_decode_kernel(DecodeParams p) {
     // before it is needed; -1 marks an id outside the pool. Scalar loads keep
     // the tile loads' wait counter free of anything but tile data.
     auto read_id = [&](const Cursor& c) -> int {
-        const int id = p.block_tables[(size_t)c.s * mb + c.bi];
+        const int id = uniform_read(p.block_tables, (size_t)c.s * mb + c.bi);
         return (id < 0 || id >= p.num_blocks) ? -1 : id;
     };
     int ic_id = read_id(ic);
@@ -447,33 +467,37 @@ void paged_decode_kernel(DecodeParams p) {
     const uint32_t lane_off = (uint32_t)(row * ROW_BYTES + col * KB);
     Chunk<KT> kr[kPrefetch][NI], vr[kPrefetch][NI];
     bool slot_bad[kPrefetch];
-    size_t last_off = 0;
-    // Where ic's tile lives; once the slice is exhausted the last tile is
-    // read again, so that every iteration issues the same loads (this keeps
-    // the compiler's memory waits exact).
-    auto ic_offset = [&](bool& bad_tile) -> size_t {
-        bad_tile = false;
-        if (ic_valid) {
-            bad_tile = ic_id < 0;
-            last_off = cache_row_offset(ic_id < 0 ? 0 : ic_id, ic.g, 0, H, ROW_BYTES);
-        }
-        return last_off;
+    // Where ic's tile lives, and how many of its bytes to read: a whole tile,
+    // or none once the slice is exhausted or the block id is outside the pool
+    // (such a tile's piece is written as NaN). Every iteration issues the
+    // same loads either way, which keeps the compiler's memory waits exact;
+    // a load past a buffer resource's size returns zeros without touching
+    // memory.
+    struct TileRef {
+        size_t off;
+        uint32_t bytes;
+    };
+    auto ic_tile = [&](bool& bad_tile) -> TileRef {
+        bad_tile = ic_valid && ic_id < 0;
+        if (!ic_valid || ic_id < 0) return TileRef{0, 0u};
+        return TileRef{cache_row_offset(ic_id, ic.g, 0, H, ROW_BYTES),
+                       (uint32_t)(kBlock * ROW_BYTES)};
     };
     // Each tile is read through its own buffer resource (base = the tile,
     // 16 rows), nontemporal: every cache byte is used once per call. The
     // scheduling barriers keep a refill after the last read of the slot it
     // overwrites, so the ring registers stay put from one pass to the next
     // (no copies of data still in flight).
-    auto issue_k = [&](int slot, size_t off) {
-        const __amdgpu_buffer_rsrc_t t = make_rsrc(p.k_cache + off, kBlock * ROW_BYTES);
+    auto issue_k = [&](int slot, TileRef t_) {
+        const __amdgpu_buffer_rsrc_t t = make_rsrc(p.k_cache + t_.off, t_.bytes);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int r = 0; r < NI; ++r)
             kr[slot][r] = load_chunk_stream<KT>(t, lane_off + r * RPI * ROW_BYTES);
         __builtin_amdgcn_sched_barrier(0);
     };
-    auto issue_v = [&](int slot, size_t off) {
-        const __amdgpu_buffer_rsrc_t t = make_rsrc(p.v_cache + off, kBlock * ROW_BYTES);
+    auto issue_v = [&](int slot, TileRef t_) {
+        const __amdgpu_buffer_rsrc_t t = make_rsrc(p.v_cache + t_.off, t_.bytes);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int r = 0; r < NI; ++r)
@@ -481,14 +505,16 @@ void paged_decode_kernel(DecodeParams p) {
         __builtin_amdgcn_sched_barrier(0);
     };
 
+    // The query first: the oldest load in flight, so the first tile's wait
+    // covers it and the loop never has to wait for everything.
+    load_q(cc.s, cc.g);
 #pragma unroll
     for (int slot = 0; slot < kPrefetch; ++slot) {
-        const size_t off = ic_offset(slot_bad[slot]);
-        issue_k(slot, off);
-        issue_v(slot, off);
+        const TileRef t = ic_tile(slot_bad[slot]);
+        issue_k(slot, t);
+        issue_v(slot, t);
         ic_advance();
     }
-    load_q(cc.s, cc.g);
 
     float m[GM], l[GM], acc[GM][kElemsPerLane];
 #pragma unroll
@@ -501,6 +527,17 @@ void paged_decode_kernel(DecodeParams p) {
     const float qk_scale = p.qk_scale_log2;
     bool active = true;  // cc holds a tile still to compute
 
+    // Split segments whose partials this wave was the last to deliver. Only
+    // the first and the last piece of a slice can be partial, so there are at
+    // most two; they are merged after the stream, which keeps the merge's
+    // loads and registers out of the streaming loop.
+    struct Pending {
+        int s, g, nb;
+        int64_t seg;
+    };
+    Pending pend0{}, pend1{};
+    int npend = 0;
+
     // Every pass of the loop computes one tile per ring slot and issues the
     // loads that refill the slot, unconditionally: a pass after the last
     // tile only re-reads and computes on data nobody keeps. Only the piece
@@ -511,7 +548,7 @@ void paged_decode_kernel(DecodeParams p) {
         for (int slot = 0; slot < kPrefetch; ++slot) {
             piece_bad |= slot_bad[slot];
             bool next_bad;
-            const size_t nxt_off = ic_offset(next_bad);
+            const TileRef nxt = ic_tile(next_bad);
 
             // ---- one row instruction at a time: QK, online softmax, P.V ----
             // The next K goes out once the last QK has read this slot's K, the
@@ -526,7 +563,10 @@ void paged_decode_kernel(DecodeParams p) {
                     x[h] = group_sum<LPR>(qr[h].dot(kr[slot][r])) * qk_scale;
                     x[h] = live ? x[h] : -INFINITY;
                 }
-                if (r == NI - 1) issue_k(slot, nxt_off);
+                if (r == NI - 1) {
+                    settle(x);
+                    issue_k(slot, nxt);
+                }
 #pragma unroll
                 for (int h = 0; h < GM; ++h) {
                     if (__any(x[h] > m[h] + kLazyRescale)) {
@@ -545,6 +585,7 @@ void paged_decode_kernel(DecodeParams p) {
                 chunk_to_f32<KT>(vr[slot][r], vf);
 #pragma unroll
                 for (int e = 0; e < kElemsPerLane; ++e) vf[e] = live ? vf[e] : 0.f;
+                if (r == NI - 1) settle(vf);
 #pragma unroll
                 for (int h = 0; h < GM; ++h) {
                     const float pr = __builtin_amdgcn_exp2f(x[h] - m[h]);
@@ -553,7 +594,7 @@ void paged_decode_kernel(DecodeParams p) {
                     for (int e = 0; e < kElemsPerLane; ++e) acc[h][e] = fmaf(pr, vf[e], acc[h][e]);
                 }
             }
-            issue_v(slot, nxt_off);
+            issue_v(slot, nxt);
             slot_bad[slot] = next_bad;
             ic_advance();
 
@@ -616,12 +657,10 @@ void paged_decode_kernel(DecodeParams p) {
                 old = __builtin_amdgcn_readfirstlane(old);
                 const int w0 = worker_of(cc.seg, total, nw);
                 const int w1 = worker_of(cc.seg + cc.nb - 1, total, nw);
-                if (old == w1 - w0) {
-                    // every partial of the segment is in: merge them (log-sum-exp)
-                    merge_segment<QT, D, GM>(p, w0, w1, (int64_t)w0 * total / nw < cc.seg ? 1 : 0,
-                                             G, orow, lane);
-                    if (lane == 0)  // ready for the next call
-                        __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (old == w1 - w0) {  // every partial of the segment is in
+                    const Pending pd{cc.s, cc.g, cc.nb, cc.seg};
+                    if (npend == 0) pend0 = pd; else pend1 = pd;
+                    ++npend;
                 }
             }
 
@@ -634,6 +673,9 @@ void paged_decode_kernel(DecodeParams p) {
             first_piece = false;
             piece_bad = false;
             load_q(cc.s, cc.g);
+            // The query has landed before this path joins the streaming one,
+            // so the join does not make every tile wait for all loads.
+            __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
             for (int h = 0; h < GM; ++h) {
                 m[h] = -INFINITY;
@@ -642,6 +684,19 @@ void paged_decode_kernel(DecodeParams p) {
                 for (int e = 0; e < kElemsPerLane; ++e) acc[h][e] = 0.f;
             }
         }
+    }
+
+    // Merge the split segments this wave completed (log-sum-exp over the
+    // partials) and leave their counters at zero for the next call.
+    for (int i = 0; i < npend; ++i) {
+        const Pending& pd = i == 0 ? pend0 : pend1;
+        const int w0 = worker_of(pd.seg, total, nw);
+        const int w1 = worker_of(pd.seg + pd.nb - 1, total, nw);
+        const int k0 = (int64_t)w0 * total / nw < pd.seg ? 1 : 0;
+        merge_segment<QT, D, GM>(p, w0, w1, k0, G, (size_t)pd.s * Hq + (size_t)pd.g * G, lane);
+        if (lane == 0)
+            __hip_atomic_store(p.counters + (size_t)pd.s * H + pd.g, 0, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -666,7 +721,9 @@ static hipError_t launch_typed(const DecodeArgs& a) {
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return hipErrorInvalidDevice;
-        nw = per_cu * cus * kWavesPerGroup;
+        // two workgroups (8 waves) per CU: measured best on the 40 x 8192 GQA
+        // shape; more waves only add contention for the vector ALUs
+        nw = (per_cu < 2 ? per_cu : 2) * cus * kWavesPerGroup;
         if (nw > kMaxWorkers) nw = kMaxWorkers;
     }
     // never more workers than tiles could exist
