@@ -174,6 +174,16 @@ def main():
     dev = torch.device("cuda:0")
     layers = build_layers(args.workload, dev)
     descs = [B.desc_for(b.k_cache, b.kv_dtype, b.k_scale, b.v_scale) for b in layers]
+    # The library's caches, filled from each layer's token rows with
+    # pkv_kv_append (the row-order copies are dropped after, except layer 0's,
+    # which the CPU baseline reads).
+    caches = []
+    for i, b in enumerate(layers):
+        caches.append(B.fill_cache(b.k_cache, b.v_cache, descs[i]))
+        if i > 0:
+            b.k_cache = b.v_cache = None
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     outs = [torch.empty_like(b.q) for b in layers]
     b0 = layers[0]
     ws = B.decode_workspace(b0.num_seqs, b0.num_q_heads, b0.num_kv_heads, b0.head_dim,
@@ -185,10 +195,10 @@ def main():
     def step(evs=None):
         for i, b in enumerate(layers):
             if do_append:
-                B.pkv_kv_append(b.new_k, b.new_v, b.slot_mapping, b.k_cache, b.v_cache, descs[i])
+                B.pkv_kv_append(b.new_k, b.new_v, b.slot_mapping, *caches[i], descs[i])
             if evs is not None:
                 evs[i][0].record(stream)
-            B.pkv_paged_attention_decode(b.q, b.k_cache, b.v_cache, descs[i], b.block_tables,
+            B.pkv_paged_attention_decode(b.q, *caches[i], descs[i], b.block_tables,
                                          b.context_lens, b.scale, outs[i],
                                          num_workers=args.workers, workspace=ws)
             if evs is not None:

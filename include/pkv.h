@@ -32,10 +32,18 @@
  *    kernels skip such slots and turn such sequences into NaN rows, as
  *    documented per call.
  *
- * KV cache layout (one tensor each for K and V, same shape):
- *     cache[num_blocks][num_kv_heads][16][head_dim]
- * element (blk, g, off, j) at ((blk * num_kv_heads + g) * 16 + off) * head_dim
- * + j. One (block, KV head) tile is 16 * head_dim elements, contiguous.
+ * KV cache layout (one tensor each for K and V, same size):
+ *     num_blocks * num_kv_heads * 16 * head_dim elements.
+ * One (block, KV head) tile -- the 16 token rows of that block for that KV
+ * head, 16 * head_dim elements -- is contiguous, tile (blk, g) first element
+ * at (blk * num_kv_heads + g) * 16 * head_dim. Inside a tile, row `off`
+ * (0..15), element j (0..head_dim-1) is at
+ *     K: ((j / 8) * 16 + off) * 8 + j % 8    (8-element slabs, token-minor)
+ *     V: j * 16 + off                        (element-major)
+ * an order chosen so that the decode kernel's matrix-core operands load as
+ * contiguous runs. Only the library writes this order (pkv_kv_append) and
+ * reads it (decode, pkv_debug_gather): callers pass whole rows in and get
+ * whole rows out, and need the layout only to size the tensors.
  * Token position t of a sequence lives in physical block
  * block_tables[s][t / 16], row t % 16 ([ttlab] section 4: logical block ->
  * physical block through the request's block table). A slot is the flat row
@@ -114,7 +122,9 @@ size_t pkv_cache_tensor_bytes(const pkv_cache_desc *cache);
  *  k, v          [num_tokens][num_kv_heads][head_dim] in kv_dtype (device)
  *  kv_dtype      must equal cache->dtype: the rows are copied byte for byte
  *  slot_mapping  int64 [num_tokens] (device). Token i goes to block
- *                slot / 16, row slot % 16, for every KV head. A negative
+ *                slot / 16, row slot % 16, for every KV head (stored in the
+ *                in-tile order above; filling every slot of a pool from
+ *                row-order data is how a caller builds a cache). A negative
  *                slot skips the token; a slot >= num_blocks * 16 is also
  *                skipped (precondition violation, never written).
  *  num_tokens    >= 0 (0 is a no-op that still validates)

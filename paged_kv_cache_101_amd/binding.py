@@ -210,6 +210,43 @@ def pkv_debug_gather(k_cache: torch.Tensor, v_cache: torch.Tensor, desc: pkv_cac
     _check("pkv_debug_gather", rc)
 
 
+def fill_cache(k_blocks: torch.Tensor, v_blocks: torch.Tensor, desc: pkv_cache_desc,
+               stream=None):
+    """Cache tensors holding the given block contents.
+
+    k_blocks, v_blocks: [num_blocks][H_kv][16][d] in the cache dtype, the token
+    rows of every block in order (unused rows included). Every row is written
+    with pkv_kv_append at slot block * 16 + row, the way a prefill fills a
+    cache. The returned tensors have the same shape and dtype; their bytes are
+    in the library's in-block layout (include/pkv.h), not in row order."""
+    nb, H, B, d = k_blocks.shape
+    _need(v_blocks.shape == k_blocks.shape and B == PKV_BLOCK_SIZE,
+          "blocks must be [num_blocks][H_kv][16][d]")
+    rows_k = k_blocks.permute(0, 2, 1, 3).reshape(nb * B, H, d).contiguous()
+    rows_v = v_blocks.permute(0, 2, 1, 3).reshape(nb * B, H, d).contiguous()
+    slots = torch.arange(nb * B, dtype=torch.int64, device=k_blocks.device)
+    k_cache = torch.empty_like(k_blocks)
+    v_cache = torch.empty_like(v_blocks)
+    pkv_kv_append(rows_k, rows_v, slots, k_cache, v_cache, desc, stream)
+    return k_cache, v_cache
+
+
+def read_cache(k_cache: torch.Tensor, v_cache: torch.Tensor, desc: pkv_cache_desc,
+               stream=None):
+    """The inverse of fill_cache: the [num_blocks][H_kv][16][d] token rows of
+    every block, read with pkv_debug_gather through one block table that lists
+    the whole pool in order."""
+    nb, H, B, d = k_cache.shape
+    dev = k_cache.device
+    bt = torch.arange(nb, dtype=torch.int32, device=dev).view(1, nb)
+    ctx = torch.tensor([nb * B], dtype=torch.int32, device=dev)
+    k_out = torch.empty((1, H, nb * B, d), dtype=k_cache.dtype, device=dev)
+    v_out = torch.empty_like(k_out)
+    pkv_debug_gather(k_cache, v_cache, desc, bt, ctx, nb * B, k_out, v_out, stream)
+    return (k_out.view(H, nb, B, d).permute(1, 0, 2, 3).contiguous(),
+            v_out.view(H, nb, B, d).permute(1, 0, 2, 3).contiguous())
+
+
 # Names as the pages' problem statement gives them.
 kv_append = pkv_kv_append
 paged_attention_decode = pkv_paged_attention_decode

@@ -7,29 +7,40 @@
 // 16-token physical blocks; a group of G query heads shares one KV head.
 //
 // Work decomposition: a persistent, evenly split tile stream
-//   * A "tile" is one (sequence s, KV head g, logical block b): 16 K rows and
-//     16 V rows of D elements, contiguous in the pool. All tiles of the batch
-//     are numbered s-major, then g, then b. Each worker wave takes an equal
-//     contiguous slice of that numbering (within one tile of every other
+//   * A "tile" is one (sequence s, KV head g, logical block b): 16 tokens of K
+//     and of V, D elements each, contiguous in the pool. All tiles of the
+//     batch are numbered s-major, then g, then b. Each worker wave takes an
+//     equal contiguous slice of that numbering (within one tile of every other
 //     wave), whatever the mix of sequence lengths.
-//   * A wave streams its slice: the K and V tiles of the next tile are in
-//     flight while the current one is computed (K of the next is issued as
-//     soon as the current QK is done, V after the current P.V).
+//   * A wave streams its slice: the next tile's K is in flight while the
+//     current tile's scores and softmax are computed, its V while the current
+//     P.V runs. Cache tiles use nontemporal loads (read once).
 //   * A slice covers whole (s, g) segments and at most two partial ones. A
 //     segment finished by one wave is written out directly. A segment split
 //     over several waves (the split-KV case) leaves one partial (running max
 //     m, sum l, unnormalised accumulator) per wave in the workspace; the last
 //     wave to finish the segment, found with a device-scope counter, merges
 //     them with the log-sum-exp rule and writes the output.
-//   * Tiles are 16 rows x D elements. A lane owns 8 consecutive elements of a
-//     row, so D/8 lanes cover a row and one wave instruction covers 64*8
-//     contiguous elements: every load is coalesced and goes straight to
-//     registers; cache tiles use nontemporal loads (read once).
-//   * QK: per-lane dot products (dot2 instructions for 16-bit data), then a
-//     DPP sum across the D/8 lanes of the row. Online softmax in log2 units
-//     with a lazily moved maximum; P.V accumulates in float32.
+//
+// Per tile, both contractions run on the matrix cores, in the operand layouts
+// of the 16x16 MFMA shapes (lane l: column/row l % 16, k-group l / 16):
+//   * QK^T as S^T = K_tile (16 tokens x D) . Q^T (D x 16 head columns, the G
+//     query heads of the KV head, zero-padded): D/32 MFMA 16x16x32 (16-bit),
+//     each lane feeding one token's 8-element K slab straight from its load.
+//     Lane l ends with the scores of head l % 16 for tokens 4*(l/16) + j.
+//   * Those four scores per lane are exactly the A operand of P.V:
+//     O (16 heads x D) += P (16 x 16 tokens) . V_tile (16 tokens x D), as D/16
+//     MFMA 16x16x16 whose B operand is 4 tokens of one element row of V,
+//     again straight from the load (V is stored element-major in the tile).
+//   * Softmax is online in log2 units with a lazily moved maximum: the scores
+//     of a tile only trigger a rescale (a wave-uniform branch with the
+//     cross-lane max) when one exceeds the running max by more than 8.
+//   * P is rounded to the query's 16-bit type for the P.V operand, and the sum
+//     l accumulates the rounded weights, so the output is an exactly
+//     normalised average. float32 caches use the float32 MFMA (16x16x4) and
+//     keep P in float32. fp8 K/V are widened exactly to the query's type.
 // Positions >= n inside a sequence's last block are excluded by select
-// (score -inf, V row zero), never by arithmetic, so garbage or NaN there
+// (score -inf, V element zero), never by arithmetic, so garbage or NaN there
 // cannot leak.
 #include <atomic>
 
@@ -59,123 +70,221 @@ struct DecodeParams {
 };
 
 constexpr float kLog2e = 1.44269504088896340736f;
-constexpr int kWavesPerGroup = 4;
+constexpr int kWavesPerGroup = 1;  // one worker wave per workgroup: any count spreads evenly
 constexpr int kThreads = kWavesPerGroup * kWave;
 constexpr int kPrefetch = 1;  // tiles whose K and V a wave has in flight
 
-template <int KT, int D>
-struct DecodeShape {
-    static constexpr int kLanesPerRow = D / kElemsPerLane;          // 16 (D=128) or 8 (D=64)
-    static constexpr int kRowsPerInst = kWave / kLanesPerRow;        // 4 or 8
-    static constexpr int kInstPerTile = kBlock / kRowsPerInst;       // 4 or 2
-};
-
-// Query registers: 8 elements per head, kept packed for the dot2 paths.
-template <int QT, int KT>
-struct QRegs;
-
-template <>
-struct QRegs<PKV_F16, PKV_F16> {
-    half2_t v[4];
-    __device__ __forceinline__ void load(const uint8_t* p) {
-        uint4 a = *reinterpret_cast<const uint4*>(p);
-        v[0] = __builtin_bit_cast(half2_t, a.x);
-        v[1] = __builtin_bit_cast(half2_t, a.y);
-        v[2] = __builtin_bit_cast(half2_t, a.z);
-        v[3] = __builtin_bit_cast(half2_t, a.w);
-    }
-    __device__ __forceinline__ void zero() {
-        for (int i = 0; i < 4; ++i) v[i] = half2_t{0, 0};
-    }
-    __device__ __forceinline__ float dot(const Chunk<PKV_F16>& k) const {
-        float acc = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, k.w[i]), v[i], acc, false);
-        return acc;
-    }
-};
-
-template <>
-struct QRegs<PKV_BF16, PKV_BF16> {
-    bf162_t v[4];
-    __device__ __forceinline__ void load(const uint8_t* p) {
-        uint4 a = *reinterpret_cast<const uint4*>(p);
-        v[0] = __builtin_bit_cast(bf162_t, a.x);
-        v[1] = __builtin_bit_cast(bf162_t, a.y);
-        v[2] = __builtin_bit_cast(bf162_t, a.z);
-        v[3] = __builtin_bit_cast(bf162_t, a.w);
-    }
-    __device__ __forceinline__ void zero() {
-        for (int i = 0; i < 4; ++i) v[i] = __builtin_bit_cast(bf162_t, 0u);
-    }
-    __device__ __forceinline__ float dot(const Chunk<PKV_BF16>& k) const {
-        float acc = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, k.w[i]), v[i], acc,
-                                                  false);
-        return acc;
-    }
-};
-
-// float32 query over float32 caches.
-template <>
-struct QRegs<PKV_F32, PKV_F32> {
-    float v[8];
-    __device__ __forceinline__ void load(const uint8_t* p) {
-        Chunk<PKV_F32> c = load_chunk<PKV_F32>(p);
-        chunk_to_f32<PKV_F32>(c, v);
-    }
-    __device__ __forceinline__ void zero() {
-        for (int i = 0; i < 8; ++i) v[i] = 0.f;
-    }
-    __device__ __forceinline__ float dot(const Chunk<PKV_F32>& k) const {
-        float acc = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc = fmaf(v[i], __builtin_bit_cast(float, k.w[i]), acc);
-        return acc;
-    }
-};
-
-// 16-bit query over an fp8 cache: the 8 codes of a chunk are widened to the
-// query's type (exact: every E4M3 value is a bf16 and an f16 value; the
-// scaled conversions run with scale 1), then the same dot2 path.
-template <>
-struct QRegs<PKV_BF16, PKV_FP8_E4M3> : QRegs<PKV_BF16, PKV_BF16> {
-    __device__ __forceinline__ float dot(const Chunk<PKV_FP8_E4M3>& k) const {
-        float acc = 0.f;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const bf162_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(k.w[i], 1.0f, false);
-            const bf162_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(k.w[i], 1.0f, true);
-            acc = __builtin_amdgcn_fdot2_f32_bf16(lo, v[2 * i], acc, false);
-            acc = __builtin_amdgcn_fdot2_f32_bf16(hi, v[2 * i + 1], acc, false);
-        }
-        return acc;
-    }
-};
-
-template <>
-struct QRegs<PKV_F16, PKV_FP8_E4M3> : QRegs<PKV_F16, PKV_F16> {
-    __device__ __forceinline__ float dot(const Chunk<PKV_FP8_E4M3>& k) const {
-        float acc = 0.f;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const half2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(k.w[i], 1.0f, false);
-            const half2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(k.w[i], 1.0f, true);
-            acc = __builtin_amdgcn_fdot2(lo, v[2 * i], acc, false);
-            acc = __builtin_amdgcn_fdot2(hi, v[2 * i + 1], acc, false);
-        }
-        return acc;
-    }
-};
-
 // Scores are kept in log2 units; a wave only rescales its running sums when a
 // new score exceeds its running max by more than kLazyRescale (2^8 headroom
-// for the unnormalised weights, far inside float32 range). The result is the
-// same softmax: every weight is exp2(x - m) against one common m per wave.
+// for the unnormalised weights, far inside float32 and f16 range). The result
+// is the same softmax: every weight is exp2(x - m) against one common m.
 constexpr float kLazyRescale = 8.0f;
+
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// N dwords at byte `voff` of a buffer resource, nontemporal.
+template <int N>
+__device__ __forceinline__ void load_dwords(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t* w) {
+    constexpr int kNontemporal = 2;
+    if constexpr (N == 1) {
+        w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, kNontemporal);
+    } else if constexpr (N == 2) {
+        const u32x2_t a = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, kNontemporal);
+        w[0] = a[0];
+        w[1] = a[1];
+    } else {
+        static_assert(N % 4 == 0, "dword count");
+#pragma unroll
+        for (int c = 0; c < N / 4; ++c) {
+            const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16 * c, 0, kNontemporal);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[4 * c + i] = a[i];
+        }
+    }
+}
+
+// The per-tile matrix work for cache type KT and query type QT.
+//   K: NK loads per lane, load i = the 8-element slab (l/16) + 4i of token l%16;
+//   V: NVL loads per lane, load i = tokens 4*(l/16) .. +3 of element columns
+//      16*(2i) + l%16 and 16*(2i+1) + l%16 (one 8-element run of the tile).
+template <int KT, int QT, int D>
+struct TileMath {
+    static constexpr int KB = Elem<KT>::bytes;
+    static constexpr int QB = Elem<QT>::bytes;
+    static constexpr int NK = D / 32;
+    static constexpr int NV = D / 16;   // P.V blocks of 16 element columns
+    static constexpr int NVL = D / 32;  // V loads (two blocks each)
+    static constexpr int KW = 2 * KB;   // dwords per K load (8 elements)
+    static constexpr int VW = KB;       // dwords of one block's 4 tokens
+    static constexpr int VLW = 2 * VW;  // dwords per V load (8 elements)
+    static constexpr bool kF32 = (KT == PKV_F32);
+    static constexpr int QW = 8 * QB / 4;  // dwords per query slab
+
+    // Query slabs of head l % 16 matching the K loads (zero for padded heads).
+    struct Q {
+        uint32_t w[NK][QW];
+    };
+
+    __device__ static void load_q(Q& q, const uint8_t* row, bool valid, int g4) {
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+            if (valid) {
+                const uint4* src = reinterpret_cast<const uint4*>(row + (size_t)8 * (g4 + 4 * i) * QB);
+#pragma unroll
+                for (int c = 0; c < QW / 4; ++c) {
+                    const uint4 a = src[c];
+                    q.w[i][4 * c] = a.x;
+                    q.w[i][4 * c + 1] = a.y;
+                    q.w[i][4 * c + 2] = a.z;
+                    q.w[i][4 * c + 3] = a.w;
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < QW; ++c) q.w[i][c] = 0u;
+            }
+        }
+    }
+
+    // Two fp8 codes (bytes 0-1, or 2-3 with `hi`) as two elements of the 16-bit
+    // compute type, packed in one dword. Exact: every E4M3 value is an f16
+    // and a bf16 value (the scaled conversion runs with scale 1).
+    template <bool HI>
+    __device__ static uint32_t widen_fp8_pair(uint32_t w) {
+        if constexpr (QT == PKV_F16)
+            return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+        else
+            return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+    }
+
+    // 8 K elements (one slab entry) in the 16-bit compute type.
+    template <typename V8>
+    __device__ static V8 k_operand(const uint32_t* kw) {
+        if constexpr (KT == PKV_FP8_E4M3) {
+            u32x4_t u;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                u[2 * i] = widen_fp8_pair<false>(kw[i]);
+                u[2 * i + 1] = widen_fp8_pair<true>(kw[i]);
+            }
+            return __builtin_bit_cast(V8, u);
+        } else {
+            const u32x4_t u = {kw[0], kw[1], kw[2], kw[3]};
+            return __builtin_bit_cast(V8, u);
+        }
+    }
+
+    // S^T (tokens 4*(l/16) + j, head l % 16) of one tile.
+    __device__ static f32x4_t qk(const uint32_t (&kr)[NK][KW], const Q& q) {
+        f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+            if constexpr (kF32) {
+                // k index of MFMA e is element 8*(l/16 + 4i) + e of token / head
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    s = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, kr[i][e]),
+                                                             __builtin_bit_cast(float, q.w[i][e]),
+                                                             s, 0, 0, 0);
+            } else if constexpr (QT == PKV_F16) {
+                const u32x4_t qu = {q.w[i][0], q.w[i][1], q.w[i][2], q.w[i][3]};
+                s = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<f16x8_t>(kr[i]),
+                                                           __builtin_bit_cast(f16x8_t, qu), s, 0, 0,
+                                                           0);
+            } else {
+                const u32x4_t qu = {q.w[i][0], q.w[i][1], q.w[i][2], q.w[i][3]};
+                s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<bf16x8_t>(kr[i]),
+                                                            __builtin_bit_cast(bf16x8_t, qu), s, 0,
+                                                            0, 0);
+            }
+        }
+        return s;
+    }
+
+    // Zero the V elements of tokens this lane holds at or past the live count
+    // (nlive = live tokens among its four, any integer).
+    __device__ static void mask_v(uint32_t (&vr)[NVL][VLW], int nlive) {
+        uint32_t m[VW];
+        if constexpr (VW == 1) {
+            m[0] = nlive >= 4 ? ~0u : nlive <= 0 ? 0u : (1u << (8 * nlive)) - 1u;
+        } else if constexpr (VW == 2) {
+            m[0] = nlive >= 2 ? ~0u : nlive == 1 ? 0xFFFFu : 0u;
+            m[1] = nlive >= 4 ? ~0u : nlive == 3 ? 0xFFFFu : 0u;
+        } else {
+#pragma unroll
+            for (int i = 0; i < VW; ++i) m[i] = i < nlive ? ~0u : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < NVL; ++j)
+#pragma unroll
+            for (int i = 0; i < VLW; ++i) vr[j][i] &= m[i % VW];
+    }
+
+    // o[j] (heads 4*(l/16) + r, element 16j + l%16) += P . V_tile; returns the
+    // sum of this lane's four weights as they entered the product.
+    // (block j's 4 tokens: dwords (j % 2) * VW .. of load j / 2)
+    __device__ static float pv(const float (&pr)[4], const uint32_t (&vr)[NVL][VLW], f32x4_t (&o)[NV]) {
+        if constexpr (kF32) {
+#pragma unroll
+            for (int j = 0; j < NV; ++j)
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+                    o[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                        pr[kk], __builtin_bit_cast(float, vr[j / 2][(j % 2) * VW + kk]), o[j], 0, 0, 0);
+            return (pr[0] + pr[1]) + (pr[2] + pr[3]);
+        } else if constexpr (QT == PKV_F16) {
+            const f16x4_t a = {(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3]};
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                f16x4_t b;
+                const uint32_t* vj = &vr[j / 2][(j % 2) * VW];
+                if constexpr (KT == PKV_FP8_E4M3) {
+                    const u32x2_t u = {widen_fp8_pair<false>(vj[0]), widen_fp8_pair<true>(vj[0])};
+                    b = __builtin_bit_cast(f16x4_t, u);
+                } else {
+                    const u32x2_t u = {vj[0], vj[1]};
+                    b = __builtin_bit_cast(f16x4_t, u);
+                }
+                o[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, o[j], 0, 0, 0);
+            }
+            return ((float)a[0] + (float)a[1]) + ((float)a[2] + (float)a[3]);
+        } else {
+            const bf16x4_t a = {(__bf16)pr[0], (__bf16)pr[1], (__bf16)pr[2], (__bf16)pr[3]};
+            const i16x4_t ai = __builtin_bit_cast(i16x4_t, a);
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                i16x4_t b;
+                const uint32_t* vj = &vr[j / 2][(j % 2) * VW];
+                if constexpr (KT == PKV_FP8_E4M3) {
+                    const u32x2_t u = {widen_fp8_pair<false>(vj[0]), widen_fp8_pair<true>(vj[0])};
+                    b = __builtin_bit_cast(i16x4_t, u);
+                } else {
+                    const u32x2_t u = {vj[0], vj[1]};
+                    b = __builtin_bit_cast(i16x4_t, u);
+                }
+                o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ai, b, o[j], 0, 0, 0);
+            }
+            return ((float)a[0] + (float)a[1]) + ((float)a[2] + (float)a[3]);
+        }
+    }
+};
+
+// Value of `v` in lane addr / 4 (addr a byte address, as the LDS crossbar
+// takes it; no LDS memory is used).
+__device__ __forceinline__ float lane_fetch(int addr, float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(addr, __builtin_bit_cast(int, v)));
+}
+
+// Everything that computes v happens before this point, and no memory access
+// moves across it. Placed between the last use of a ring slot and the loads
+// that refill it, it keeps the compiler from sinking that use past the refill
+// (which would make the slot's old and new contents live at once, land the
+// refill in other registers and copy it back at the loop latch).
+__device__ __forceinline__ void settle(f32x4_t& v) { asm volatile("" : "+v"(v) : : "memory"); }
 
 __device__ __forceinline__ int tiles_of(int n, int max_ctx) {
     return (n > 0 && n <= max_ctx) ? (n + kBlock - 1) / kBlock : 0;
@@ -197,32 +306,6 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
     return v;
 }
 
-// 8 float32 values rounded into the output type, one 16- or 32-byte store.
-template <int OT>
-__device__ __forceinline__ void store8(void* base, size_t idx, const float* f) {
-    if constexpr (OT == PKV_F32) {
-        float4* d = reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + idx);
-        d[0] = make_float4(f[0], f[1], f[2], f[3]);
-        d[1] = make_float4(f[4], f[5], f[6], f[7]);
-    } else {
-        uint32_t w[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint16_t lo, hi;
-            if constexpr (OT == PKV_F16) {
-                lo = __builtin_bit_cast(uint16_t, (_Float16)f[2 * i]);
-                hi = __builtin_bit_cast(uint16_t, (_Float16)f[2 * i + 1]);
-            } else {
-                lo = f32_to_bf16_rne(f[2 * i]);
-                hi = f32_to_bf16_rne(f[2 * i + 1]);
-            }
-            w[i] = (uint32_t)lo | ((uint32_t)hi << 16);
-        }
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(base) + idx) =
-            make_uint4(w[0], w[1], w[2], w[3]);
-    }
-}
-
 // Partials cross between waves on different XCDs (each XCD has its own L2).
 // They are written and read with agent-scope atomic (write-through, coherent)
 // accesses, and the writer waits for its stores to complete before it bumps
@@ -240,16 +323,6 @@ __device__ __forceinline__ float coherent_load(const float* p) {
 // scalar load, which leaves the vector-memory wait counter to the tile data.
 __device__ __forceinline__ int32_t uniform_read(const int32_t* base, size_t i) {
     return ((const __attribute__((address_space(4))) int32_t*)base)[i];
-}
-
-// Everything that computes v[] happens before this point, and no memory
-// access moves across it. Placed between the last read of a ring slot and the
-// loads that refill it, it keeps the old and the new contents of the slot from
-// being live at once, so the refill can land in the same registers.
-template <int N>
-__device__ __forceinline__ void settle(float (&v)[N]) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]) : : "memory");
 }
 
 // The worker wave whose slice [a_w, a_{w+1}) holds tile f, a_w = floor(w*T/NW).
@@ -325,13 +398,11 @@ __device__ __forceinline__ void merge_segment(const DecodeParams& p, int w0, int
 template <int KT, int QT, int D, int GM>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void paged_decode_kernel(DecodeParams p) {
-    using Shape = DecodeShape<KT, D>;
-    constexpr int LPR = Shape::kLanesPerRow;
-    constexpr int RPI = Shape::kRowsPerInst;
-    constexpr int NI = Shape::kInstPerTile;
+    using TM = TileMath<KT, QT, D>;
+    constexpr int NK = TM::NK, NV = TM::NV, NVL = TM::NVL, KW = TM::KW, VLW = TM::VLW;
     constexpr int KB = Elem<KT>::bytes;
     constexpr int QB = Elem<QT>::bytes;
-    constexpr int ROW_BYTES = D * KB;
+    constexpr uint32_t kTileBytes = (uint32_t)kBlock * D * KB;
     constexpr int SLOT = decode_slot_floats(GM, D);
 
     const int lane = lane_id();
@@ -435,9 +506,8 @@ void paged_decode_kernel(DecodeParams p) {
 
     Cursor ic = cc;  // the next tile to load (kPrefetch tiles ahead of cc)
     bool ic_valid = true;
-    // Block id of ic's tile, read with a wave-uniform (scalar) load one tile
-    // before it is needed; -1 marks an id outside the pool. Scalar loads keep
-    // the tile loads' wait counter free of anything but tile data.
+    // Block id of ic's tile, read one tile before it is needed; -1 marks an
+    // id outside the pool.
     auto read_id = [&](const Cursor& c) -> int {
         const int id = uniform_read(p.block_tables, (size_t)c.s * mb + c.bi);
         return (id < 0 || id >= p.num_blocks) ? -1 : id;
@@ -449,24 +519,23 @@ void paged_decode_kernel(DecodeParams p) {
         if (ic_valid) ic_id = read_id(ic);
     };
 
-    const int row = lane / LPR;                        // which of the RPI rows
-    const int col = (lane % LPR) * kElemsPerLane;      // first element this lane owns
-
-    QRegs<QT, KT> qr[GM];
-    auto load_q = [&](int s, int g) {
+    // Lane roles in the MFMA layouts: column t = l % 16 (the head for scores,
+    // the token for K operands, the element for V operands and outputs) and
+    // k-group g4 = l / 16.
+    const int t = lane & 15;
+    const int g4 = lane >> 4;
+    const uint32_t k_off = (uint32_t)((g4 * kBlock + t) * 8 * KB);  // slab g4, token t
+    const uint32_t v_off = (uint32_t)((t * 4 + g4) * 8 * KB);  // column t, tokens 4*g4..
+    const int x16 = (lane ^ 16) << 2, x32 = (lane ^ 32) << 2;       // cross-group partners
+    int head_lane[4];                                                // lane holding head 4*g4 + j
 #pragma unroll
-        for (int h = 0; h < GM; ++h) {
-            if (h < G)
-                qr[h].load(p.q + (((size_t)s * Hq + g * G + h) * D + col) * QB);
-            else
-                qr[h].zero();
-        }
+    for (int j = 0; j < 4; ++j) head_lane[j] = (4 * g4 + j) << 2;
+
+    typename TM::Q q;
+    auto load_q = [&](int s, int g) {
+        TM::load_q(q, p.q + ((size_t)s * Hq + (size_t)g * G + t) * D * QB, t < G, g4);
     };
 
-    // tile base (wave-uniform, scalar registers) + this lane's byte offset
-    const uint32_t lane_off = (uint32_t)(row * ROW_BYTES + col * KB);
-    Chunk<KT> kr[kPrefetch][NI], vr[kPrefetch][NI];
-    bool slot_bad[kPrefetch];
     // Where ic's tile lives, and how many of its bytes to read: a whole tile,
     // or none once the slice is exhausted or the block id is outside the pool
     // (such a tile's piece is written as NaN). Every iteration issues the
@@ -480,28 +549,25 @@ void paged_decode_kernel(DecodeParams p) {
     auto ic_tile = [&](bool& bad_tile) -> TileRef {
         bad_tile = ic_valid && ic_id < 0;
         if (!ic_valid || ic_id < 0) return TileRef{0, 0u};
-        return TileRef{cache_row_offset(ic_id, ic.g, 0, H, ROW_BYTES),
-                       (uint32_t)(kBlock * ROW_BYTES)};
+        return TileRef{tile_elem_offset(ic_id, ic.g, H, D) * KB, kTileBytes};
     };
-    // Each tile is read through its own buffer resource (base = the tile,
-    // 16 rows), nontemporal: every cache byte is used once per call. The
-    // scheduling barriers keep a refill after the last read of the slot it
-    // overwrites, so the ring registers stay put from one pass to the next
-    // (no copies of data still in flight).
+    uint32_t kr[kPrefetch][NK][KW], vr[kPrefetch][NVL][VLW];
+    bool slot_bad[kPrefetch];
+    // Each tile is read through its own buffer resource (base = the tile),
+    // nontemporal: every cache byte is used once per call. The scheduling
+    // barriers keep the loads of a refill together.
     auto issue_k = [&](int slot, TileRef t_) {
-        const __amdgpu_buffer_rsrc_t t = make_rsrc(p.k_cache + t_.off, t_.bytes);
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(p.k_cache + t_.off, t_.bytes);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int r = 0; r < NI; ++r)
-            kr[slot][r] = load_chunk_stream<KT>(t, lane_off + r * RPI * ROW_BYTES);
+        for (int i = 0; i < NK; ++i) load_dwords<KW>(r, k_off + i * 4 * kBlock * 8 * KB, kr[slot][i]);
         __builtin_amdgcn_sched_barrier(0);
     };
     auto issue_v = [&](int slot, TileRef t_) {
-        const __amdgpu_buffer_rsrc_t t = make_rsrc(p.v_cache + t_.off, t_.bytes);
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(p.v_cache + t_.off, t_.bytes);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int r = 0; r < NI; ++r)
-            vr[slot][r] = load_chunk_stream<KT>(t, lane_off + r * RPI * ROW_BYTES);
+        for (int i = 0; i < NVL; ++i) load_dwords<VLW>(r, v_off + i * 32 * kBlock * KB, vr[slot][i]);
         __builtin_amdgcn_sched_barrier(0);
     };
 
@@ -510,20 +576,18 @@ void paged_decode_kernel(DecodeParams p) {
     load_q(cc.s, cc.g);
 #pragma unroll
     for (int slot = 0; slot < kPrefetch; ++slot) {
-        const TileRef t = ic_tile(slot_bad[slot]);
-        issue_k(slot, t);
-        issue_v(slot, t);
+        const TileRef tr = ic_tile(slot_bad[slot]);
+        issue_k(slot, tr);
+        issue_v(slot, tr);
         ic_advance();
     }
 
-    float m[GM], l[GM], acc[GM][kElemsPerLane];
+    // Running state of the piece: max m and weight sum l of head t (this
+    // lane's share of the tokens), accumulators of heads 4*g4 + r.
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4_t o[NV];
 #pragma unroll
-    for (int h = 0; h < GM; ++h) {
-        m[h] = -INFINITY;
-        l[h] = 0.f;
-#pragma unroll
-        for (int e = 0; e < kElemsPerLane; ++e) acc[h][e] = 0.f;
-    }
+    for (int j = 0; j < NV; ++j) o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const float qk_scale = p.qk_scale_log2;
     bool active = true;  // cc holds a tile still to compute
 
@@ -540,9 +604,8 @@ void paged_decode_kernel(DecodeParams p) {
 
     // Every pass of the loop computes one tile per ring slot and issues the
     // loads that refill the slot, unconditionally: a pass after the last
-    // tile only re-reads and computes on data nobody keeps. Only the piece
-    // bookkeeping depends on `active`. One back edge with the same loads on
-    // every path lets the compiler wait for exactly the tile it needs.
+    // tile only reads zeros and computes on data nobody keeps. Only the piece
+    // bookkeeping depends on `active`.
     while (active) {
 #pragma unroll
         for (int slot = 0; slot < kPrefetch; ++slot) {
@@ -550,50 +613,45 @@ void paged_decode_kernel(DecodeParams p) {
             bool next_bad;
             const TileRef nxt = ic_tile(next_bad);
 
-            // ---- one row instruction at a time: QK, online softmax, P.V ----
-            // The next K goes out once the last QK has read this slot's K, the
-            // next V once the last P.V has read this slot's V.
-            const int live_rows = cc.n - cc.bi * kBlock;   // rows < live_rows hold positions < n
+            // ---- scores; the next K goes out as soon as this K is consumed ----
+            f32x4_t sc = TM::qk(kr[slot], q);
+            settle(sc);
+            issue_k(slot, nxt);
+
+            float x[4];
 #pragma unroll
-            for (int r = 0; r < NI; ++r) {
-                const bool live = r * RPI + row < live_rows;
-                float x[GM];
+            for (int j = 0; j < 4; ++j) x[j] = sc[j] * qk_scale;
+            const int live = cc.n - cc.bi * kBlock;  // tokens < live hold positions < n
+            if (live < kBlock) {
 #pragma unroll
-                for (int h = 0; h < GM; ++h) {
-                    x[h] = group_sum<LPR>(qr[h].dot(kr[slot][r])) * qk_scale;
-                    x[h] = live ? x[h] : -INFINITY;
-                }
-                if (r == NI - 1) {
-                    settle(x);
-                    issue_k(slot, nxt);
-                }
-#pragma unroll
-                for (int h = 0; h < GM; ++h) {
-                    if (__any(x[h] > m[h] + kLazyRescale)) {
-                        float bm = x[h];
-#pragma unroll
-                        for (int sh = LPR; sh < kWave; sh <<= 1) bm = fmaxf(bm, __shfl_xor(bm, sh, kWave));
-                        const float mn = fmaxf(m[h], bm);
-                        const float c = __builtin_amdgcn_exp2f(m[h] - mn);
-                        l[h] *= c;
-#pragma unroll
-                        for (int e = 0; e < kElemsPerLane; ++e) acc[h][e] *= c;
-                        m[h] = mn;
-                    }
-                }
-                float vf[kElemsPerLane];
-                chunk_to_f32<KT>(vr[slot][r], vf);
-#pragma unroll
-                for (int e = 0; e < kElemsPerLane; ++e) vf[e] = live ? vf[e] : 0.f;
-                if (r == NI - 1) settle(vf);
-#pragma unroll
-                for (int h = 0; h < GM; ++h) {
-                    const float pr = __builtin_amdgcn_exp2f(x[h] - m[h]);
-                    l[h] += pr;
-#pragma unroll
-                    for (int e = 0; e < kElemsPerLane; ++e) acc[h][e] = fmaf(pr, vf[e], acc[h][e]);
-                }
+                for (int j = 0; j < 4; ++j) x[j] = 4 * g4 + j < live ? x[j] : -INFINITY;
+                TM::mask_v(vr[slot], live - 4 * g4);
             }
+
+            // ---- online softmax: move the max only when a score outgrows it ----
+            const float xm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+            if (__any(xm > m_run + kLazyRescale)) {
+                float tm = fmaxf(xm, lane_fetch(x16, xm));
+                tm = fmaxf(tm, lane_fetch(x32, tm));  // tile max of head t
+                const float mn = fmaxf(m_run, tm);
+                const float c = __builtin_amdgcn_exp2f(m_run - mn);
+                l_run *= c;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float cr = lane_fetch(head_lane[r], c);  // factor of head 4*g4 + r
+#pragma unroll
+                    for (int j = 0; j < NV; ++j) o[j][r] *= cr;
+                }
+                m_run = mn;
+            }
+            float pr[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pr[j] = __builtin_amdgcn_exp2f(x[j] - m_run);
+
+            // ---- P.V; the next V goes out once this V is consumed ----
+            l_run += TM::pv(pr, vr[slot], o);
+#pragma unroll
+            for (int j = 0; j < NV; ++j) settle(o[j]);
             issue_v(slot, nxt);
             slot_bad[slot] = next_bad;
             ic_advance();
@@ -605,49 +663,36 @@ void paged_decode_kernel(DecodeParams p) {
             }
 
             // ---- the piece is done: write it out, or leave a partial ----
-            // Sum the rows of the wave (lanes with equal `col` hold different rows).
-#pragma unroll
-            for (int h = 0; h < GM; ++h) {
-#pragma unroll
-                for (int sh = LPR; sh < kWave; sh <<= 1) l[h] += __shfl_xor(l[h], sh, kWave);
-#pragma unroll
-                for (int e = 0; e < kElemsPerLane; ++e) {
-                    float v = acc[h][e];
-#pragma unroll
-                    for (int sh = LPR; sh < kWave; sh <<= 1) v += __shfl_xor(v, sh, kWave);
-                    acc[h][e] = v;
-                }
-            }
+            float lt = l_run + lane_fetch(x16, l_run);
+            lt += lane_fetch(x32, lt);  // weight sum of head t over the piece
             const size_t orow = (size_t)cc.s * Hq + (size_t)cc.g * G;  // first output row
             if (clo == 0 && cc.hi == cc.nb) {
                 // the whole segment: normalise and store
-                if (lane < LPR) {
 #pragma unroll
-                    for (int h = 0; h < GM; ++h) {
-                        if (h >= G) break;
-                        float o[kElemsPerLane];
-                        const float sc = p.v_scale / l[h];
+                for (int r = 0; r < 4; ++r) {
+                    const int hh = 4 * g4 + r;
+                    const float sc_r = p.v_scale / lane_fetch(head_lane[r], lt);
+                    if (hh < G) {
 #pragma unroll
-                        for (int e = 0; e < kElemsPerLane; ++e) o[e] = piece_bad ? nan : acc[h][e] * sc;
-                        store8<QT>(p.out, (orow + h) * D + col, o);
+                        for (int j = 0; j < NV; ++j)
+                            store_f32_as<QT>(p.out, (orow + hh) * D + 16 * j + t,
+                                             piece_bad ? nan : o[j][r] * sc_r);
                     }
                 }
             } else {
                 // partial of a split segment: unnormalised accumulator, max, sum
                 float* slotp = p.slots + (size_t)(2 * w + (first_piece ? 0 : 1)) * SLOT;
-                if (lane < LPR) {
 #pragma unroll
-                    for (int h = 0; h < GM; ++h)
+                for (int r = 0; r < 4; ++r) {
+                    const int hh = 4 * g4 + r;
+                    if (hh < GM) {
 #pragma unroll
-                        for (int e = 0; e < kElemsPerLane; ++e)
-                            coherent_store(slotp + h * D + col + e, acc[h][e]);
-                }
-                if (lane == 0) {
-#pragma unroll
-                    for (int h = 0; h < GM; ++h) {
-                        coherent_store(slotp + GM * D + h, piece_bad ? nan : m[h]);
-                        coherent_store(slotp + GM * D + GM + h, piece_bad ? nan : l[h]);
+                        for (int j = 0; j < NV; ++j) coherent_store(slotp + hh * D + 16 * j + t, o[j][r]);
                     }
+                }
+                if (lane < GM) {
+                    coherent_store(slotp + GM * D + lane, piece_bad ? nan : m_run);
+                    coherent_store(slotp + GM * D + GM + lane, piece_bad ? nan : lt);
                 }
                 __builtin_amdgcn_s_waitcnt(0);  // the partial has landed before it is announced
                 int* counter = p.counters + (size_t)cc.s * H + cc.g;
@@ -676,13 +721,10 @@ void paged_decode_kernel(DecodeParams p) {
             // The query has landed before this path joins the streaming one,
             // so the join does not make every tile wait for all loads.
             __builtin_amdgcn_s_waitcnt(0);
+            m_run = -INFINITY;
+            l_run = 0.f;
 #pragma unroll
-            for (int h = 0; h < GM; ++h) {
-                m[h] = -INFINITY;
-                l[h] = 0.f;
-#pragma unroll
-                for (int e = 0; e < kElemsPerLane; ++e) acc[h][e] = 0.f;
-            }
+            for (int j = 0; j < NV; ++j) o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
     }
 
@@ -707,7 +749,7 @@ static hipError_t launch_typed(const DecodeArgs& a) {
     auto kernel = paged_decode_kernel<KT, QT, D, GM>;
     int nw = a.num_workers;
     if (nw == 0) {
-        // fill the device: resident workgroups per CU x CUs x 4 waves
+        // three worker waves per CU
         static std::atomic<int> per_cu_cache{0};
         int per_cu = per_cu_cache.load(std::memory_order_relaxed);
         if (per_cu == 0) {
@@ -721,9 +763,10 @@ static hipError_t launch_typed(const DecodeArgs& a) {
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return hipErrorInvalidDevice;
-        // two workgroups (8 waves) per CU: measured best on the 40 x 8192 GQA
-        // shape; more waves only add contention for the vector ALUs
-        nw = (per_cu < 2 ? per_cu : 2) * cus * kWavesPerGroup;
+        // three waves per CU: measured best on the 40 x 8192 GQA shape (a sweep
+        // over 2..16 per CU); more concurrent streams lower the bandwidth the
+        // memory system delivers and widen the spread between waves
+        nw = (per_cu < 3 ? per_cu : 3) * cus * kWavesPerGroup;
         if (nw > kMaxWorkers) nw = kMaxWorkers;
     }
     // never more workers than tiles could exist

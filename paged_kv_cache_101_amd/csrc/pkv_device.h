@@ -1,6 +1,6 @@
 // pkv_device.h -- device-side building blocks shared by the libpkv kernels:
-// element types, the cache addressing, cross-lane reductions (DPP within a
-// 16-lane row, swizzles across rows) and round-to-nearest-even stores.
+// element types, the in-block cache layout, cross-lane reductions (DPP within
+// a 16-lane row, swizzles across rows) and round-to-nearest-even stores.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -12,12 +12,9 @@ namespace pkv {
 
 constexpr int kBlock = PKV_BLOCK_SIZE;  // tokens per physical block
 constexpr int kWave = 64;               // CDNA wavefront width
-constexpr int kElemsPerLane = 8;        // cache elements a lane owns per row chunk
 
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
 
 template <int DT>
 struct Elem;
@@ -38,49 +35,28 @@ struct Elem<PKV_FP8_E4M3> {
     static constexpr int bytes = 1;
 };
 
-// Byte offset of row `off` of tile (blk, g) in a [num_blocks][H][16][D] cache
-// with `row_bytes` = D * element bytes. The only place the layout is spelled
-// out on the device: decode, gather and append all go through it.
-__device__ __forceinline__ size_t cache_row_offset(int64_t blk, int g, int off, int num_kv_heads,
-                                                   int row_bytes) {
-    return ((size_t)(blk * num_kv_heads + g) * kBlock + off) * (size_t)row_bytes;
+// Cache layout. The pool is [num_blocks][H][16 * D] elements: one tile of 16
+// tokens x D elements per (physical block, KV head), tiles contiguous. Inside a
+// tile the two caches are ordered for the matrix-core operands of decode:
+//   K: [D/8][16][8]  token t, element e at ((e / 8) * 16 + t) * 8 + e % 8
+//      (8-element slabs: the 16 tokens' slab i lie together, so the slabs a
+//      QK instruction consumes are one contiguous run);
+//   V: token t, element e = 16 * j + c (element column c of 16-element block
+//      j) at (((j / 2) * 16 + c) * 4 + t / 4) * 8 + (j % 2) * 4 + t % 4
+//      (P.V contracts over tokens: 4 consecutive tokens of one element
+//      column, for two neighbouring element blocks, form one 8-element run,
+//      and the 64 runs of a block pair are contiguous).
+// These three functions are the only place the layout is spelled out on the
+// device: decode, gather and append all go through them.
+__device__ __forceinline__ size_t tile_elem_offset(int64_t blk, int g, int num_kv_heads, int d) {
+    return (size_t)(blk * num_kv_heads + g) * kBlock * (size_t)d;
 }
-
-// 8 elements held by one lane, as raw dwords (f32: 8, 16-bit: 4, fp8: 2).
-template <int DT>
-struct Chunk {
-    static constexpr int dwords = Elem<DT>::bytes * kElemsPerLane / 4;
-    uint32_t w[dwords];
-};
-
-// Loads of 8 elements through a plain pointer (optionally nontemporal).
-template <typename V>
-__device__ __forceinline__ V load_vec(const uint8_t* p, bool stream) {
-    const V* q = reinterpret_cast<const V*>(p);
-    return stream ? __builtin_nontemporal_load(q) : *q;
+__device__ __forceinline__ int k_elem_index(int t, int e) {
+    return ((e >> 3) * kBlock + t) * 8 + (e & 7);
 }
-
-template <int DT, bool STREAM = false>
-__device__ __forceinline__ Chunk<DT> load_chunk(const uint8_t* p) {
-    Chunk<DT> c;
-    if constexpr (Chunk<DT>::dwords == 8) {
-        u32x4_t a = load_vec<u32x4_t>(p, STREAM);
-        u32x4_t b = load_vec<u32x4_t>(p + 16, STREAM);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            c.w[i] = a[i];
-            c.w[4 + i] = b[i];
-        }
-    } else if constexpr (Chunk<DT>::dwords == 4) {
-        u32x4_t a = load_vec<u32x4_t>(p, STREAM);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) c.w[i] = a[i];
-    } else {
-        u32x2_t a = load_vec<u32x2_t>(p, STREAM);
-        c.w[0] = a[0];
-        c.w[1] = a[1];
-    }
-    return c;
+__device__ __forceinline__ int v_elem_index(int t, int e) {
+    const int j = e >> 4, c = e & 15;
+    return ((((j >> 1) * kBlock + c) * 4 + (t >> 2)) * 2 + (j & 1)) * 4 + (t & 3);
 }
 
 // Buffer resource for `bytes` bytes at `base` (raw, untyped dwords). Loads
@@ -88,71 +64,6 @@ __device__ __forceinline__ Chunk<DT> load_chunk(const uint8_t* p) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                              0x00020000);
-}
-
-// 8 elements at byte `voff` of a buffer, nontemporal (streamed past the
-// caches). The address lives in one 32-bit VGPR plus the scalar resource.
-template <int DT>
-__device__ __forceinline__ Chunk<DT> load_chunk_stream(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-    constexpr int kNontemporal = 2;
-    Chunk<DT> c;
-    if constexpr (Chunk<DT>::dwords == 8) {
-        u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kNontemporal);
-        u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, 0, kNontemporal);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            c.w[i] = a[i];
-            c.w[4 + i] = b[i];
-        }
-    } else if constexpr (Chunk<DT>::dwords == 4) {
-        u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kNontemporal);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) c.w[i] = a[i];
-    } else {
-        u32x2_t a = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, kNontemporal);
-        c.w[0] = a[0];
-        c.w[1] = a[1];
-    }
-    return c;
-}
-
-template <int DT>
-__device__ __forceinline__ void zero_chunk(Chunk<DT>& c) {
-#pragma unroll
-    for (int i = 0; i < Chunk<DT>::dwords; ++i) c.w[i] = 0u;
-}
-
-// The 8 elements of a chunk as float32 (exact for every storage type).
-// fp8: the hardware OCP E4M3FN -> f32 conversion, two bytes per instruction.
-template <int DT>
-__device__ __forceinline__ void chunk_to_f32(const Chunk<DT>& c, float* f) {
-    if constexpr (DT == PKV_F32) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = __builtin_bit_cast(float, c.w[i]);
-    } else if constexpr (DT == PKV_F16) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            half2_t h = __builtin_bit_cast(half2_t, c.w[i]);
-            f[2 * i] = (float)h.x;
-            f[2 * i + 1] = (float)h.y;
-        }
-    } else if constexpr (DT == PKV_BF16) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f[2 * i] = __builtin_bit_cast(float, c.w[i] << 16);
-            f[2 * i + 1] = __builtin_bit_cast(float, c.w[i] & 0xFFFF0000u);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(c.w[i], false);
-            auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(c.w[i], true);
-            f[4 * i] = lo[0];
-            f[4 * i + 1] = lo[1];
-            f[4 * i + 2] = hi[0];
-            f[4 * i + 3] = hi[1];
-        }
-    }
 }
 
 // float32 -> storage type with round-to-nearest-even (the default rounding

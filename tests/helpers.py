@@ -10,6 +10,8 @@ Tolerances (written here, used by every parity test):
   * every type also rms(err) / rms(oracle) <= 1e-2, so an output that is
     merely small (long contexts average towards 0) cannot pass by accident.
 """
+import weakref
+
 import numpy as np
 import torch
 
@@ -33,16 +35,38 @@ def desc(b: W.DecodeBatch):
     return B.desc_for(b.k_cache, b.kv_dtype, b.k_scale, b.v_scale)
 
 
+# A batch's caches (b.k_cache, b.v_cache) hold its blocks in token-row order,
+# the form the oracle reads. The library's caches are built from them once
+# with fill_cache (pkv_kv_append of every row) and kept per row-order tensor.
+# Entries are keyed by the identity of the row-order K tensor and dropped when
+# it is freed.
+_DEVICE_CACHES = {}
+
+
+def device_caches(b: W.DecodeBatch):
+    key = id(b.k_cache)
+    hit = _DEVICE_CACHES.get(key)
+    if hit is None or hit[0]() is not b.k_cache or hit[1]() is not b.v_cache:
+        kc, vc = B.fill_cache(b.k_cache, b.v_cache, desc(b))
+        hit = (weakref.ref(b.k_cache), weakref.ref(b.v_cache), kc, vc)
+        _DEVICE_CACHES[key] = hit
+        weakref.finalize(b.k_cache, _DEVICE_CACHES.pop, key, None)
+    return hit[2], hit[3]
+
+
 def gpu_append(b: W.DecodeBatch):
-    B.pkv_kv_append(b.new_k, b.new_v, b.slot_mapping, b.k_cache, b.v_cache, desc(b))
+    """Append the batch's new rows into its library caches (the row-order
+    caches keep the state before the append)."""
+    kc, vc = device_caches(b)
+    B.pkv_kv_append(b.new_k, b.new_v, b.slot_mapping, kc, vc, desc(b))
 
 
 def gpu_decode(b: W.DecodeBatch, num_workers=0, out=None, workspace=None) -> torch.Tensor:
     if out is None:
         out = torch.empty_like(b.q)
-    B.pkv_paged_attention_decode(b.q, b.k_cache, b.v_cache, desc(b), b.block_tables,
-                                 b.context_lens, b.scale, out, num_workers=num_workers,
-                                 workspace=workspace)
+    kc, vc = device_caches(b)
+    B.pkv_paged_attention_decode(b.q, kc, vc, desc(b), b.block_tables, b.context_lens, b.scale,
+                                 out, num_workers=num_workers, workspace=workspace)
     return out
 
 

@@ -34,6 +34,7 @@ def test_single_token_returns_every_code_exactly(gpu, q_dtype, v_scale, P):
     q = torch.randn((1, Hq, d), device=gpu).to(tdt)
     out = torch.empty_like(q)
     desc = B.cache_desc(nb, H, d, "fp8", 0.5, v_scale)
+    kc, vc = B.fill_cache(kc, vc, desc)
     B.pkv_paged_attention_decode(q, kc, vc, desc, bt, cl, 0.1, out, num_workers=P)
     torch.cuda.synchronize()
     got = out.to(torch.float64).cpu().numpy()
