@@ -40,6 +40,11 @@ def lib():
         L.oracle_fp8_e4m3_to_double.restype = c_dbl
         L.oracle_fp8_e4m3_encode.argtypes = [c_dbl, c_dbl]
         L.oracle_fp8_e4m3_encode.restype = ctypes.c_uint8
+        L.oracle_fp8_e4m3_encode_f32.argtypes = [ctypes.c_float, ctypes.c_float]
+        L.oracle_fp8_e4m3_encode_f32.restype = ctypes.c_uint8
+        L.oracle_kv_append_fp8.argtypes = [vp, vp, c_int, vp, c_i64, vp, vp, c_i64, c_i64, c_i64,
+                                           ctypes.c_float, ctypes.c_float]
+        L.oracle_kv_append_fp8.restype = c_int
         L.oracle_kv_bytes_per_token.argtypes = [c_i64, c_i64, c_i64, c_i64]
         L.oracle_kv_bytes_per_token.restype = ctypes.c_uint64
         L.oracle_kv_append.argtypes = [vp, vp, c_int, vp, c_i64, vp, vp, c_i64, c_i64, c_i64]
@@ -98,6 +103,11 @@ def fp8_e4m3_encode(x: float, scale: float = 1.0) -> int:
     return lib().oracle_fp8_e4m3_encode(float(x), float(scale))
 
 
+def fp8_e4m3_encode_f32(x: float, scale: float = 1.0) -> int:
+    """The code of the float32 quotient x / scale (see pkv_oracle.c)."""
+    return lib().oracle_fp8_e4m3_encode_f32(float(x), float(scale))
+
+
 # ---- sizing ----------------------------------------------------------------
 
 def kv_bytes_per_token(num_layers: int, num_kv_heads: int, head_dim: int, elem_bytes: int) -> int:
@@ -117,6 +127,20 @@ def kv_append(k, v, slot_mapping, k_cache, v_cache):
                                 _ptr(k_cache), _ptr(v_cache), num_blocks, H, d)
     if rc != 0:
         raise ValueError("oracle_kv_append: slot out of range")
+
+
+def kv_append_fp8(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale):
+    """In-place quantising append of float32 / float16 / bfloat16 rows (bfloat16
+    as uint16 bits) into uint8 E4M3FN caches (see pkv_oracle.c)."""
+    num_blocks, H, blk, d = k_cache.shape
+    assert blk == BLOCK and k.shape[1:] == (H, d) and v.shape == k.shape and k.dtype == v.dtype
+    assert k_cache.dtype == v_cache.dtype == np.uint8
+    slots = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    rc = lib().oracle_kv_append_fp8(_ptr(k), _ptr(v), _dtype_code(k), _ptr(slots), k.shape[0],
+                                    _ptr(k_cache), _ptr(v_cache), num_blocks, H, d,
+                                    float(k_scale), float(v_scale))
+    if rc != 0:
+        raise ValueError("oracle_kv_append_fp8: bad dtype or slot out of range")
 
 
 def gather(k_cache, v_cache, block_tables, context_lens, max_ctx, fill=None):

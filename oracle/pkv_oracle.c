@@ -135,6 +135,18 @@ uint8_t oracle_fp8_e4m3_encode(double x, double c)
     return (uint8_t)(best | (neg << 7));
 }
 
+/* The same rounding applied to a quotient taken in float32: y = x / c as one
+ * IEEE single-precision division (round to nearest even), then the nearest
+ * code of y as above. This is the precision in which a quantising append
+ * decides each code (the library's kernel divides in float32), so both sides
+ * decide in the same arithmetic; with c a power of two it equals
+ * oracle_fp8_e4m3_encode(x, c). */
+uint8_t oracle_fp8_e4m3_encode_f32(float x, float c)
+{
+    volatile float y = x / c;
+    return oracle_fp8_e4m3_encode((double)y, 1.0);
+}
+
 /* Element idx of an array of dtype dt, converted exactly to double. */
 static double load_elem(const void *base, size_t idx, int dt)
 {
@@ -207,6 +219,42 @@ int oracle_kv_append(const void *k, const void *v, int dtype, const int64_t *slo
  * bytes: k_out and v_out are [S][H_kv][max_ctx][d]. Position t of sequence s
  * lives in physical block block_tables[s][t / 16], row t % 16. Rows at or past
  * the sequence's context length are left untouched. */
+/* Quantising append into an fp8 cache (ttlab page, section 2: fp8 halves the
+ * bytes per element; section 4: rows are written slot by slot). Each new
+ * token's rows, in float32, float16 or bfloat16 (src_dtype), go to block
+ * slot / 16, row slot % 16 like oracle_kv_append, every element x becoming
+ * oracle_fp8_e4m3_encode_f32(x, k_scale) in K and (x, v_scale) in V. A negative
+ * slot skips the token. Returns OR_BAD for a slot past the pool. */
+int oracle_kv_append_fp8(const void *k, const void *v, int src_dtype,
+                         const int64_t *slot_mapping, int64_t num_tokens, uint8_t *k_cache,
+                         uint8_t *v_cache, int64_t num_blocks, int64_t num_kv_heads,
+                         int64_t head_dim, float k_scale, float v_scale)
+{
+    if (src_dtype != OR_F32 && src_dtype != OR_F16 && src_dtype != OR_BF16)
+        return OR_BAD;
+    for (int64_t i = 0; i < num_tokens; ++i) {
+        int64_t slot = slot_mapping[i];
+        if (slot < 0)
+            continue;
+        if (slot >= num_blocks * OR_BLOCK)
+            return OR_BAD;
+        int64_t blk = slot / OR_BLOCK;
+        int64_t off = slot % OR_BLOCK;
+        for (int64_t g = 0; g < num_kv_heads; ++g) {
+            size_t dst = cache_index(blk, g, off, 0, num_kv_heads, head_dim);
+            size_t src = (size_t)((i * num_kv_heads + g) * head_dim);
+            for (int64_t j = 0; j < head_dim; ++j) {
+                /* every float16 / bfloat16 value is exactly a float32 value */
+                float kx = (float)load_elem(k, src + j, src_dtype);
+                float vx = (float)load_elem(v, src + j, src_dtype);
+                k_cache[dst + j] = oracle_fp8_e4m3_encode_f32(kx, k_scale);
+                v_cache[dst + j] = oracle_fp8_e4m3_encode_f32(vx, v_scale);
+            }
+        }
+    }
+    return OR_OK;
+}
+
 int oracle_gather(const void *k_cache, const void *v_cache, int dtype, int64_t num_blocks,
                   int64_t num_kv_heads, int64_t head_dim, const int32_t *block_tables,
                   int64_t max_blocks_per_seq, const int32_t *context_lens, int64_t num_seqs,
