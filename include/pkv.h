@@ -39,7 +39,9 @@
  * at (blk * num_kv_heads + g) * 16 * head_dim. Inside a tile, row `off`
  * (0..15), element j (0..head_dim-1) is at
  *     K: ((j / 8) * 16 + off) * 8 + j % 8    (8-element slabs, token-minor)
- *     V: j * 16 + off                        (element-major)
+ *     V: (((j / 32) * 16 + j % 16) * 4 + off / 4) * 8 + ((j / 16) % 2) * 4 + off % 4
+ *        (runs of 4 consecutive rows of one element, two element blocks of
+ *        16 interleaved)
  * an order chosen so that the decode kernel's matrix-core operands load as
  * contiguous runs. Only the library writes this order (pkv_kv_append) and
  * reads it (decode, pkv_debug_gather): callers pass whole rows in and get
@@ -120,7 +122,15 @@ size_t pkv_cache_tensor_bytes(const pkv_cache_desc *cache);
  * a request grows; the block-table figure shows a last block 6/16 full.)
  *
  *  k, v          [num_tokens][num_kv_heads][head_dim] in kv_dtype (device)
- *  kv_dtype      must equal cache->dtype: the rows are copied byte for byte
+ *  kv_dtype      equal to cache->dtype: the rows are copied byte for byte.
+ *                Or PKV_F32 / PKV_F16 / PKV_BF16 into a PKV_FP8_E4M3 cache
+ *                ([ttlab] section 2: fp8 storage, one byte per element):
+ *                element x of K is stored as the E4M3FN code of the float32
+ *                quotient x / cache->k_scale (one IEEE single-precision
+ *                division, round to nearest even), V likewise with v_scale;
+ *                the code is the nearest one, ties to an even mantissa,
+ *                quotients beyond +-448 (and infinities) saturate to +-448,
+ *                NaN becomes 0x7F.
  *  slot_mapping  int64 [num_tokens] (device). Token i goes to block
  *                slot / 16, row slot % 16, for every KV head (stored in the
  *                in-tile order above; filling every slot of a pool from
@@ -131,7 +141,8 @@ size_t pkv_cache_tensor_bytes(const pkv_cache_desc *cache);
  *  k_cache, v_cache  the pool tensors (device), updated in place
  * Two tokens with the same slot in one call race (precondition: distinct).
  * Errors: INVALID_ARG (null pointer with num_tokens > 0, bad desc),
- * UNSUPPORTED (block size, head_dim, dtype, kv_dtype != cache dtype), HIP. */
+ * UNSUPPORTED (block size, head_dim, dtype, a kv_dtype / cache dtype pair
+ * other than the above), HIP. */
 int pkv_kv_append(const void *k, const void *v, int32_t kv_dtype, const int64_t *slot_mapping,
                   int32_t num_tokens, void *k_cache, void *v_cache, const pkv_cache_desc *cache,
                   hipStream_t stream);

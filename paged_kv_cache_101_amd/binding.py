@@ -156,14 +156,19 @@ def decode_workspace(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_di
 def pkv_kv_append(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
                   k_cache: torch.Tensor, v_cache: torch.Tensor, desc: pkv_cache_desc,
                   stream=None) -> None:
-    """k, v: [T][H_kv][d] in the cache dtype; slot_mapping: int64 [T]."""
+    """k, v: [T][H_kv][d] in the cache dtype, or float32 / float16 / bfloat16
+    rows into an fp8 cache (quantised with desc.k_scale / desc.v_scale);
+    slot_mapping: int64 [T]."""
     T = k.shape[0]
     _need(k.shape == v.shape and k.dim() == 3, "k and v must be [T][H_kv][d]")
     _need(slot_mapping.dtype == torch.int64 and slot_mapping.numel() == T,
           "slot_mapping must be int64 [T]")
     for t in (k, v, slot_mapping, k_cache, v_cache):
         _need(t.is_contiguous() and t.is_cuda, "all tensors must be contiguous device tensors")
-    _need(k.dtype == k_cache.dtype == v_cache.dtype == v.dtype, "k/v/cache dtypes differ")
+    _need(k.dtype == v.dtype and k_cache.dtype == v_cache.dtype, "k/v or cache dtypes differ")
+    _need(k.dtype == k_cache.dtype
+          or (_dtype_of(k_cache, "fp8") == PKV_FP8_E4M3 and _dtype_of(k) != PKV_FP8_E4M3),
+          "k/v must be in the cache dtype, or 16/32-bit floats into an fp8 cache")
     rc = lib().pkv_kv_append(_ptr(k), _ptr(v), _dtype_of(k), _ptr(slot_mapping), T,
                              _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc), _stream(stream))
     _check("pkv_kv_append", rc)

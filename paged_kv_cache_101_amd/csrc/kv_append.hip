@@ -63,6 +63,113 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
     }
 }
 
+// ---- quantising append into an fp8 cache -------------------------------------
+//
+// (ttlab page, section 2: fp8 storage halves the bytes per element again.)
+// Each element x of a float32 / float16 / bfloat16 row is stored as the OCP
+// E4M3FN code of y = x / scale, the quotient taken in float32 (IEEE, round to
+// nearest even), with k_scale for K and v_scale for V.
+
+// E4M3FN code of a float32 value, from the format's definition (sign, 4
+// exponent bits with bias 7, 3 mantissa bits, no infinity, 0x7F / 0xFF NaN,
+// largest finite 448): round to nearest, ties to the even mantissa; values
+// beyond +-448 (and infinities) saturate to +-448; NaN becomes 0x7F.
+__device__ __forceinline__ uint32_t fp8_e4m3_code(float y) {
+    if (y != y) return 0x7Fu;
+    const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+    const float a = fabsf(y);
+    if (a >= 448.f) return sign | 0x7Eu;
+    if (a < 0.015625f)  // below 2^-6: multiples of 2^-9 (8 * 2^-9 is the smallest normal)
+        return sign | (uint32_t)__builtin_rintf(a * 512.f);
+    // normal: keep 3 of float32's 23 mantissa bits with round to nearest even
+    // (a carry moves the exponent), then rebias the exponent from 127 to 7
+    const uint32_t b = __float_as_uint(a);
+    return sign | (((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - (120u << 3));
+}
+
+template <int SRC>
+__device__ __forceinline__ void load8_f32(const uint8_t* p, float* f) {
+    if constexpr (SRC == PKV_F32) {
+        const float4 a = reinterpret_cast<const float4*>(p)[0];
+        const float4 b = reinterpret_cast<const float4*>(p)[1];
+        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+        f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+    } else {
+        const uint4 a = *reinterpret_cast<const uint4*>(p);
+        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (SRC == PKV_F16) {
+                f[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] & 0xFFFFu));
+                f[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] >> 16));
+            } else {
+                f[2 * i] = __uint_as_float(w[i] << 16);
+                f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+            }
+        }
+    }
+}
+
+template <int SRC>
+__global__ __launch_bounds__(256) void kv_append_fp8_kernel(
+    const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
+    const int64_t* __restrict__ slot_mapping, int num_tokens, uint8_t* __restrict__ k_cache,
+    uint8_t* __restrict__ v_cache, int num_blocks, int num_kv_heads, int head_dim, float k_scale,
+    float v_scale) {
+    constexpr int SB = Elem<SRC>::bytes;
+    const int groups = head_dim / 8;
+    const int64_t total = (int64_t)num_tokens * num_kv_heads * groups;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int c = (int)(idx % groups);
+        const int64_t row = idx / groups;  // token * H + g
+        const int g = (int)(row % num_kv_heads);
+        const int64_t tok = row / num_kv_heads;
+        const int64_t slot = slot_mapping[tok];
+        if (slot < 0 || slot >= (int64_t)num_blocks * kBlock) continue;
+        const int t = (int)(slot % kBlock);
+        const size_t tile = tile_elem_offset(slot / kBlock, g, num_kv_heads, head_dim);
+        const size_t src = ((size_t)row * head_dim + (size_t)c * 8) * SB;
+        float kf[8], vf[8];
+        load8_f32<SRC>(k + src, kf);
+        load8_f32<SRC>(v + src, vf);
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            lo |= fp8_e4m3_code(kf[e] / k_scale) << (8 * e);
+            hi |= fp8_e4m3_code(kf[4 + e] / k_scale) << (8 * e);
+        }
+        *reinterpret_cast<uint2*>(k_cache + tile + k_elem_index(t, c * 8)) = make_uint2(lo, hi);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            v_cache[tile + v_elem_index(t, c * 8 + e)] = (uint8_t)fp8_e4m3_code(vf[e] / v_scale);
+    }
+}
+
+hipError_t launch_kv_append_fp8(const void* k, const void* v, int src_dtype,
+                                const int64_t* slot_mapping, int num_tokens, void* k_cache,
+                                void* v_cache, int num_blocks, int num_kv_heads, int head_dim,
+                                float k_scale, float v_scale, hipStream_t stream) {
+    if (num_tokens == 0) return hipSuccess;
+    const int64_t total = (int64_t)num_tokens * num_kv_heads * (head_dim / 8);
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    auto args = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           static_cast<const uint8_t*>(k), static_cast<const uint8_t*>(v),
+                           slot_mapping, num_tokens, static_cast<uint8_t*>(k_cache),
+                           static_cast<uint8_t*>(v_cache), num_blocks, num_kv_heads, head_dim,
+                           k_scale, v_scale);
+    };
+    if (src_dtype == PKV_F32)
+        args(kv_append_fp8_kernel<PKV_F32>);
+    else if (src_dtype == PKV_F16)
+        args(kv_append_fp8_kernel<PKV_F16>);
+    else
+        args(kv_append_fp8_kernel<PKV_BF16>);
+    return hipGetLastError();
+}
+
 hipError_t launch_kv_append(const void* k, const void* v, int elem_bytes,
                             const int64_t* slot_mapping, int num_tokens, void* k_cache,
                             void* v_cache, int num_blocks, int num_kv_heads, int head_dim,

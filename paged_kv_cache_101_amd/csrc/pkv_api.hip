@@ -67,16 +67,24 @@ PKV_EXPORT int pkv_kv_append(const void* k, const void* v, int32_t kv_dtype,
     int rc = check_cache(cache);
     if (rc != PKV_OK) return rc;
     if (num_tokens < 0) return PKV_ERR_INVALID_ARG;
-    if (kv_dtype != cache->dtype) return PKV_ERR_UNSUPPORTED;
+    // a byte copy, or quantising float32 / float16 / bfloat16 rows into an fp8 cache
+    const bool quantise = cache->dtype == PKV_FP8_E4M3 &&
+                          (kv_dtype == PKV_F32 || kv_dtype == PKV_F16 || kv_dtype == PKV_BF16);
+    if (kv_dtype != cache->dtype && !quantise) return PKV_ERR_UNSUPPORTED;
     if (k_cache == nullptr || v_cache == nullptr) return PKV_ERR_INVALID_ARG;
     if (num_tokens > 0 && (k == nullptr || v == nullptr || slot_mapping == nullptr))
         return PKV_ERR_INVALID_ARG;
     if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
         return PKV_ERR_INVALID_ARG;
     if (num_tokens == 0) return PKV_OK;
-    hipError_t err = pkv::launch_kv_append(k, v, elem_bytes(cache->dtype), slot_mapping,
-                                           num_tokens, k_cache, v_cache, cache->num_blocks,
-                                           cache->num_kv_heads, cache->head_dim, stream);
+    hipError_t err =
+        quantise ? pkv::launch_kv_append_fp8(k, v, kv_dtype, slot_mapping, num_tokens, k_cache,
+                                             v_cache, cache->num_blocks, cache->num_kv_heads,
+                                             cache->head_dim, cache->k_scale, cache->v_scale,
+                                             stream)
+                 : pkv::launch_kv_append(k, v, elem_bytes(cache->dtype), slot_mapping, num_tokens,
+                                         k_cache, v_cache, cache->num_blocks, cache->num_kv_heads,
+                                         cache->head_dim, stream);
     return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

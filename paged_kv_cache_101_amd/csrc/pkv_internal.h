@@ -61,6 +61,11 @@ hipError_t launch_kv_append(const void* k, const void* v, int elem_bytes,
                             void* v_cache, int num_blocks, int num_kv_heads, int head_dim,
                             hipStream_t stream);
 
+hipError_t launch_kv_append_fp8(const void* k, const void* v, int src_dtype,
+                                const int64_t* slot_mapping, int num_tokens, void* k_cache,
+                                void* v_cache, int num_blocks, int num_kv_heads, int head_dim,
+                                float k_scale, float v_scale, hipStream_t stream);
+
 hipError_t launch_paged_decode(const DecodeArgs& a);
 
 hipError_t launch_gather(const void* k_cache, const void* v_cache, int elem_bytes,
