@@ -152,12 +152,21 @@ int pkv_kv_append(const void *k, const void *v, int32_t kv_dtype, const int64_t 
 
 /* Workspace bytes pkv_paged_attention_decode needs for this batch shape and
  * worker count (num_workers 0 = the device default, sized for
- * PKV_MAX_WORKERS): int32 counters [num_seqs][num_kv_heads] rounded up to 256
- * bytes, then 2 * workers float partial slots of Gp * head_dim + pad(2 * Gp)
- * floats each, Gp being G = num_q_heads / num_kv_heads rounded up to 1, 2, 4,
- * 6 or 8 and pad() rounding up to a multiple of 4. Returns 0 for invalid
- * arguments (non-positive sizes, G not a whole number or above 8,
- * num_workers < 0 or > PKV_MAX_WORKERS). */
+ * PKV_MAX_WORKERS): 2 * workers float partial slots of Gp * head_dim +
+ * pad(2 * Gp) floats each at the front, Gp being G = num_q_heads /
+ * num_kv_heads rounded up to 1, 2, 4, 6 or 8 and pad() rounding up to a
+ * multiple of 4; int32 counters [num_seqs][num_kv_heads] in the last bytes;
+ * each part rounded up to 256 bytes. Returns 0 for invalid arguments
+ * (non-positive sizes, G not a whole number or above 8, num_workers < 0 or
+ * > PKV_MAX_WORKERS).
+ *
+ * Workspace rule (both decode entry points): the counters sit in the last
+ * bytes of the workspace as passed (workspace_bytes rounded down to 256) and
+ * must be zero when a call starts; every call leaves them zero. Float
+ * scratch sits at the front. So a workspace sized for the largest shape a
+ * caller runs (num_seqs, num_groups, num_workers; same heads and head_dim)
+ * and zeroed once serves any call of that shape or smaller, passed with the
+ * same workspace_bytes, without being cleared again. */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t head_dim, int32_t num_workers);
 
@@ -195,11 +204,9 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *  num_workers   waves sharing the work: 0 = enough to fill the device,
  *                otherwise 1..PKV_MAX_WORKERS
  *  workspace, workspace_bytes  at least pkv_decode_workspace_bytes(...) of
- *                device memory, 256-byte aligned. Its counter region (the
- *                first num_seqs * num_kv_heads int32, rounded up to 256
- *                bytes) must be all zero before the first call that uses it;
- *                every call leaves it zero again. Two calls must not use one
- *                workspace at the same time.
+ *                device memory, 256-byte aligned, zeroed before its first
+ *                use (see the workspace rule above). Two calls must not use
+ *                one workspace at the same time.
  *  out           [num_seqs][num_q_heads][head_dim] in q_dtype (device); must
  *                not alias any input or the workspace
  * A sequence whose length exceeds max_blocks_per_seq * 16, or whose needed
@@ -211,6 +218,65 @@ int pkv_paged_attention_decode(const void *q, int32_t q_dtype, int32_t num_seqs,
                                int32_t max_blocks_per_seq, const int32_t *context_lens,
                                float scale, int32_t num_workers, void *workspace,
                                size_t workspace_bytes, void *out, hipStream_t stream);
+
+/* Workspace bytes pkv_paged_attention_decode_shared_prefix needs. Front:
+ * the decode slots for the worker count, float32 suffix results
+ * (num_seqs * num_q_heads * head_dim, then num_seqs * num_q_heads floats) and
+ * 2048 prefix partial slots of 16 * head_dim + 32 floats. End: int32 prefix
+ * counters (num_kv_heads * (ceil(num_seqs * G / 16) + num_groups)), then the
+ * decode counters [num_seqs][num_kv_heads]. Each part is rounded up to 256
+ * bytes. Returns 0 where pkv_decode_workspace_bytes does, or for
+ * num_groups < 0 or > num_seqs. */
+size_t pkv_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t num_groups, int32_t num_workers);
+
+/* Paged decode for a batch whose sequences share prefixes: the same result
+ * as pkv_paged_attention_decode with the same arguments (up to float32
+ * rounding order), reading each shared block once per KV head for all the
+ * sequences that reference it instead of once per sequence.
+ * ([ttlab] section 4 and [redhat]: sequences with a common prefix map its
+ *  logical blocks to one physical copy, listed in each of their block
+ *  tables.)
+ *
+ * Prefix groups (device arrays, read by the kernels only):
+ *  group_starts         int32 [num_groups + 1]: group j is the run of
+ *                       sequences [group_starts[j], group_starts[j + 1])
+ *  group_prefix_blocks  int32 [num_groups]: P_j, the number of leading
+ *                       logical blocks that every member of group j maps to
+ *                       the same physical blocks (full blocks: 16 * P_j
+ *                       tokens)
+ * Preconditions: every member's first P_j block-table entries equal those of
+ * the group's first sequence (the library reads the group's blocks from that
+ * row), and every member's context_lens holds them (n >= 16 * P_j). A member
+ * with n < 16 * P_j, or longer than max_blocks_per_seq * 16, gets a NaN row.
+ * Sequences outside every group, and groups with P_j = 0, are decoded as by
+ * pkv_paged_attention_decode. The description is used only as a whole: if
+ * group_starts is not non-decreasing inside [0, num_seqs] or some P_j lies
+ * outside [0, max_blocks_per_seq], it is ignored and every sequence is
+ * decoded plainly (still the same result).
+ *
+ * How: two launches on the stream. The suffix pass is the decode kernel over
+ * each member's blocks after its group's prefix; it leaves the members' rows
+ * as float32 (normalised output, log2-sum-exp) in the workspace. The prefix
+ * pass stacks the (member, query head) rows of a group 16 at a time against
+ * each shared tile, splits the prefix into chunks when there are few rows,
+ * and merges the chunk partials with the suffix results by the log-sum-exp
+ * rule into out.
+ *
+ *  num_groups   0..num_seqs (0: plain decode; the arrays may then be NULL)
+ *  workspace    at least pkv_shared_prefix_workspace_bytes(...) bytes,
+ *               256-byte aligned, zeroed before its first use (the
+ *               workspace rule above). One call at a time.
+ * All other arguments as for pkv_paged_attention_decode. Errors: as for
+ * pkv_paged_attention_decode, plus INVALID_ARG for num_groups outside
+ * [0, num_seqs] or a NULL group array with num_groups > 0. */
+int pkv_paged_attention_decode_shared_prefix(
+    const void *q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads, const void *k_cache,
+    const void *v_cache, const pkv_cache_desc *cache, const int32_t *block_tables,
+    int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_groups,
+    const int32_t *group_starts, const int32_t *group_prefix_blocks, float scale,
+    int32_t num_workers, void *workspace, size_t workspace_bytes, void *out, hipStream_t stream);
 
 /* Gather through the block tables (the same device addressing code as the
  * decode kernel), for checking indexing byte for byte:

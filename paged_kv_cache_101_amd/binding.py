@@ -33,6 +33,7 @@ _TORCH_CODES = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: 
 
 EXPORTS = ("pkv_status_string", "pkv_kv_bytes_per_token", "pkv_cache_tensor_bytes",
            "pkv_kv_append", "pkv_decode_workspace_bytes", "pkv_paged_attention_decode",
+           "pkv_shared_prefix_workspace_bytes", "pkv_paged_attention_decode_shared_prefix",
            "pkv_debug_gather")
 
 
@@ -76,6 +77,11 @@ def lib():
         L.pkv_paged_attention_decode.argtypes = [vp, i32, i32, i32, vp, vp, descp, vp, i32, vp,
                                                  f32, i32, vp, sz, vp, vp]
         L.pkv_paged_attention_decode.restype = ctypes.c_int
+        L.pkv_shared_prefix_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+        L.pkv_shared_prefix_workspace_bytes.restype = sz
+        L.pkv_paged_attention_decode_shared_prefix.argtypes = [
+            vp, i32, i32, i32, vp, vp, descp, vp, i32, vp, i32, vp, vp, f32, i32, vp, sz, vp, vp]
+        L.pkv_paged_attention_decode_shared_prefix.restype = ctypes.c_int
         L.pkv_debug_gather.argtypes = [vp, vp, descp, vp, i32, vp, i32, i32, vp, vp, vp]
         L.pkv_debug_gather.restype = ctypes.c_int
         _lib = L
@@ -200,6 +206,56 @@ def pkv_paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: 
         _ptr(block_tables), mb, _ptr(context_lens), float(scale), num_workers,
         _ptr(workspace), ws_bytes, _ptr(out), _stream(stream))
     _check("pkv_paged_attention_decode", rc)
+
+
+def pkv_shared_prefix_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                                      head_dim: int, num_groups: int, num_workers: int = 0) -> int:
+    return int(lib().pkv_shared_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,
+                                                       head_dim, num_groups, num_workers))
+
+
+def shared_prefix_workspace(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                            num_groups: int, num_workers: int = 0, device=None) -> torch.Tensor:
+    """A zero-filled shared-prefix decode workspace (reusable call after call)."""
+    n = pkv_shared_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                          num_groups, num_workers)
+    _need(n > 0, "invalid shared-prefix decode shape")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def pkv_paged_attention_decode_shared_prefix(
+        q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, desc: pkv_cache_desc,
+        block_tables: torch.Tensor, context_lens: torch.Tensor, group_starts: torch.Tensor,
+        group_prefix_blocks: torch.Tensor, scale: float, out: torch.Tensor, num_workers: int = 0,
+        workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """As pkv_paged_attention_decode, plus prefix groups: group_starts int32
+    [G + 1] and group_prefix_blocks int32 [G] (device); group j is sequences
+    [group_starts[j], group_starts[j + 1]) sharing their first
+    group_prefix_blocks[j] blocks."""
+    S, Hq, d = q.shape
+    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+          and block_tables.shape[0] == S, "block_tables must be int32 [S][max_blocks]")
+    _need(context_lens.dtype == torch.int32 and context_lens.numel() == S,
+          "context_lens must be int32 [S]")
+    ng = group_prefix_blocks.numel()
+    _need(group_starts.dtype == torch.int32 and group_prefix_blocks.dtype == torch.int32
+          and group_starts.numel() == ng + 1, "group arrays must be int32 [G + 1] and [G]")
+    for t in (q, k_cache, v_cache, block_tables, context_lens, out, group_starts,
+              group_prefix_blocks):
+        _need(t.is_contiguous() and t.is_cuda, "all tensors must be contiguous device tensors")
+    mb = block_tables.shape[1]
+    if workspace is None:
+        workspace = shared_prefix_workspace(S, Hq, desc.num_kv_heads, d, ng, num_workers,
+                                            q.device)
+    _need(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a device tensor")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    rc = lib().pkv_paged_attention_decode_shared_prefix(
+        _ptr(q), _dtype_of(q), S, Hq, _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
+        _ptr(block_tables), mb, _ptr(context_lens), ng, _ptr(group_starts),
+        _ptr(group_prefix_blocks), float(scale), num_workers, _ptr(workspace), ws_bytes,
+        _ptr(out), _stream(stream))
+    _check("pkv_paged_attention_decode_shared_prefix", rc)
 
 
 def pkv_debug_gather(k_cache: torch.Tensor, v_cache: torch.Tensor, desc: pkv_cache_desc,

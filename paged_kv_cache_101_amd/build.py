@@ -18,7 +18,7 @@ LIB = os.path.join(PKG, "libpkv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["pkv_api.hip", "kv_append.hip", "paged_decode.hip"]
+SOURCES = ["pkv_api.hip", "kv_append.hip", "paged_decode.hip", "shared_prefix.hip"]
 
 CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-fvisibility=hidden",

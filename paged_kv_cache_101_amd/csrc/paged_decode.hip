@@ -42,10 +42,16 @@
 // Positions >= n inside a sequence's last block are excluded by select
 // (score -inf, V element zero), never by arithmetic, so garbage or NaN there
 // cannot leak.
+//
+// Suffix pass of the shared-prefix decode (PFX): a sequence in a prefix group
+// streams only the blocks after its group's shared ones, and its rows go to a
+// float32 result (the normalised output without v_scale, and the
+// log2-sum-exp of its scores) that the prefix pass merges with the prefix's
+// partials (shared_prefix.hip). Other sequences are decoded as usual.
 #include <atomic>
 
-#include "pkv_device.h"
 #include "pkv_internal.h"
+#include "pkv_tile.h"
 
 namespace pkv {
 
@@ -67,262 +73,36 @@ struct DecodeParams {
     int* counters;        // [S][H_kv], zero on entry and on exit
     float* slots;         // [2 * num_workers][GM * (D + 2)]
     void* out;
+    // suffix pass only (PFX): the prefix-group description and the float32
+    // results of grouped sequences
+    int num_groups;
+    const int32_t* group_starts;  // [num_groups + 1]
+    const int32_t* group_prefix;  // [num_groups]
+    float* res_o;                 // [S][H_q][D]: acc / l
+    float* res_lse;               // [S][H_q]: m + log2(l), log2 units of the scores
 };
 
-constexpr float kLog2e = 1.44269504088896340736f;
 constexpr int kWavesPerGroup = 1;  // one worker wave per workgroup: any count spreads evenly
 constexpr int kThreads = kWavesPerGroup * kWave;
 constexpr int kPrefetch = 1;  // tiles whose K and V a wave has in flight
 
-// Scores are kept in log2 units; a wave only rescales its running sums when a
-// new score exceeds its running max by more than kLazyRescale (2^8 headroom
-// for the unnormalised weights, far inside float32 and f16 range). The result
-// is the same softmax: every weight is exp2(x - m) against one common m.
-constexpr float kLazyRescale = 8.0f;
-
-typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-// N dwords at byte `voff` of a buffer resource, nontemporal.
-template <int N>
-__device__ __forceinline__ void load_dwords(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t* w) {
-    constexpr int kNontemporal = 2;
-    if constexpr (N == 1) {
-        w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, kNontemporal);
-    } else if constexpr (N == 2) {
-        const u32x2_t a = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, kNontemporal);
-        w[0] = a[0];
-        w[1] = a[1];
-    } else {
-        static_assert(N % 4 == 0, "dword count");
-#pragma unroll
-        for (int c = 0; c < N / 4; ++c) {
-            const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16 * c, 0, kNontemporal);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) w[4 * c + i] = a[i];
-        }
-    }
+// Tiles of a sequence of n tokens whose first `pre` blocks are left out
+// (pre = 0: all of them). A length outside (0, max_ctx] has none.
+__device__ __forceinline__ int tiles_of(int n, int pre, int max_ctx) {
+    if (n <= 0 || n > max_ctx) return 0;
+    const int m = n - pre * kBlock;
+    return m > 0 ? (m + kBlock - 1) / kBlock : 0;
 }
 
-// The per-tile matrix work for cache type KT and query type QT.
-//   K: NK loads per lane, load i = the 8-element slab (l/16) + 4i of token l%16;
-//   V: NVL loads per lane, load i = tokens 4*(l/16) .. +3 of element columns
-//      16*(2i) + l%16 and 16*(2i+1) + l%16 (one 8-element run of the tile).
-template <int KT, int QT, int D>
-struct TileMath {
-    static constexpr int KB = Elem<KT>::bytes;
-    static constexpr int QB = Elem<QT>::bytes;
-    static constexpr int NK = D / 32;
-    static constexpr int NV = D / 16;   // P.V blocks of 16 element columns
-    static constexpr int NVL = D / 32;  // V loads (two blocks each)
-    static constexpr int KW = 2 * KB;   // dwords per K load (8 elements)
-    static constexpr int VW = KB;       // dwords of one block's 4 tokens
-    static constexpr int VLW = 2 * VW;  // dwords per V load (8 elements)
-    static constexpr bool kF32 = (KT == PKV_F32);
-    static constexpr int QW = 8 * QB / 4;  // dwords per query slab
-
-    // Query slabs of head l % 16 matching the K loads (zero for padded heads).
-    struct Q {
-        uint32_t w[NK][QW];
-    };
-
-    __device__ static void load_q(Q& q, const uint8_t* row, bool valid, int g4) {
-#pragma unroll
-        for (int i = 0; i < NK; ++i) {
-            if (valid) {
-                const uint4* src = reinterpret_cast<const uint4*>(row + (size_t)8 * (g4 + 4 * i) * QB);
-#pragma unroll
-                for (int c = 0; c < QW / 4; ++c) {
-                    const uint4 a = src[c];
-                    q.w[i][4 * c] = a.x;
-                    q.w[i][4 * c + 1] = a.y;
-                    q.w[i][4 * c + 2] = a.z;
-                    q.w[i][4 * c + 3] = a.w;
-                }
-            } else {
-#pragma unroll
-                for (int c = 0; c < QW; ++c) q.w[i][c] = 0u;
-            }
-        }
-    }
-
-    // Two fp8 codes (bytes 0-1, or 2-3 with `hi`) as two elements of the 16-bit
-    // compute type, packed in one dword. Exact: every E4M3 value is an f16
-    // and a bf16 value (the scaled conversion runs with scale 1).
-    template <bool HI>
-    __device__ static uint32_t widen_fp8_pair(uint32_t w) {
-        if constexpr (QT == PKV_F16)
-            return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
-        else
-            return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
-    }
-
-    // 8 K elements (one slab entry) in the 16-bit compute type.
-    template <typename V8>
-    __device__ static V8 k_operand(const uint32_t* kw) {
-        if constexpr (KT == PKV_FP8_E4M3) {
-            u32x4_t u;
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                u[2 * i] = widen_fp8_pair<false>(kw[i]);
-                u[2 * i + 1] = widen_fp8_pair<true>(kw[i]);
-            }
-            return __builtin_bit_cast(V8, u);
-        } else {
-            const u32x4_t u = {kw[0], kw[1], kw[2], kw[3]};
-            return __builtin_bit_cast(V8, u);
-        }
-    }
-
-    // S^T (tokens 4*(l/16) + j, head l % 16) of one tile.
-    __device__ static f32x4_t qk(const uint32_t (&kr)[NK][KW], const Q& q) {
-        f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < NK; ++i) {
-            if constexpr (kF32) {
-                // k index of MFMA e is element 8*(l/16 + 4i) + e of token / head
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    s = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, kr[i][e]),
-                                                             __builtin_bit_cast(float, q.w[i][e]),
-                                                             s, 0, 0, 0);
-            } else if constexpr (QT == PKV_F16) {
-                const u32x4_t qu = {q.w[i][0], q.w[i][1], q.w[i][2], q.w[i][3]};
-                s = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<f16x8_t>(kr[i]),
-                                                           __builtin_bit_cast(f16x8_t, qu), s, 0, 0,
-                                                           0);
-            } else {
-                const u32x4_t qu = {q.w[i][0], q.w[i][1], q.w[i][2], q.w[i][3]};
-                s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<bf16x8_t>(kr[i]),
-                                                            __builtin_bit_cast(bf16x8_t, qu), s, 0,
-                                                            0, 0);
-            }
-        }
-        return s;
-    }
-
-    // Zero the V elements of tokens this lane holds at or past the live count
-    // (nlive = live tokens among its four, any integer).
-    __device__ static void mask_v(uint32_t (&vr)[NVL][VLW], int nlive) {
-        uint32_t m[VW];
-        if constexpr (VW == 1) {
-            m[0] = nlive >= 4 ? ~0u : nlive <= 0 ? 0u : (1u << (8 * nlive)) - 1u;
-        } else if constexpr (VW == 2) {
-            m[0] = nlive >= 2 ? ~0u : nlive == 1 ? 0xFFFFu : 0u;
-            m[1] = nlive >= 4 ? ~0u : nlive == 3 ? 0xFFFFu : 0u;
-        } else {
-#pragma unroll
-            for (int i = 0; i < VW; ++i) m[i] = i < nlive ? ~0u : 0u;
-        }
-#pragma unroll
-        for (int j = 0; j < NVL; ++j)
-#pragma unroll
-            for (int i = 0; i < VLW; ++i) vr[j][i] &= m[i % VW];
-    }
-
-    // o[j] (heads 4*(l/16) + r, element 16j + l%16) += P . V_tile; returns the
-    // sum of this lane's four weights as they entered the product.
-    // (block j's 4 tokens: dwords (j % 2) * VW .. of load j / 2)
-    __device__ static float pv(const float (&pr)[4], const uint32_t (&vr)[NVL][VLW], f32x4_t (&o)[NV]) {
-        if constexpr (kF32) {
-#pragma unroll
-            for (int j = 0; j < NV; ++j)
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    o[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                        pr[kk], __builtin_bit_cast(float, vr[j / 2][(j % 2) * VW + kk]), o[j], 0, 0, 0);
-            return (pr[0] + pr[1]) + (pr[2] + pr[3]);
-        } else if constexpr (QT == PKV_F16) {
-            const f16x4_t a = {(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3]};
-#pragma unroll
-            for (int j = 0; j < NV; ++j) {
-                f16x4_t b;
-                const uint32_t* vj = &vr[j / 2][(j % 2) * VW];
-                if constexpr (KT == PKV_FP8_E4M3) {
-                    const u32x2_t u = {widen_fp8_pair<false>(vj[0]), widen_fp8_pair<true>(vj[0])};
-                    b = __builtin_bit_cast(f16x4_t, u);
-                } else {
-                    const u32x2_t u = {vj[0], vj[1]};
-                    b = __builtin_bit_cast(f16x4_t, u);
-                }
-                o[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, o[j], 0, 0, 0);
-            }
-            return ((float)a[0] + (float)a[1]) + ((float)a[2] + (float)a[3]);
-        } else {
-            const bf16x4_t a = {(__bf16)pr[0], (__bf16)pr[1], (__bf16)pr[2], (__bf16)pr[3]};
-            const i16x4_t ai = __builtin_bit_cast(i16x4_t, a);
-#pragma unroll
-            for (int j = 0; j < NV; ++j) {
-                i16x4_t b;
-                const uint32_t* vj = &vr[j / 2][(j % 2) * VW];
-                if constexpr (KT == PKV_FP8_E4M3) {
-                    const u32x2_t u = {widen_fp8_pair<false>(vj[0]), widen_fp8_pair<true>(vj[0])};
-                    b = __builtin_bit_cast(i16x4_t, u);
-                } else {
-                    const u32x2_t u = {vj[0], vj[1]};
-                    b = __builtin_bit_cast(i16x4_t, u);
-                }
-                o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ai, b, o[j], 0, 0, 0);
-            }
-            return ((float)a[0] + (float)a[1]) + ((float)a[2] + (float)a[3]);
-        }
-    }
-};
-
-// Value of `v` in lane addr / 4 (addr a byte address, as the LDS crossbar
-// takes it; no LDS memory is used).
-__device__ __forceinline__ float lane_fetch(int addr, float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(addr, __builtin_bit_cast(int, v)));
-}
-
-// Everything that computes v happens before this point, and no memory access
-// moves across it. Placed between the last use of a ring slot and the loads
-// that refill it, it keeps the compiler from sinking that use past the refill
-// (which would make the slot's old and new contents live at once, land the
-// refill in other registers and copy it back at the loop latch).
-__device__ __forceinline__ void settle(f32x4_t& v) { asm volatile("" : "+v"(v) : : "memory"); }
-
-__device__ __forceinline__ int tiles_of(int n, int max_ctx) {
-    return (n > 0 && n <= max_ctx) ? (n + kBlock - 1) / kBlock : 0;
-}
-
-// Sum over the wave, returned as a wave-uniform (scalar) value.
-__device__ __forceinline__ int wave_sum_int(int v) {
-#pragma unroll
-    for (int sh = 1; sh < kWave; sh <<= 1) v += __shfl_xor(v, sh, kWave);
-    return __builtin_amdgcn_readfirstlane(v);
-}
-
-__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int u = __shfl_up(v, d, kWave);
-        if (lane >= d) v += u;
-    }
-    return v;
-}
-
-// Partials cross between waves on different XCDs (each XCD has its own L2).
-// They are written and read with agent-scope atomic (write-through, coherent)
-// accesses, and the writer waits for its stores to complete before it bumps
-// the segment counter; no cache writeback or invalidate of a whole L2 (what a
-// device-scope fence costs on this chip) is needed.
-__device__ __forceinline__ void coherent_store(float* p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float coherent_load(const float* p) {
-    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// A wave-uniform read of an input table the kernel never writes (block
-// tables, context lengths): through the constant address space it becomes a
-// scalar load, which leaves the vector-memory wait counter to the tile data.
-__device__ __forceinline__ int32_t uniform_read(const int32_t* base, size_t i) {
-    return ((const __attribute__((address_space(4))) int32_t*)base)[i];
+// Write a float32 suffix result for rows (s, h), h < Hq, with no suffix
+// tiles: empty (n == 16 * pre: weight zero) or not valid (NaN).
+template <int D>
+__device__ __forceinline__ void write_empty_result(const DecodeParams& p, int s, bool empty,
+                                                   int lane) {
+    const int Hq = p.num_q_heads;
+    const float o = empty ? 0.f : __builtin_nanf("");
+    for (int idx = lane; idx < Hq * D; idx += kWave) p.res_o[(size_t)s * Hq * D + idx] = o;
+    for (int h = lane; h < Hq; h += kWave) p.res_lse[(size_t)s * Hq + h] = empty ? -INFINITY : o;
 }
 
 // The worker wave whose slice [a_w, a_{w+1}) holds tile f, a_w = floor(w*T/NW).
@@ -337,7 +117,8 @@ __device__ __forceinline__ int worker_of(int64_t f, int64_t total, int nw) {
 // are in flight at a time.
 template <int QT, int D, int GM>
 __device__ __forceinline__ void merge_segment(const DecodeParams& p, int w0, int w1,
-                                                        int k0, int G, size_t orow, int lane) {
+                                                        int k0, int G, size_t orow, int lane,
+                                                        bool to_result) {
     constexpr int SLOT = decode_slot_floats(GM, D);
     static_assert(D % kWave == 0, "head size must be a multiple of the wave width");
     constexpr int PER_LANE = GM * D / kWave;  // accumulator elements per lane
@@ -387,6 +168,19 @@ __device__ __forceinline__ void merge_segment(const DecodeParams& p, int w0, int
             }
         }
     }
+    if (to_result) {
+        // suffix pass: the normalised rows and their log2-sum-exp, float32
+#pragma unroll
+        for (int i = 0; i < PER_LANE; ++i) {
+            const int idx = i * kWave + lane;
+            const int h = (i * kWave) / D, e = idx % D;
+            if (idx < GM * D && h < G) p.res_o[(orow + h) * D + e] = o[i] / lsum[h];
+        }
+#pragma unroll
+        for (int h = 0; h < GM; ++h)
+            if (h < G && lane == 0) p.res_lse[orow + h] = mx[h] + __log2f(lsum[h]);
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < PER_LANE; ++i) {
         const int idx = i * kWave + lane;
@@ -395,7 +189,7 @@ __device__ __forceinline__ void merge_segment(const DecodeParams& p, int w0, int
     }
 }
 
-template <int KT, int QT, int D, int GM>
+template <int KT, int QT, int D, int GM, bool PFX>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void paged_decode_kernel(DecodeParams p) {
     using TM = TileMath<KT, QT, D>;
@@ -413,12 +207,29 @@ void paged_decode_kernel(DecodeParams p) {
     const int mb = p.max_blocks_per_seq;
     const int max_ctx = mb * kBlock;
     const float nan = __builtin_nanf("");
+    // prefix groups (suffix pass only; an unusable description counts as none)
+    const int ng = PFX ? usable_groups(p.group_starts, p.group_prefix, p.num_groups, S, mb, lane) : 0;
+    auto pre_uniform = [&](int s) -> int {
+        if constexpr (PFX) return prefix_blocks_of<true>(p.group_starts, p.group_prefix, ng, s);
+        else return 0;
+    };
+    auto pre_lane = [&](int s) -> int {
+        if constexpr (PFX) return prefix_blocks_of<false>(p.group_starts, p.group_prefix, ng, s);
+        else return 0;
+    };
 
     // Sequences with no tiles: a zero row (n <= 0) or a NaN row (n longer than
-    // the block-table row). One wave writes each.
+    // the block-table row). In the suffix pass a grouped sequence with no
+    // suffix tiles gets an empty result (n == 16 * pre) or a NaN one (its
+    // length does not hold its group's prefix). One wave writes each.
     for (int s = w; s < S; s += nw_launch) {
         const int n = p.context_lens[s];
-        if (n > 0 && n <= max_ctx) continue;
+        const int pre = pre_uniform(s);
+        if (tiles_of(n, pre, max_ctx) > 0) continue;
+        if (PFX && pre > 0) {
+            write_empty_result<D>(p, s, n == pre * kBlock, lane);
+            continue;
+        }
         const float fill = n <= 0 ? 0.f : nan;
         for (int idx = lane; idx < Hq * D; idx += kWave)
             store_f32_as<QT>(p.out, (size_t)s * Hq * D + idx, fill);
@@ -428,7 +239,7 @@ void paged_decode_kernel(DecodeParams p) {
     int64_t total = 0;
     for (int base = 0; base < S; base += kWave) {
         const int s = base + lane;
-        total += wave_sum_int(s < S ? tiles_of(p.context_lens[s], max_ctx) : 0);
+        total += wave_sum_int(s < S ? tiles_of(p.context_lens[s], pre_lane(s), max_ctx) : 0);
     }
     total *= H;
     if (total == 0) return;
@@ -444,7 +255,7 @@ void paged_decode_kernel(DecodeParams p) {
         int64_t before = 0;
         for (int base = 0; base < S; base += kWave) {
             const int s = base + lane;
-            const int t = s < S ? tiles_of(p.context_lens[s], max_ctx) * H : 0;
+            const int t = s < S ? tiles_of(p.context_lens[s], pre_lane(s), max_ctx) * H : 0;
             const int incl = wave_inclusive_scan(t, lane);
             const int64_t lo = before + incl - t;
             const unsigned long long hit = __ballot(t > 0 && lo <= a && a < before + incl);
@@ -458,11 +269,13 @@ void paged_decode_kernel(DecodeParams p) {
         }
     }
 
-    // A position in the tile stream: segment (s, g) of sequence length n and
-    // nb tiles whose first tile has index seg; block bi; the wave's slice of
-    // the segment ends at block hi. All fields are wave-uniform.
+    // A position in the tile stream: segment (s, g) of nb tiles whose first
+    // tile has index seg; block bi counted from the sequence's first streamed
+    // block pre (0 unless it is in a prefix group), n the length counted from
+    // there; the wave's slice of the segment ends at block hi. All fields are
+    // wave-uniform.
     struct Cursor {
-        int s, g, n, nb, bi, hi;
+        int s, g, n, pre, nb, bi, hi;
         int64_t seg;
     };
     // Move c to the first block of the next segment (order s, then g) inside
@@ -473,16 +286,18 @@ void paged_decode_kernel(DecodeParams p) {
         if (c.g + 1 < H) {
             ++c.g;
         } else {
-            int s = c.s + 1, n = 0, nb = 0;
+            int s = c.s + 1, n = 0, pre = 0, nb = 0;
             for (; s < S; ++s) {
                 n = uniform_read(p.context_lens, s);
-                nb = tiles_of(n, max_ctx);
+                pre = pre_uniform(s);
+                nb = tiles_of(n, pre, max_ctx);
                 if (nb > 0) break;
             }
             if (s >= S) return false;  // cannot happen: tiles after seg exist
             c.s = s;
             c.g = 0;
-            c.n = n;
+            c.n = n - pre * kBlock;
+            c.pre = pre;
             c.nb = nb;
         }
         c.seg = seg;
@@ -493,8 +308,10 @@ void paged_decode_kernel(DecodeParams p) {
 
     Cursor cc;  // the tile being computed
     cc.s = cs;
+    cc.pre = pre_uniform(cs);
     cc.n = uniform_read(p.context_lens, cs);
-    cc.nb = tiles_of(cc.n, max_ctx);
+    cc.nb = tiles_of(cc.n, cc.pre, max_ctx);
+    cc.n -= cc.pre * kBlock;
     if (cc.nb == 0) return;  // cannot happen: tile a lies in a non-empty sequence
     cc.g = (int)((a - seq_base) / cc.nb);
     cc.bi = (int)((a - seq_base) % cc.nb);
@@ -509,7 +326,7 @@ void paged_decode_kernel(DecodeParams p) {
     // Block id of ic's tile, read one tile before it is needed; -1 marks an
     // id outside the pool.
     auto read_id = [&](const Cursor& c) -> int {
-        const int id = uniform_read(p.block_tables, (size_t)c.s * mb + c.bi);
+        const int id = uniform_read(p.block_tables, (size_t)c.s * mb + c.pre + c.bi);
         return (id < 0 || id >= p.num_blocks) ? -1 : id;
     };
     int ic_id = read_id(ic);
@@ -596,7 +413,7 @@ void paged_decode_kernel(DecodeParams p) {
     // most two; they are merged after the stream, which keeps the merge's
     // loads and registers out of the streaming loop.
     struct Pending {
-        int s, g, nb;
+        int s, g, pre, nb;
         int64_t seg;
     };
     Pending pend0{}, pend1{};
@@ -666,7 +483,20 @@ void paged_decode_kernel(DecodeParams p) {
             float lt = l_run + lane_fetch(x16, l_run);
             lt += lane_fetch(x32, lt);  // weight sum of head t over the piece
             const size_t orow = (size_t)cc.s * Hq + (size_t)cc.g * G;  // first output row
-            if (clo == 0 && cc.hi == cc.nb) {
+            if (PFX && cc.pre > 0 && clo == 0 && cc.hi == cc.nb) {
+                // the whole suffix of a grouped sequence: float32 result
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int hh = 4 * g4 + r;
+                    const float inv = 1.f / lane_fetch(head_lane[r], lt);
+                    if (hh < G) {
+#pragma unroll
+                        for (int j = 0; j < NV; ++j)
+                            p.res_o[(orow + hh) * D + 16 * j + t] = piece_bad ? nan : o[j][r] * inv;
+                    }
+                }
+                if (lane < G) p.res_lse[orow + lane] = piece_bad ? nan : m_run + __log2f(lt);
+            } else if (clo == 0 && cc.hi == cc.nb) {
                 // the whole segment: normalise and store
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -703,7 +533,7 @@ void paged_decode_kernel(DecodeParams p) {
                 const int w0 = worker_of(cc.seg, total, nw);
                 const int w1 = worker_of(cc.seg + cc.nb - 1, total, nw);
                 if (old == w1 - w0) {  // every partial of the segment is in
-                    const Pending pd{cc.s, cc.g, cc.nb, cc.seg};
+                    const Pending pd{cc.s, cc.g, cc.pre, cc.nb, cc.seg};
                     if (npend == 0) pend0 = pd; else pend1 = pd;
                     ++npend;
                 }
@@ -735,7 +565,8 @@ void paged_decode_kernel(DecodeParams p) {
         const int w0 = worker_of(pd.seg, total, nw);
         const int w1 = worker_of(pd.seg + pd.nb - 1, total, nw);
         const int k0 = (int64_t)w0 * total / nw < pd.seg ? 1 : 0;
-        merge_segment<QT, D, GM>(p, w0, w1, k0, G, (size_t)pd.s * Hq + (size_t)pd.g * G, lane);
+        merge_segment<QT, D, GM>(p, w0, w1, k0, G, (size_t)pd.s * Hq + (size_t)pd.g * G, lane,
+                                 PFX && pd.pre > 0);
         if (lane == 0)
             __hip_atomic_store(p.counters + (size_t)pd.s * H + pd.g, 0, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
@@ -744,12 +575,16 @@ void paged_decode_kernel(DecodeParams p) {
 
 // ---- dispatch ------------------------------------------------------------------
 
-template <int KT, int QT, int D, int GM>
+template <int KT, int QT, int D, int GM, bool PFX>
 static hipError_t launch_typed(const DecodeArgs& a) {
-    auto kernel = paged_decode_kernel<KT, QT, D, GM>;
+    auto kernel = paged_decode_kernel<KT, QT, D, GM, PFX>;
     int nw = a.num_workers;
     if (nw == 0) {
-        // three worker waves per CU
+        // worker waves per CU so that about 12 KiB of K tiles (and as much V)
+        // are in flight per CU with one tile per wave: 3 for 16-bit d 128
+        // tiles, 6 for fp8 d 128, clamped to 2..8
+        constexpr int kTileBytes = kBlock * D * Elem<KT>::bytes;
+        constexpr int kTarget = 12288 / kTileBytes < 2 ? 2 : 12288 / kTileBytes > 8 ? 8 : 12288 / kTileBytes;
         static std::atomic<int> per_cu_cache{0};
         int per_cu = per_cu_cache.load(std::memory_order_relaxed);
         if (per_cu == 0) {
@@ -763,10 +598,12 @@ static hipError_t launch_typed(const DecodeArgs& a) {
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return hipErrorInvalidDevice;
-        // three waves per CU: measured best on the 40 x 8192 GQA shape (a sweep
-        // over 2..16 per CU); more concurrent streams lower the bandwidth the
-        // memory system delivers and widen the spread between waves
-        nw = (per_cu < 3 ? per_cu : 3) * cus * kWavesPerGroup;
+        // Measured on the 40 x 8192 fp16 GQA shape, 3 per CU is best (a sweep
+        // over 2..16 per CU): more concurrent streams lower the bandwidth the
+        // memory system delivers and widen the spread between waves. fp8
+        // tiles carry half the bytes, and the 16 x 32768 fp8 shape runs 27%
+        // faster at 6 per CU than at 3.
+        nw = (per_cu < kTarget ? per_cu : kTarget) * cus * kWavesPerGroup;
         if (nw > kMaxWorkers) nw = kMaxWorkers;
     }
     // never more workers than tiles could exist
@@ -792,25 +629,33 @@ static hipError_t launch_typed(const DecodeArgs& a) {
     p.counters = a.counters;
     p.slots = a.slots;
     p.out = a.out;
+    p.num_groups = PFX ? a.num_groups : 0;
+    p.group_starts = a.group_starts;
+    p.group_prefix = a.group_prefix;
+    p.res_o = a.res_o;
+    p.res_lse = a.res_lse;
     const int grid = (nw + kWavesPerGroup - 1) / kWavesPerGroup;
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, a.stream, p);
     return hipGetLastError();
 }
 
-template <int KT, int QT, int D>
+template <int KT, int QT, int D, bool PFX>
 static hipError_t launch_group(const DecodeArgs& a) {
     switch (padded_group(a.group)) {
-    case 1: return launch_typed<KT, QT, D, 1>(a);
-    case 2: return launch_typed<KT, QT, D, 2>(a);
-    case 4: return launch_typed<KT, QT, D, 4>(a);
-    case 6: return launch_typed<KT, QT, D, 6>(a);
-    default: return launch_typed<KT, QT, D, 8>(a);
+    case 1: return launch_typed<KT, QT, D, 1, PFX>(a);
+    case 2: return launch_typed<KT, QT, D, 2, PFX>(a);
+    case 4: return launch_typed<KT, QT, D, 4, PFX>(a);
+    case 6: return launch_typed<KT, QT, D, 6, PFX>(a);
+    default: return launch_typed<KT, QT, D, 8, PFX>(a);
     }
 }
 
 template <int KT, int QT>
 static hipError_t launch_dim(const DecodeArgs& a) {
-    return a.head_dim == 64 ? launch_group<KT, QT, 64>(a) : launch_group<KT, QT, 128>(a);
+    if (a.res_o != nullptr)
+        return a.head_dim == 64 ? launch_group<KT, QT, 64, true>(a)
+                                : launch_group<KT, QT, 128, true>(a);
+    return a.head_dim == 64 ? launch_group<KT, QT, 64, false>(a) : launch_group<KT, QT, 128, false>(a);
 }
 
 hipError_t launch_paged_decode(const DecodeArgs& a) {

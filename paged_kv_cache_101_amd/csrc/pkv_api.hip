@@ -99,15 +99,15 @@ PKV_EXPORT size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_hea
                                        num_workers == 0 ? pkv::kMaxWorkers : num_workers);
 }
 
-PKV_EXPORT int pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t num_seqs,
-                                          int32_t num_q_heads, const void* k_cache,
-                                          const void* v_cache, const pkv_cache_desc* cache,
-                                          const int32_t* block_tables,
-                                          int32_t max_blocks_per_seq,
-                                          const int32_t* context_lens, float scale,
-                                          int32_t num_workers, void* workspace,
-                                          size_t workspace_bytes, void* out,
-                                          hipStream_t stream) {
+namespace {
+
+// Checks shared by the two decode entry points (all but the workspace size),
+// filling the launch arguments.
+int decode_args(pkv::DecodeArgs& a, const void* q, int32_t q_dtype, int32_t num_seqs,
+                int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                const pkv_cache_desc* cache, const int32_t* block_tables,
+                int32_t max_blocks_per_seq, const int32_t* context_lens, float scale,
+                int32_t num_workers, void* workspace, void* out, hipStream_t stream) {
     int rc = check_cache(cache);
     if (rc != PKV_OK) return rc;
     if (num_seqs <= 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0)
@@ -130,12 +130,9 @@ PKV_EXPORT int pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_
     if (!(scale == scale)) return PKV_ERR_INVALID_ARG;
     if (num_workers < 0) return PKV_ERR_INVALID_ARG;
     if (num_workers > pkv::kMaxWorkers) return PKV_ERR_UNSUPPORTED;
-    const size_t need = pkv_decode_workspace_bytes(num_seqs, num_q_heads, cache->num_kv_heads,
-                                                   cache->head_dim, num_workers);
-    if (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
-        return PKV_ERR_WORKSPACE;
+    if (workspace == nullptr || ((uintptr_t)workspace & 255u) != 0) return PKV_ERR_WORKSPACE;
 
-    pkv::DecodeArgs a{};
+    a = pkv::DecodeArgs{};
     a.q = q;
     a.q_dtype = q_dtype;
     a.kv_dtype = kv;
@@ -154,12 +151,86 @@ PKV_EXPORT int pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_
     a.k_scale = cache->k_scale;
     a.v_scale = cache->v_scale;
     a.num_workers = num_workers;
-    a.counters = static_cast<int*>(workspace);
-    a.slots = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                       pkv::decode_counter_bytes(num_seqs, cache->num_kv_heads));
+    a.slots = static_cast<float*>(workspace);  // counters: set by the entry point
     a.out = out;
     a.stream = stream;
+    return PKV_OK;
+}
+
+}  // namespace
+
+PKV_EXPORT int pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_t num_seqs,
+                                          int32_t num_q_heads, const void* k_cache,
+                                          const void* v_cache, const pkv_cache_desc* cache,
+                                          const int32_t* block_tables,
+                                          int32_t max_blocks_per_seq,
+                                          const int32_t* context_lens, float scale,
+                                          int32_t num_workers, void* workspace,
+                                          size_t workspace_bytes, void* out,
+                                          hipStream_t stream) {
+    pkv::DecodeArgs a;
+    const int rc = decode_args(a, q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, cache,
+                               block_tables, max_blocks_per_seq, context_lens, scale, num_workers,
+                               workspace, out, stream);
+    if (rc != PKV_OK) return rc;
+    if (workspace_bytes < pkv_decode_workspace_bytes(num_seqs, num_q_heads, cache->num_kv_heads,
+                                                     cache->head_dim, num_workers))
+        return PKV_ERR_WORKSPACE;
+    a.counters = reinterpret_cast<int*>(
+        static_cast<char*>(workspace) +
+        pkv::tail_offset(workspace_bytes, pkv::decode_counter_bytes(num_seqs, cache->num_kv_heads)));
     hipError_t err = pkv::launch_paged_decode(a);
+    return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+PKV_EXPORT size_t pkv_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                                    int32_t num_kv_heads, int32_t head_dim,
+                                                    int32_t num_groups, int32_t num_workers) {
+    if (pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, num_workers) == 0 ||
+        num_groups < 0 || num_groups > num_seqs)
+        return 0;
+    return pkv::shared_prefix_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, num_groups,
+                                     num_workers == 0 ? pkv::kMaxWorkers : num_workers)
+        .total;
+}
+
+PKV_EXPORT int pkv_paged_attention_decode_shared_prefix(
+    const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads, const void* k_cache,
+    const void* v_cache, const pkv_cache_desc* cache, const int32_t* block_tables,
+    int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_groups,
+    const int32_t* group_starts, const int32_t* group_prefix_blocks, float scale,
+    int32_t num_workers, void* workspace, size_t workspace_bytes, void* out, hipStream_t stream) {
+    pkv::DecodeArgs a;
+    const int rc = decode_args(a, q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, cache,
+                               block_tables, max_blocks_per_seq, context_lens, scale, num_workers,
+                               workspace, out, stream);
+    if (rc != PKV_OK) return rc;
+    if (num_groups < 0 || num_groups > num_seqs) return PKV_ERR_INVALID_ARG;
+    if (num_groups > 0 && (group_starts == nullptr || group_prefix_blocks == nullptr))
+        return PKV_ERR_INVALID_ARG;
+    if (workspace_bytes < pkv_shared_prefix_workspace_bytes(num_seqs, num_q_heads,
+                                                            cache->num_kv_heads, cache->head_dim,
+                                                            num_groups, num_workers))
+        return PKV_ERR_WORKSPACE;
+    const pkv::SharedPrefixLayout l =
+        pkv::shared_prefix_layout(num_seqs, num_q_heads, cache->num_kv_heads, cache->head_dim,
+                                  num_groups, num_workers == 0 ? pkv::kMaxWorkers : num_workers);
+    char* ws = static_cast<char*>(workspace);
+    const size_t dctr = pkv::tail_offset(workspace_bytes, l.decode_counter_bytes);
+    a.counters = reinterpret_cast<int*>(ws + dctr);
+    hipError_t err;
+    if (num_groups == 0) {
+        err = pkv::launch_paged_decode(a);  // no prefix groups: plain decode
+    } else {
+        a.num_groups = num_groups;
+        a.group_starts = group_starts;
+        a.group_prefix = group_prefix_blocks;
+        a.res_o = reinterpret_cast<float*>(ws + l.res_o);
+        a.res_lse = reinterpret_cast<float*>(ws + l.res_lse);
+        a.prefix_slots = reinterpret_cast<float*>(ws + l.prefix_slots);
+        a.prefix_counters = reinterpret_cast<int*>(ws + dctr - l.prefix_counter_bytes);
+        err = pkv::launch_shared_prefix(a);
+    }
     return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

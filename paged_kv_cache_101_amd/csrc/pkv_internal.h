@@ -19,16 +19,76 @@ constexpr int padded_group(int g) { return g <= 1 ? 1 : g <= 2 ? 2 : g <= 4 ? 4 
 // heads x D, then GM maxima and GM sums, padded to a multiple of 4 floats.
 constexpr int decode_slot_floats(int gm, int d) { return gm * d + ((2 * gm + 3) & ~3); }
 
-// Decode workspace: int32 counters [S][H_kv] (rounded up to 256 bytes), then
-// 2 * workers partial slots.
+inline size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Workspaces keep float scratch at the front and the int32 counters (which
+// must be zero when a call starts, and are left zero by every call) in the
+// last bytes. Float scratch of any call fits below the counters of any other
+// call sized no larger, so one workspace, zeroed once and sized for the
+// largest shape, serves every smaller call without clearing it again.
+//
+// Decode: 2 * workers partial slots at the front, counters [S][H_kv] at the
+// end, each part a multiple of 256 bytes.
+inline size_t decode_slot_bytes(int num_q_heads, int num_kv_heads, int head_dim, int workers) {
+    const int gm = padded_group(num_q_heads / num_kv_heads);
+    return round256((size_t)2 * workers * decode_slot_floats(gm, head_dim) * sizeof(float));
+}
 inline size_t decode_counter_bytes(int num_seqs, int num_kv_heads) {
-    return (((size_t)num_seqs * num_kv_heads * sizeof(int32_t)) + 255) & ~(size_t)255;
+    return round256((size_t)num_seqs * num_kv_heads * sizeof(int32_t));
 }
 inline size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
                                      int head_dim, int workers) {
-    const int gm = padded_group(num_q_heads / num_kv_heads);
-    return decode_counter_bytes(num_seqs, num_kv_heads) +
-           (size_t)2 * workers * decode_slot_floats(gm, head_dim) * sizeof(float);
+    return decode_slot_bytes(num_q_heads, num_kv_heads, head_dim, workers) +
+           decode_counter_bytes(num_seqs, num_kv_heads);
+}
+// Start of the last `bytes` bytes of a workspace of ws_bytes (256-aligned).
+inline size_t tail_offset(size_t ws_bytes, size_t bytes) { return (ws_bytes & ~(size_t)255) - bytes; }
+
+// ---- shared-prefix decode ----------------------------------------------------
+// The prefix pass aims at about this many tasks (KV head x row block of 16
+// query rows x chunk of the prefix): four waves per CU of a 256-CU device.
+constexpr int kPrefixTargetTasks = 1024;
+
+// One prefix partial: accumulators [16 rows][D], then 16 maxima and 16 sums.
+constexpr int prefix_slot_floats(int d) { return 16 * d + 32; }
+
+// Row blocks of 16 (member, head) rows over all groups, at most.
+inline int64_t prefix_row_blocks_bound(int num_seqs, int group, int num_groups) {
+    return ((int64_t)num_seqs * group + 15) / 16 + num_groups;
+}
+// Prefix tasks, at most: H * row blocks with one chunk, else fewer than
+// 2 * target (the chunk count is ceil(target / (H * row blocks))).
+inline int64_t prefix_task_bound(int num_seqs, int group, int num_kv_heads, int num_groups) {
+    const int64_t one = (int64_t)num_kv_heads * prefix_row_blocks_bound(num_seqs, group, num_groups);
+    return one > 2 * kPrefixTargetTasks ? one : 2 * kPrefixTargetTasks;
+}
+
+// Byte offsets in the shared-prefix workspace. Front: the suffix pass's
+// decode slots, the float32 suffix results [S][H_q][D] and [S][H_q], and
+// 2 * target prefix partial slots. End: the prefix pass's counters
+// [H_kv][row blocks], then the suffix pass's counters [S][H_kv].
+struct SharedPrefixLayout {
+    size_t res_o, res_lse, prefix_slots, floats;   // float part (from the start)
+    size_t prefix_counter_bytes, decode_counter_bytes;
+    size_t total;
+};
+inline SharedPrefixLayout shared_prefix_layout(int num_seqs, int num_q_heads, int num_kv_heads,
+                                               int head_dim, int num_groups, int workers) {
+    SharedPrefixLayout l;
+    size_t off = decode_slot_bytes(num_q_heads, num_kv_heads, head_dim, workers);
+    l.res_o = off;
+    off += round256((size_t)num_seqs * num_q_heads * head_dim * sizeof(float));
+    l.res_lse = off;
+    off += round256((size_t)num_seqs * num_q_heads * sizeof(float));
+    l.prefix_slots = off;
+    off += round256((size_t)2 * kPrefixTargetTasks * prefix_slot_floats(head_dim) * sizeof(float));
+    l.floats = off;
+    l.prefix_counter_bytes = round256(
+        (size_t)num_kv_heads * prefix_row_blocks_bound(num_seqs, num_q_heads / num_kv_heads, num_groups) *
+        sizeof(int32_t));
+    l.decode_counter_bytes = decode_counter_bytes(num_seqs, num_kv_heads);
+    l.total = l.floats + l.prefix_counter_bytes + l.decode_counter_bytes;
+    return l;
 }
 
 struct DecodeArgs {
@@ -54,6 +114,16 @@ struct DecodeArgs {
     float* slots;     // partial slots
     void* out;
     hipStream_t stream;
+    // Shared-prefix decode only. With res_o set, the decode launch is the
+    // suffix pass: grouped sequences skip their shared blocks and leave
+    // float32 results in res_o / res_lse instead of writing out.
+    int num_groups = 0;
+    const int32_t* group_starts = nullptr;  // [num_groups + 1] (device)
+    const int32_t* group_prefix = nullptr;  // [num_groups] (device)
+    float* res_o = nullptr;                 // [S][H_q][D]
+    float* res_lse = nullptr;               // [S][H_q]
+    int* prefix_counters = nullptr;         // prefix pass: [H_kv][row blocks], zero on entry
+    float* prefix_slots = nullptr;          // prefix pass: partial slots
 };
 
 hipError_t launch_kv_append(const void* k, const void* v, int elem_bytes,
@@ -67,6 +137,10 @@ hipError_t launch_kv_append_fp8(const void* k, const void* v, int src_dtype,
                                 float k_scale, float v_scale, hipStream_t stream);
 
 hipError_t launch_paged_decode(const DecodeArgs& a);
+
+// The shared-prefix decode: the suffix pass (launch_paged_decode with res_o
+// set), then the prefix pass that merges and writes out.
+hipError_t launch_shared_prefix(const DecodeArgs& a);
 
 hipError_t launch_gather(const void* k_cache, const void* v_cache, int elem_bytes,
                          int num_blocks, int num_kv_heads, int head_dim,

@@ -99,6 +99,10 @@ class DecodeBatch:
     new_k: Optional[torch.Tensor] = None   # [T][H_kv][d]
     new_v: Optional[torch.Tensor] = None
     slot_mapping: Optional[torch.Tensor] = None  # int64 [T]
+    # prefix groups: sequences [starts[j], starts[j+1]) share their first
+    # prefix[j] blocks (None: no description)
+    group_starts: Optional[torch.Tensor] = None  # int32 [G + 1]
+    group_prefix: Optional[torch.Tensor] = None  # int32 [G]
     meta: dict = field(default_factory=dict)
 
     @property
@@ -120,28 +124,69 @@ class DecodeBatch:
         return n * 2 * self.num_kv_heads * self.head_dim * b
 
 
+def group_prefix_of(num_seqs: int, groups) -> np.ndarray:
+    """Shared blocks of each sequence under a list of (start, end, blocks)."""
+    pre = np.zeros(num_seqs, dtype=np.int64)
+    for a, b, p in groups:
+        pre[a:b] = p
+    return pre
+
+
+def group_arrays(groups):
+    """The library's description of (start, end, blocks) groups: group j is
+    sequences [starts[j], starts[j + 1]), so groups are adjacent runs; a gap
+    between two groups becomes a group with no shared blocks."""
+    starts, prefix, end = [], [], None
+    for a, b, p in sorted(groups):
+        if end is not None and a > end:
+            starts.append(end)
+            prefix.append(0)
+        starts.append(a)
+        prefix.append(p)
+        end = b
+    if end is not None:
+        starts.append(end)
+    return starts, prefix
+
+
+def blocks_needed(blocks_per_seq: Sequence[int], groups) -> int:
+    """Physical blocks a batch uses: each group's prefix once, plus every
+    sequence's own blocks."""
+    pre = group_prefix_of(len(blocks_per_seq), groups)
+    return int(sum(p for _, _, p in groups) +
+               sum(max(0, b - pre[s]) for s, b in enumerate(blocks_per_seq)))
+
+
 def assign_blocks(blocks_per_seq: Sequence[int], num_blocks: int, rng: np.random.Generator,
-                  shared_prefix_blocks: int = 0, max_blocks: Optional[int] = None):
+                  shared_prefix_blocks: int = 0, max_blocks: Optional[int] = None,
+                  groups=None):
     """Block tables from a shuffled pool; block 0 is the null block.
 
-    The first ``shared_prefix_blocks`` logical blocks of every sequence map to
-    the same physical blocks (one copy of a common prefix)."""
+    ``groups`` lists (start, end, P): sequences [start, end) map their first P
+    logical blocks to the same P physical blocks (one copy of a common
+    prefix). ``shared_prefix_blocks`` is the one-group case over every
+    sequence. Each group's blocks are handed out first, in group order."""
     S = len(blocks_per_seq)
+    if groups is None:
+        groups = [(0, S, shared_prefix_blocks)] if shared_prefix_blocks else []
     mb = max_blocks if max_blocks is not None else max(1, max(blocks_per_seq))
-    need = shared_prefix_blocks + sum(max(0, b - shared_prefix_blocks) for b in blocks_per_seq)
+    need = blocks_needed(blocks_per_seq, groups)
     if need > num_blocks - 1:
         raise ValueError(f"pool of {num_blocks} blocks too small for {need} (+1 null)")
     ids = rng.permutation(np.arange(1, num_blocks, dtype=np.int64))
     bt = np.zeros((S, mb), dtype=np.int32)
-    shared = ids[:shared_prefix_blocks]
-    nxt = shared_prefix_blocks
+    nxt = 0
+    for a, b, p in groups:
+        shared = ids[nxt:nxt + p]
+        nxt += p
+        for s in range(a, b):
+            n = min(p, blocks_per_seq[s])
+            bt[s, :n] = shared[:n]
+    pre = group_prefix_of(S, groups)
     for s, nb in enumerate(blocks_per_seq):
-        for i in range(nb):
-            if i < shared_prefix_blocks:
-                bt[s, i] = shared[i]
-            else:
-                bt[s, i] = ids[nxt]
-                nxt += 1
+        for i in range(int(pre[s]), nb):
+            bt[s, i] = ids[nxt]
+            nxt += 1
     return bt
 
 
@@ -168,6 +213,7 @@ def make_batch(name: str, case_id: int, context_lens: Sequence[int], num_q_heads
                num_kv_heads: int, head_dim: int, kv_dtype: str, q_dtype: str,
                device="cpu", layer: int = 0, num_blocks: Optional[int] = None,
                pool_factor: float = 1.0, shared_prefix_blocks: int = 0,
+               prefix_groups=None,
                max_blocks: Optional[int] = None, canary: bool = False,
                append_last: bool = False,
                scale: Optional[float] = None, structure_layer: Optional[int] = None) -> DecodeBatch:
@@ -182,11 +228,14 @@ def make_batch(name: str, case_id: int, context_lens: Sequence[int], num_q_heads
     S = ctx.shape[0]
     bps = [(max(int(n), 0) + BLOCK - 1) // BLOCK for n in ctx]
     mb = max_blocks if max_blocks is not None else max(1, max(bps) if bps else 1)
-    need = shared_prefix_blocks + sum(max(0, b - shared_prefix_blocks) for b in bps)
+    if prefix_groups is None:
+        prefix_groups = [(0, S, shared_prefix_blocks)] if shared_prefix_blocks else []
+    prefix_groups = [(int(a), int(b), int(p)) for a, b, p in prefix_groups]
+    need = blocks_needed(bps, prefix_groups)
     if num_blocks is None:
         num_blocks = int(math.ceil(pool_factor * need)) + 1
     rng = np.random.default_rng([case_id, 1, layer if structure_layer is None else structure_layer])
-    bt = assign_blocks(bps, num_blocks, rng, shared_prefix_blocks, mb)
+    bt = assign_blocks(bps, num_blocks, rng, max_blocks=mb, groups=prefix_groups)
 
     H, d = num_kv_heads, head_dim
     cache_shape = (num_blocks, H, BLOCK, d)
@@ -234,6 +283,7 @@ def make_batch(name: str, case_id: int, context_lens: Sequence[int], num_q_heads
         new_v = to_storage(nv, kv_dtype, v_scale)
 
     q = qx.to(STORAGE[q_dtype][0])
+    starts, prefix = group_arrays(prefix_groups)
     return DecodeBatch(
         name=name, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
         kv_dtype=kv_dtype, q_dtype=q_dtype, num_blocks=num_blocks,
@@ -242,7 +292,12 @@ def make_batch(name: str, case_id: int, context_lens: Sequence[int], num_q_heads
         scale=scale if scale is not None else 1.0 / math.sqrt(head_dim),
         k_scale=k_scale, v_scale=v_scale,
         new_k=new_k, new_v=new_v, slot_mapping=slot_mapping,
-        meta={"case_id": case_id, "layer": layer, "shared_prefix_blocks": shared_prefix_blocks})
+        group_starts=(torch.tensor(starts, dtype=torch.int32, device=device)
+                      if prefix_groups else None),
+        group_prefix=(torch.tensor(prefix, dtype=torch.int32, device=device)
+                      if prefix_groups else None),
+        meta={"case_id": case_id, "layer": layer, "shared_prefix_blocks": shared_prefix_blocks,
+              "prefix_groups": prefix_groups})
 
 
 # ---- the five workloads ----------------------------------------------------

@@ -104,3 +104,19 @@ def assert_close(got: np.ndarray, ref: np.ndarray, kv_dtype: str, what: str = ""
     assert e["mean"] <= tol["mean"], f"{what}: mean err {e['mean']:.3g} > {tol['mean']} ({e})"
     assert e["rel_rms"] <= tol["rel_rms"], f"{what}: rel rms {e['rel_rms']:.3g} ({e})"
     return e
+
+
+def gpu_shared_decode(b: W.DecodeBatch, num_workers=0, out=None, workspace=None,
+                      group_starts=None, group_prefix=None, context_lens=None) -> torch.Tensor:
+    """The shared-prefix decode of a batch, with its own prefix groups unless
+    others are given."""
+    if out is None:
+        out = torch.empty_like(b.q)
+    kc, vc = device_caches(b)
+    gs = b.group_starts if group_starts is None else group_starts
+    gp = b.group_prefix if group_prefix is None else group_prefix
+    cl = b.context_lens if context_lens is None else context_lens
+    B.pkv_paged_attention_decode_shared_prefix(b.q, kc, vc, desc(b), b.block_tables, cl, gs, gp,
+                                               b.scale, out, num_workers=num_workers,
+                                               workspace=workspace)
+    return out

@@ -57,16 +57,20 @@ def _slot_floats(gp, d):
     return gp * d + ((2 * gp + 3) // 4) * 4
 
 
+def r256(x):
+    return -(-x // 256) * 256
+
+
 def test_workspace_bytes_formula():
-    # counters [S][H_kv] int32 rounded up to 256 B, then 2 slots per worker
-    ctr = -(-40 * 8 * 4 // 256) * 256
-    assert B.pkv_decode_workspace_bytes(40, 32, 8, 128, 2048) == ctr + 2 * 2048 * _slot_floats(4, 128) * 4
-    assert B.pkv_decode_workspace_bytes(40, 32, 8, 128, 0) == ctr + 2 * 4096 * _slot_floats(4, 128) * 4
+    # 2 slots per worker, then counters [S][H_kv] int32, each rounded up to 256 B
+    ctr = r256(40 * 8 * 4)
+    assert B.pkv_decode_workspace_bytes(40, 32, 8, 128, 2048) == r256(2 * 2048 * _slot_floats(4, 128) * 4) + ctr
+    assert B.pkv_decode_workspace_bytes(40, 32, 8, 128, 0) == r256(2 * 4096 * _slot_floats(4, 128) * 4) + ctr
     # G = 6 and G = 5 use 6-head slots, G = 3 uses 4, G = 7 uses 8
-    assert B.pkv_decode_workspace_bytes(64, 12, 2, 128, 10) == 512 + 20 * _slot_floats(6, 128) * 4
-    assert B.pkv_decode_workspace_bytes(1, 5, 1, 64, 1) == 256 + 2 * _slot_floats(6, 64) * 4
-    assert B.pkv_decode_workspace_bytes(1, 3, 1, 64, 1) == 256 + 2 * _slot_floats(4, 64) * 4
-    assert B.pkv_decode_workspace_bytes(1, 7, 1, 64, 1) == 256 + 2 * _slot_floats(8, 64) * 4
+    assert B.pkv_decode_workspace_bytes(64, 12, 2, 128, 10) == 512 + r256(20 * _slot_floats(6, 128) * 4)
+    assert B.pkv_decode_workspace_bytes(1, 5, 1, 64, 1) == 256 + r256(2 * _slot_floats(6, 64) * 4)
+    assert B.pkv_decode_workspace_bytes(1, 3, 1, 64, 1) == 256 + r256(2 * _slot_floats(4, 64) * 4)
+    assert B.pkv_decode_workspace_bytes(1, 7, 1, 64, 1) == 256 + r256(2 * _slot_floats(8, 64) * 4)
     assert B.pkv_decode_workspace_bytes(4, 4, 3, 64, 1) == 0        # 4 % 3 != 0
     assert B.pkv_decode_workspace_bytes(4, 18, 2, 64, 1) == 0       # G = 9
     assert B.pkv_decode_workspace_bytes(4, 4, 1, 64, -1) == 0
@@ -127,9 +131,55 @@ def _append(**kw):
     (dict(desc=B.pkv_cache_desc(16, 8, 2, 128, B.PKV_F16, 1, 1)), B.PKV_ERR_UNSUPPORTED),
     (dict(v=FAKE + 8), B.PKV_ERR_INVALID_ARG),
     (dict(T=0, k=None, v=None, slots=None), B.PKV_OK),        # empty append is a no-op
+    # quantising append: 16/32-bit rows into an fp8 cache, never the reverse
+    (dict(T=0, dt=B.PKV_BF16, desc=B.cache_desc(16, 2, 128, "fp8", 0.5, 0.5)), B.PKV_OK),
+    (dict(T=0, dt=B.PKV_F32, desc=B.cache_desc(16, 2, 128, "fp8", 0.5, 0.5)), B.PKV_OK),
+    (dict(dt=B.PKV_FP8_E4M3), B.PKV_ERR_UNSUPPORTED),         # fp8 rows into an f16 cache
+    (dict(dt=B.PKV_F16, desc=B.cache_desc(16, 2, 128, "fp8", 0.0, 0.5)), B.PKV_ERR_INVALID_ARG),
 ])
 def test_append_rejects_before_any_hip_call(kw, status):
     assert _append(**kw) == status
+
+
+def test_shared_prefix_workspace_bytes_formula():
+    S, Hq, H, d, ng, W = 256, 32, 8, 128, 3, 768
+    base = B.pkv_decode_workspace_bytes(S, Hq, H, d, W)  # decode slots + decode counters
+    res = r256(S * Hq * d * 4) + r256(S * Hq * 4)
+    ctr = r256(H * (-(-S * (Hq // H) // 16) + ng) * 4)
+    slots = r256(2 * 1024 * (16 * d + 32) * 4)
+    assert B.pkv_shared_prefix_workspace_bytes(S, Hq, H, d, ng, W) == base + res + ctr + slots
+    assert B.pkv_shared_prefix_workspace_bytes(S, Hq, H, d, ng, 0) == \
+        B.pkv_decode_workspace_bytes(S, Hq, H, d, 0) + res + ctr + slots
+    assert B.pkv_shared_prefix_workspace_bytes(S, Hq, H, d, -1, W) == 0
+    assert B.pkv_shared_prefix_workspace_bytes(S, Hq, H, d, S + 1, W) == 0
+    assert B.pkv_shared_prefix_workspace_bytes(4, 18, 2, 64, 1, 1) == 0  # G = 9
+
+
+def _shared(**kw):
+    a = dict(q=FAKE, q_dtype=B.PKV_BF16, S=4, Hq=8, k=FAKE, v=FAKE,
+             desc=B.cache_desc(16, 2, 128, "bf16"), bt=FAKE, mb=64, cl=FAKE, ng=1, gs=FAKE,
+             gp=FAKE, scale=0.1, P=0, ws=FAKE, ws_bytes=1 << 40, out=FAKE)
+    a.update(kw)
+    return B.lib().pkv_paged_attention_decode_shared_prefix(
+        a["q"], a["q_dtype"], a["S"], a["Hq"], a["k"], a["v"], ctypes.byref(a["desc"]), a["bt"],
+        a["mb"], a["cl"], a["ng"], a["gs"], a["gp"], a["scale"], a["P"], a["ws"], a["ws_bytes"],
+        a["out"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ng=-1), B.PKV_ERR_INVALID_ARG),
+    (dict(ng=5), B.PKV_ERR_INVALID_ARG),                      # more groups than sequences
+    (dict(gs=None), B.PKV_ERR_INVALID_ARG),
+    (dict(gp=None), B.PKV_ERR_INVALID_ARG),
+    (dict(q=None), B.PKV_ERR_INVALID_ARG),
+    (dict(Hq=18), B.PKV_ERR_UNSUPPORTED),
+    (dict(q_dtype=B.PKV_F16), B.PKV_ERR_UNSUPPORTED),         # f16 q over a bf16 cache
+    (dict(ws=None), B.PKV_ERR_WORKSPACE),
+    (dict(ws_bytes=1 << 20), B.PKV_ERR_WORKSPACE),            # a decode-sized one is too small
+    (dict(ws=FAKE + 16), B.PKV_ERR_WORKSPACE),
+])
+def test_shared_prefix_rejects_before_any_hip_call(kw, status):
+    assert _shared(**kw) == status
 
 
 def test_gather_rejects_bad_args():

@@ -153,6 +153,22 @@ def test_workspace_reuse_leaves_counters_zero(gpu):
         again = gpu_decode(b, 37, workspace=ws)
         assert W.to_numpy(again).tobytes() == W.to_numpy(first).tobytes()
     torch.cuda.synchronize()
-    assert int(ws[: b.num_seqs * b.num_kv_heads * 4].view(torch.int32).abs().sum()) == 0
+    # the counters [S][H_kv] sit in the workspace's last 256-byte-rounded bytes
+    assert int(ws[-256:].view(torch.int32).abs().sum()) == 0
     ref = oracle_decode(b)
     assert_close(out_to_f64(first), ref, "f16", "reuse")
+
+
+def test_workspace_sized_once_serves_smaller_calls(gpu):
+    """A workspace sized for the largest shape and zeroed once serves calls
+    with fewer sequences and other worker counts, in any order."""
+    from paged_kv_cache_101_amd import binding as B
+    big = W.make_batch("ws-big", 75, [3000, 17, 4500, 900, 64, 2500], 32, 8, 128, "f16", "f16",
+                       device=gpu)
+    small = W.make_batch("ws-small", 76, [700, 5000], 32, 8, 128, "f16", "f16", device=gpu)
+    ws = B.decode_workspace(6, 32, 8, 128, 0, gpu)
+    ref_big, ref_small = oracle_decode(big), oracle_decode(small)
+    for b, nw, ref in ((small, 0, ref_small), (big, 300, ref_big), (small, 5, ref_small),
+                       (big, 0, ref_big), (small, 2048, ref_small), (big, 1, ref_big)):
+        got = gpu_decode(b, nw, workspace=ws)
+        assert_close(out_to_f64(got), ref, "f16", f"S={b.num_seqs} workers={nw}")
