@@ -16,8 +16,12 @@ kernel (the decode kernel, one launch per layer) timed with HIP events on the
 stream it runs on, plus the CPU oracle timed on a bounded sample of the same
 workload on this host's cores.
 
-Other workloads (--workload qwen|prefix|fp8|tiny) time the decode call alone
-and print the same fields; they are for profiling, not the headline line.
+Other workloads (--workload qwen|prefix|prefix_shared|fp8|tiny) time the
+decode call alone and print the same fields; they are for profiling, not the
+headline line. prefix_shared is the prefix workload through the shared-prefix
+decode (each shared block read once per KV head): its value and roofline
+count the unique KV bytes (the shared prefix once, every suffix), and it also
+reports the logical bytes plain decode would read.
 """
 import argparse
 import json
@@ -39,7 +43,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="gqa40", choices=["gqa40", "qwen", "prefix", "fp8", "tiny"])
+    ap.add_argument("--workload", default="gqa40",
+                    choices=["gqa40", "qwen", "prefix", "prefix_shared", "fp8", "tiny"])
     ap.add_argument("--workers", type=int, default=0, help="worker waves (0 = fill the device)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -95,7 +100,7 @@ def build_layers(workload: str, device):
         layers = [W.gqa40_layer(device=device, layer=l, append_last=True) for l in range(40)]
     elif workload == "qwen":
         layers = [W.qwen_layer(device=device)]
-    elif workload == "prefix":
+    elif workload in ("prefix", "prefix_shared"):
         layers = [W.prefix_shared(device=device)]
     elif workload == "fp8":
         layers = [W.fp8_long(device=device)]
@@ -111,6 +116,8 @@ def describe(workload: str, layers, workers: int) -> dict:
             "gqa40": "40-layer GQA decode step: 40 layers x 40 seqs x 8192 ctx",
             "qwen": "Qwen2.5-1.5B-shaped layer decode: 64 seqs, ctx U[128,4096]",
             "prefix": "prefix sharing decode: 256 seqs, 2048 shared + U[64,512] ctx",
+            "prefix_shared": "prefix sharing decode, shared-prefix path: 256 seqs, "
+                             "2048 shared + U[64,512] ctx",
             "fp8": "long-context fp8 decode: 16 seqs x 32768 ctx",
             "tiny": "tiny MQA decode: 4 seqs, ctx {1,15,16,33}",
         }[workload],
@@ -186,8 +193,14 @@ def main():
     torch.cuda.empty_cache()
     outs = [torch.empty_like(b.q) for b in layers]
     b0 = layers[0]
-    ws = B.decode_workspace(b0.num_seqs, b0.num_q_heads, b0.num_kv_heads, b0.head_dim,
-                            args.workers, dev)
+    shared = args.workload == "prefix_shared"
+    if shared:
+        ng = int(b0.group_prefix.numel())
+        ws = B.shared_prefix_workspace(b0.num_seqs, b0.num_q_heads, b0.num_kv_heads, b0.head_dim,
+                                       ng, args.workers, dev)
+    else:
+        ws = B.decode_workspace(b0.num_seqs, b0.num_q_heads, b0.num_kv_heads, b0.head_dim,
+                                args.workers, dev)
     do_append = args.workload == "gqa40"
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
@@ -198,9 +211,14 @@ def main():
                 B.pkv_kv_append(b.new_k, b.new_v, b.slot_mapping, *caches[i], descs[i])
             if evs is not None:
                 evs[i][0].record(stream)
-            B.pkv_paged_attention_decode(b.q, *caches[i], descs[i], b.block_tables,
-                                         b.context_lens, b.scale, outs[i],
-                                         num_workers=args.workers, workspace=ws)
+            if shared:
+                B.pkv_paged_attention_decode_shared_prefix(
+                    b.q, *caches[i], descs[i], b.block_tables, b.context_lens, b.group_starts,
+                    b.group_prefix, b.scale, outs[i], num_workers=args.workers, workspace=ws)
+            else:
+                B.pkv_paged_attention_decode(b.q, *caches[i], descs[i], b.block_tables,
+                                             b.context_lens, b.scale, outs[i],
+                                             num_workers=args.workers, workspace=ws)
             if evs is not None:
                 evs[i][1].record(stream)
 
@@ -225,6 +243,14 @@ def main():
     decode_avg_ms = statistics.fmean(decode_ms)
     kv_bytes_step = sum(b.kv_bytes() for b in layers)
     kv_bytes_launch = b0.kv_bytes()
+    logical_launch = kv_bytes_launch
+    if shared:
+        # bytes a call must read: every physical row some sequence attends to, once
+        used = W.used_rows_per_block(b0.block_tables.cpu().numpy(), b0.context_lens.cpu().numpy(),
+                                     b0.num_blocks)
+        kv_bytes_launch = int(used.sum()) * 2 * b0.num_kv_heads * b0.head_dim * \
+            W.STORAGE[b0.kv_dtype][1]
+        kv_bytes_step = kv_bytes_launch * len(layers)
     seqs = b0.num_seqs
     value = kv_bytes_step / (ms_step * 1e-3) / 1e9
     achieved = kv_bytes_launch / (decode_avg_ms * 1e-3) / 1e9
@@ -232,7 +258,9 @@ def main():
     roofline = {
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-        "kernel": "paged_decode_kernel (one launch per pkv_paged_attention_decode call)",
+        "kernel": ("paged_decode_kernel suffix pass + shared_prefix_kernel (two launches per "
+                   "pkv_paged_attention_decode_shared_prefix call)" if shared else
+                   "paged_decode_kernel (one launch per pkv_paged_attention_decode call)"),
         "algorithmic_bytes_per_launch": kv_bytes_launch,
         "launch_avg_us": round(decode_avg_ms * 1e3, 2),
         "launch_p10_us": round(sorted(decode_ms)[len(decode_ms) // 10] * 1e3, 2),
@@ -252,6 +280,9 @@ def main():
         "kv_bytes_per_step": kv_bytes_step,
         "roofline": roofline, "cpu_baseline": cpu,
     }
+    if shared:
+        line["logical_kv_bytes_per_launch"] = logical_launch
+        line["logical_kv_gbps"] = round(logical_launch / (decode_avg_ms * 1e-3) / 1e9, 1)
     print(json.dumps(line), flush=True)
 
 

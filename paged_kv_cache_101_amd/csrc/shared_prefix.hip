@@ -32,6 +32,12 @@ namespace {
 
 constexpr int kRows = 16;  // query rows per task: the MFMA column count
 
+// Tiles a wave has in flight: up to 4, as many as 128 registers per lane
+// hold (float32 tiles of 128 elements: 2).
+constexpr int prefix_prefetch(int tile_dwords_per_lane) {
+    return 128 / tile_dwords_per_lane >= 4 ? 4 : 128 / tile_dwords_per_lane < 1 ? 1 : 128 / tile_dwords_per_lane;
+}
+
 struct PrefixParams {
     const uint8_t* q;
     const uint8_t* k_cache;
@@ -188,65 +194,78 @@ void shared_prefix_kernel(PrefixParams p) {
             if (id < 0 || id >= p.num_blocks) return TileRef{0, 0u, true};
             return TileRef{tile_elem_offset(id, g, H, D) * KB, kTileBytes, false};
         };
-        uint32_t kr[NK][KW], vr[NVL][VLW];
-        auto issue_k = [&](TileRef tr) {
+        // A ring of PF tiles in flight: tile b + PF is requested into the slot
+        // that tile b leaves, K as soon as the scores are out, V after P.V.
+        constexpr int PF = prefix_prefetch(NK * KW + NVL * VLW);
+        uint32_t kr[PF][NK][KW], vr[PF][NVL][VLW];
+        auto issue_k = [&](int slot, TileRef tr) {
             const __amdgpu_buffer_rsrc_t r = make_rsrc(p.k_cache + tr.off, tr.bytes);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int k = 0; k < NK; ++k)
-                load_dwords<KW, kLoadCached>(r, k_off + k * 4 * kBlock * 8 * KB, kr[k]);
+                load_dwords<KW, kLoadCached>(r, k_off + k * 4 * kBlock * 8 * KB, kr[slot][k]);
             __builtin_amdgcn_sched_barrier(0);
         };
-        auto issue_v = [&](TileRef tr) {
+        auto issue_v = [&](int slot, TileRef tr) {
             const __amdgpu_buffer_rsrc_t r = make_rsrc(p.v_cache + tr.off, tr.bytes);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int k = 0; k < NVL; ++k)
-                load_dwords<VLW, kLoadCached>(r, v_off + k * 32 * kBlock * KB, vr[k]);
+                load_dwords<VLW, kLoadCached>(r, v_off + k * 32 * kBlock * KB, vr[slot][k]);
             __builtin_amdgcn_sched_barrier(0);
         };
 
-        TileRef cur = tile_at(b0);
-        bool bad = cur.bad;
-        issue_k(cur);
-        issue_v(cur);
+        bool bad = false;
+#pragma unroll
+        for (int slot = 0; slot < PF; ++slot) {
+            const TileRef tr = tile_at(b0 + slot);
+            bad |= tr.bad;
+            issue_k(slot, tr);
+            issue_v(slot, tr);
+        }
         float m_run = -INFINITY, l_run = 0.f;
         f32x4_t o[NV];
 #pragma unroll
         for (int j = 0; j < NV; ++j) o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        // Every prefix block is full: no position is masked.
-        for (int b = b0; b < b1; ++b) {
-            const TileRef nxt = tile_at(b + 1);
-            bad |= nxt.bad;
-            f32x4_t sc = TM::qk(kr, q);
-            settle(sc);
-            issue_k(nxt);
-            float x[4];
+        // Every prefix block is full: no position is masked. A pass covers PF
+        // tiles; slots past the chunk's last tile hold zeros (a buffer load
+        // of size 0) and their scores are set to -inf.
+        for (int b = b0; b < b1; b += PF) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) x[j] = sc[j] * qk_scale;
-            const float xm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-            if (__any(xm > m_run + kLazyRescale)) {
-                float tm = fmaxf(xm, lane_fetch(x16, xm));
-                tm = fmaxf(tm, lane_fetch(x32, tm));
-                const float mn = fmaxf(m_run, tm);
-                const float cf = __builtin_amdgcn_exp2f(m_run - mn);
-                l_run *= cf;
+            for (int slot = 0; slot < PF; ++slot) {
+                const bool live = b + slot < b1;
+                const TileRef nxt = tile_at(b + slot + PF);
+                bad |= nxt.bad;
+                f32x4_t sc = TM::qk(kr[slot], q);
+                settle(sc);
+                issue_k(slot, nxt);
+                float x[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float cr = lane_fetch(head_lane[r], cf);
+                for (int j = 0; j < 4; ++j) x[j] = live ? sc[j] * qk_scale : -INFINITY;
+                const float xm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+                if (__any(xm > m_run + kLazyRescale)) {
+                    float tm = fmaxf(xm, lane_fetch(x16, xm));
+                    tm = fmaxf(tm, lane_fetch(x32, tm));
+                    const float mn = fmaxf(m_run, tm);
+                    const float cf = __builtin_amdgcn_exp2f(m_run - mn);
+                    l_run *= cf;
 #pragma unroll
-                    for (int j = 0; j < NV; ++j) o[j][r] *= cr;
+                    for (int r = 0; r < 4; ++r) {
+                        const float cr = lane_fetch(head_lane[r], cf);
+#pragma unroll
+                        for (int j = 0; j < NV; ++j) o[j][r] *= cr;
+                    }
+                    m_run = mn;
                 }
-                m_run = mn;
+                float pr[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) pr[j] = __builtin_amdgcn_exp2f(x[j] - m_run);
+                l_run += TM::pv(pr, vr[slot], o);
+#pragma unroll
+                for (int j = 0; j < NV; ++j) settle(o[j]);
+                issue_v(slot, nxt);
             }
-            float pr[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) pr[j] = __builtin_amdgcn_exp2f(x[j] - m_run);
-            l_run += TM::pv(pr, vr, o);
-#pragma unroll
-            for (int j = 0; j < NV; ++j) settle(o[j]);
-            issue_v(nxt);
         }
         float lt = l_run + lane_fetch(x16, l_run);
         lt += lane_fetch(x32, lt);  // weight sum of row t over the chunk
