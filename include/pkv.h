@@ -278,6 +278,19 @@ int pkv_paged_attention_decode_shared_prefix(
     const int32_t *group_starts, const int32_t *group_prefix_blocks, float scale,
     int32_t num_workers, void *workspace, size_t workspace_bytes, void *out, hipStream_t stream);
 
+/* Copy whole physical blocks, every KV head of K and V:
+ *     block pairs[i][1] <- block pairs[i][0],   i < num_pairs.
+ * The copy-on-write step ([ttlab] section 4): before a request appends into a
+ * block it shares with others, the block is copied and the request's table
+ * points at the copy. The block manager (pkv_blocks.h) emits the pairs.
+ *  pairs  int32 [num_pairs][2] (device); a pair with an id outside
+ *         [0, num_blocks) is skipped. A destination that is also a source, or
+ *         two pairs with one destination, in one call race.
+ * Errors: INVALID_ARG (null pointer with num_pairs > 0, negative count,
+ * misaligned cache, bad desc), UNSUPPORTED, HIP. */
+int pkv_copy_blocks(void *k_cache, void *v_cache, const pkv_cache_desc *cache,
+                    const int32_t *pairs, int32_t num_pairs, hipStream_t stream);
+
 /* Gather through the block tables (the same device addressing code as the
  * decode kernel), for checking indexing byte for byte:
  *     k_out[s][g][t][:] = K row of position t of sequence s, KV head g

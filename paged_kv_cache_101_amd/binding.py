@@ -34,7 +34,12 @@ _TORCH_CODES = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: 
 EXPORTS = ("pkv_status_string", "pkv_kv_bytes_per_token", "pkv_cache_tensor_bytes",
            "pkv_kv_append", "pkv_decode_workspace_bytes", "pkv_paged_attention_decode",
            "pkv_shared_prefix_workspace_bytes", "pkv_paged_attention_decode_shared_prefix",
-           "pkv_debug_gather")
+           "pkv_copy_blocks", "pkv_debug_gather",
+           # host block manager (pkv_blocks.h; bound in blocks.py)
+           "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_num_free_blocks", "pkv_bm_add_request",
+           "pkv_bm_can_append", "pkv_bm_append", "pkv_bm_fork", "pkv_bm_free_request",
+           "pkv_bm_num_tokens", "pkv_bm_num_blocks", "pkv_bm_ref_count", "pkv_bm_block_tables",
+           "pkv_bm_prefix_groups", "pkv_bm_prefix_cache_stats")
 
 
 class PkvError(RuntimeError):
@@ -82,6 +87,8 @@ def lib():
         L.pkv_paged_attention_decode_shared_prefix.argtypes = [
             vp, i32, i32, i32, vp, vp, descp, vp, i32, vp, i32, vp, vp, f32, i32, vp, sz, vp, vp]
         L.pkv_paged_attention_decode_shared_prefix.restype = ctypes.c_int
+        L.pkv_copy_blocks.argtypes = [vp, vp, descp, vp, i32, vp]
+        L.pkv_copy_blocks.restype = ctypes.c_int
         L.pkv_debug_gather.argtypes = [vp, vp, descp, vp, i32, vp, i32, i32, vp, vp, vp]
         L.pkv_debug_gather.restype = ctypes.c_int
         _lib = L
@@ -256,6 +263,18 @@ def pkv_paged_attention_decode_shared_prefix(
         _ptr(group_prefix_blocks), float(scale), num_workers, _ptr(workspace), ws_bytes,
         _ptr(out), _stream(stream))
     _check("pkv_paged_attention_decode_shared_prefix", rc)
+
+
+def pkv_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, desc: pkv_cache_desc,
+                    pairs: torch.Tensor, stream=None) -> None:
+    """pairs: int32 [n][2] (device) of (source block, destination block)."""
+    _need(pairs.dtype == torch.int32 and pairs.dim() == 2 and pairs.shape[1] == 2,
+          "pairs must be int32 [n][2]")
+    for t in (k_cache, v_cache, pairs):
+        _need(t.is_contiguous() and t.is_cuda, "all tensors must be contiguous device tensors")
+    rc = lib().pkv_copy_blocks(_ptr(k_cache), _ptr(v_cache), ctypes.byref(desc), _ptr(pairs),
+                               pairs.shape[0], _stream(stream))
+    _check("pkv_copy_blocks", rc)
 
 
 def pkv_debug_gather(k_cache: torch.Tensor, v_cache: torch.Tensor, desc: pkv_cache_desc,

@@ -19,6 +19,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["pkv_api.hip", "kv_append.hip", "paged_decode.hip", "shared_prefix.hip"]
+HOST_SOURCES = ["block_manager.cpp"]  # plain host C++ (g++)
+CXX = os.environ.get("CXX", "g++")
+HOST_CFLAGS = ["-O2", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", f"-I{INCLUDE}"]
 
 CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-fvisibility=hidden",
@@ -45,10 +48,25 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
+def _compile_host(src: str, verbose: bool) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [CXX, *HOST_CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"{CXX} failed for {src}:\n" + r.stdout + r.stderr)
+    if (r.stdout + r.stderr).strip() and verbose:
+        print(r.stdout + r.stderr)
+    return obj
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    with cf.ThreadPoolExecutor(max_workers=len(SOURCES) + len(HOST_SOURCES)) as ex:
+        jobs = [ex.submit(_compile, s, verbose) for s in SOURCES]
+        jobs += [ex.submit(_compile_host, s, verbose) for s in HOST_SOURCES]
+        objs = [j.result() for j in jobs]
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     if verbose:

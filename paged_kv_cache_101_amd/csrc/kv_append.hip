@@ -221,6 +221,45 @@ __global__ __launch_bounds__(256) void gather_kernel(
     }
 }
 
+// ---- whole-block copies (copy-on-write) ---------------------------------------
+//
+// (ttlab page, section 4: a block shared by several requests is copied before
+// one of them writes into it.) A physical block's KV heads are contiguous in
+// the pool -- (blk * H + g) tiles -- so a block is one run of H * 16 * D
+// elements in each cache, copied 16 bytes per thread, the same bytes in the
+// same in-tile order.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* __restrict__ k_cache,
+                                                          uint8_t* __restrict__ v_cache,
+                                                          const int32_t* __restrict__ pairs,
+                                                          int num_pairs, int num_blocks,
+                                                          int64_t block_bytes) {
+    const int64_t chunks = block_bytes / 16;  // 16-byte pieces of one block
+    const int64_t total = (int64_t)num_pairs * chunks;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t pr = idx / chunks, c = idx % chunks;
+        const int src = pairs[2 * pr], dst = pairs[2 * pr + 1];
+        if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) continue;
+        const int64_t s = (int64_t)src * block_bytes + c * 16, d = (int64_t)dst * block_bytes + c * 16;
+        *reinterpret_cast<uint4*>(k_cache + d) = *reinterpret_cast<const uint4*>(k_cache + s);
+        *reinterpret_cast<uint4*>(v_cache + d) = *reinterpret_cast<const uint4*>(v_cache + s);
+    }
+}
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, int elem_bytes, int num_blocks,
+                              int num_kv_heads, int head_dim, const int32_t* pairs,
+                              int num_pairs, hipStream_t stream) {
+    if (num_pairs == 0) return hipSuccess;
+    const int64_t block_bytes = (int64_t)num_kv_heads * kBlock * head_dim * elem_bytes;
+    const int64_t total = (int64_t)num_pairs * (block_bytes / 16);
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache), pairs,
+                       num_pairs, num_blocks, block_bytes);
+    return hipGetLastError();
+}
+
 hipError_t launch_gather(const void* k_cache, const void* v_cache, int elem_bytes,
                          int num_blocks, int num_kv_heads, int head_dim,
                          const int32_t* block_tables, int max_blocks_per_seq,

@@ -234,6 +234,20 @@ PKV_EXPORT int pkv_paged_attention_decode_shared_prefix(
     return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+PKV_EXPORT int pkv_copy_blocks(void* k_cache, void* v_cache, const pkv_cache_desc* cache,
+                               const int32_t* pairs, int32_t num_pairs, hipStream_t stream) {
+    int rc = check_cache(cache);
+    if (rc != PKV_OK) return rc;
+    if (num_pairs < 0 || k_cache == nullptr || v_cache == nullptr ||
+        (num_pairs > 0 && pairs == nullptr))
+        return PKV_ERR_INVALID_ARG;
+    if (!aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_INVALID_ARG;
+    hipError_t err = pkv::launch_copy_blocks(k_cache, v_cache, elem_bytes(cache->dtype),
+                                             cache->num_blocks, cache->num_kv_heads,
+                                             cache->head_dim, pairs, num_pairs, stream);
+    return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 PKV_EXPORT int pkv_debug_gather(const void* k_cache, const void* v_cache,
                                 const pkv_cache_desc* cache, const int32_t* block_tables,
                                 int32_t max_blocks_per_seq, const int32_t* context_lens,

@@ -142,6 +142,10 @@ hipError_t launch_paged_decode(const DecodeArgs& a);
 // set), then the prefix pass that merges and writes out.
 hipError_t launch_shared_prefix(const DecodeArgs& a);
 
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, int elem_bytes, int num_blocks,
+                              int num_kv_heads, int head_dim, const int32_t* pairs,
+                              int num_pairs, hipStream_t stream);
+
 hipError_t launch_gather(const void* k_cache, const void* v_cache, int elem_bytes,
                          int num_blocks, int num_kv_heads, int head_dim,
                          const int32_t* block_tables, int max_blocks_per_seq,

@@ -18,8 +18,12 @@ FAKE = 0x10000  # an aligned non-null address; never dereferenced by these calls
 
 
 def declared_functions():
-    text = open(os.path.join(ROOT, "include", "pkv.h")).read()
-    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", h)).read()
+            names |= set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():
@@ -180,6 +184,18 @@ def _shared(**kw):
 ])
 def test_shared_prefix_rejects_before_any_hip_call(kw, status):
     assert _shared(**kw) == status
+
+
+def test_copy_blocks_rejects_bad_args():
+    L = B.lib()
+    d = B.cache_desc(16, 2, 128, "f16")
+    assert L.pkv_copy_blocks(FAKE, FAKE, ctypes.byref(d), None, 3, None) == B.PKV_ERR_INVALID_ARG
+    assert L.pkv_copy_blocks(FAKE, FAKE, ctypes.byref(d), FAKE, -1, None) == B.PKV_ERR_INVALID_ARG
+    assert L.pkv_copy_blocks(None, FAKE, ctypes.byref(d), FAKE, 1, None) == B.PKV_ERR_INVALID_ARG
+    assert L.pkv_copy_blocks(FAKE + 8, FAKE, ctypes.byref(d), FAKE, 1, None) == B.PKV_ERR_INVALID_ARG
+    bad = B.cache_desc(16, 2, 96, "f16")
+    assert L.pkv_copy_blocks(FAKE, FAKE, ctypes.byref(bad), FAKE, 1, None) == B.PKV_ERR_UNSUPPORTED
+    assert L.pkv_copy_blocks(FAKE, FAKE, ctypes.byref(d), None, 0, None) == B.PKV_OK  # nothing to do
 
 
 def test_gather_rejects_bad_args():
