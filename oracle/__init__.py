@@ -59,6 +59,9 @@ def lib():
                                                 c_dbl, c_i64, c_i64, c_i64, vp, c_i64, vp, c_dbl,
                                                 c_i64, vp, vp, vp, vp]
         L.oracle_paged_decode_split.restype = c_int
+        L.oracle_paged_prefill.argtypes = [vp, c_int, c_i64, c_i64, vp, vp, vp, c_int, c_dbl,
+                                           c_dbl, c_i64, c_i64, c_i64, vp, c_i64, vp, c_dbl, vp]
+        L.oracle_paged_prefill.restype = c_int
         _lib = L
     return _lib
 
@@ -177,6 +180,29 @@ def paged_decode(q, k_cache, v_cache, block_tables, context_lens, scale, k_scale
                                    _ptr(bt), bt.shape[1], _ptr(cl), float(scale), _ptr(out))
     if rc != 0:
         raise ValueError("oracle_paged_decode: invalid arguments")
+    return out
+
+
+def paged_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+                  k_scale=1.0, v_scale=1.0):
+    """Paged chunked-prefill attention in double precision (see
+    pkv_oracle.c): q is [T][H_q][d] with sequence s owning rows
+    [query_start[s], query_start[s + 1]); returns out [T][H_q][d] float64."""
+    T, Hq, d = q.shape
+    num_blocks, H, blk, d2 = k_cache.shape
+    assert blk == BLOCK and d2 == d and v_cache.shape == k_cache.shape
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    qs = np.ascontiguousarray(query_start, dtype=np.int32)
+    S = cl.shape[0]
+    assert qs.shape == (S + 1,) and qs[-1] == T
+    out = np.empty((T, Hq, d), dtype=np.float64)
+    rc = lib().oracle_paged_prefill(_ptr(q), _dtype_code(q), S, Hq, _ptr(qs), _ptr(k_cache),
+                                    _ptr(v_cache), _dtype_code(k_cache), k_scale, v_scale,
+                                    num_blocks, H, d, _ptr(bt), bt.shape[1], _ptr(cl),
+                                    float(scale), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_paged_prefill: invalid arguments")
     return out
 
 

@@ -392,6 +392,61 @@ int oracle_paged_decode(const void *q, int q_dtype, int64_t num_seqs, int64_t nu
     return OR_OK;
 }
 
+/* Paged chunked-prefill attention, the plain definition. A prompt is fed in
+ * chunks within a per-step token budget (ttlab section 6, chunked prefill);
+ * the tokens of a chunk attend causally to every earlier token of their
+ * sequence and to each other, all read from the paged cache. Sequence s has
+ * q_len = query_start[s + 1] - query_start[s] query tokens, the last q_len of
+ * its n = context_lens[s] tokens (their K/V already appended). Query token i
+ * of s sits at position p = n - q_len + i; for query head h (KV head
+ * g = h / G):
+ *   out[query_start[s] + i][h] = softmax over t in [0, p] of scale * q . K_t,
+ *                                applied to V_t.
+ * q and out are [query_start[S]][H_q][d] (out in double). Invalid
+ * arguments (q_len < 0 or > n, query_start[0] != 0, out-of-range block ids)
+ * return OR_BAD. Threads split the (query row, head) pairs. */
+int oracle_paged_prefill(const void *q, int q_dtype, int64_t num_seqs, int64_t num_q_heads,
+                         const int32_t *query_start, const void *k_cache, const void *v_cache,
+                         int kv_dtype, double k_scale, double v_scale, int64_t num_blocks,
+                         int64_t num_kv_heads, int64_t head_dim, const int32_t *block_tables,
+                         int64_t max_blocks_per_seq, const int32_t *context_lens, double scale,
+                         double *out)
+{
+    if (elem_size(q_dtype) == 0 || elem_size(kv_dtype) == 0)
+        return OR_BAD;
+    if (check_decode_args(num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_tables,
+                          max_blocks_per_seq, context_lens) != OR_OK)
+        return OR_BAD;
+    if (num_seqs > 0 && query_start[0] != 0)
+        return OR_BAD;
+    for (int64_t s = 0; s < num_seqs; ++s) {
+        int64_t q_len = (int64_t)query_start[s + 1] - query_start[s];
+        if (q_len < 0 || q_len > context_lens[s])
+            return OR_BAD;
+    }
+    int64_t group = num_q_heads / num_kv_heads;
+    int64_t total = num_seqs > 0 ? query_start[num_seqs] : 0;
+    int64_t pairs = total * num_q_heads;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t pr = 0; pr < pairs; ++pr) {
+        int64_t row = pr / num_q_heads; /* query token row of q */
+        int64_t h = pr % num_q_heads;
+        int64_t s = 0;
+        while (query_start[s + 1] <= row)
+            ++s;
+        int64_t q_len = (int64_t)query_start[s + 1] - query_start[s];
+        int64_t pos = context_lens[s] - q_len + (row - query_start[s]);
+        double *o = out + pr * head_dim;
+        double m, l;
+        attend_range(q, q_dtype, pr, k_cache, v_cache, kv_dtype, k_scale, v_scale, num_kv_heads,
+                     head_dim, h / group, block_tables + s * max_blocks_per_seq, 0, pos + 1,
+                     scale, &m, &l, o);
+        for (int64_t j = 0; j < head_dim; ++j)
+            o[j] /= l;
+    }
+    return OR_OK;
+}
+
 /* Split-KV form of the same result, used to check the cross-partition
  * log-sum-exp algebra. Partition j covers positions [j*P, min((j+1)*P, n)).
  * For every non-empty partition it records m_j (max score), l_j (sum of
