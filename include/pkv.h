@@ -278,6 +278,38 @@ int pkv_paged_attention_decode_shared_prefix(
     const int32_t *group_starts, const int32_t *group_prefix_blocks, float scale,
     int32_t num_workers, void *workspace, size_t workspace_bytes, void *out, hipStream_t stream);
 
+/* Paged chunked-prefill attention: each sequence brings a chunk of new query
+ * tokens that attend causally to its cached tokens, read through its block
+ * table ([ttlab] section 6: a prompt longer than the per-step token budget is
+ * processed in chunks; section 4: the paged cache).
+ *
+ * Sequence s owns query rows [query_start[s], query_start[s + 1]) of q: its
+ * q_len newest tokens, whose K/V are already appended, so that with
+ * n = context_lens[s] token i of the chunk sits at position p = n - q_len + i.
+ * For query head h (KV head g = h / G):
+ *     out[query_start[s] + i][h] = sum_{t <= p} exp(x_t - max) V_t / sum_{t <= p} exp(x_t - max),
+ *     x_t = scale * (q[query_start[s] + i][h] . K_t)
+ * (fp8 elements read as code * k_scale / code * v_scale). One query token per
+ * sequence is decode. Arithmetic is float32 on the matrix cores; the result
+ * is rounded to nearest-even into q_dtype.
+ *
+ *  q, out        [num_tokens][num_q_heads][head_dim] in q_dtype (device)
+ *  query_start   int32 [num_seqs + 1] (device), non-decreasing from 0 to
+ *                num_tokens
+ *  block_tables, context_lens, scale, q_dtype / cache pairs: as for decode
+ * A sequence whose chunk is not inside [0, num_tokens], is longer than its
+ * context, or whose context exceeds max_blocks_per_seq * 16 is skipped (its
+ * rows are not written); one whose needed block ids fall outside the pool gets
+ * NaN rows. No workspace. Errors: INVALID_ARG, UNSUPPORTED (as decode, or a
+ * batch too large for one launch), HIP. */
+int pkv_paged_attention_prefill(const void *q, int32_t q_dtype, int32_t num_seqs,
+                                int32_t num_tokens, int32_t num_q_heads,
+                                const int32_t *query_start, const void *k_cache,
+                                const void *v_cache, const pkv_cache_desc *cache,
+                                const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                const int32_t *context_lens, float scale, void *out,
+                                hipStream_t stream);
+
 /* Copy whole physical blocks, every KV head of K and V:
  *     block pairs[i][1] <- block pairs[i][0],   i < num_pairs.
  * The copy-on-write step ([ttlab] section 4): before a request appends into a

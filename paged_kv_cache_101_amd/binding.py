@@ -34,7 +34,7 @@ _TORCH_CODES = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: 
 EXPORTS = ("pkv_status_string", "pkv_kv_bytes_per_token", "pkv_cache_tensor_bytes",
            "pkv_kv_append", "pkv_decode_workspace_bytes", "pkv_paged_attention_decode",
            "pkv_shared_prefix_workspace_bytes", "pkv_paged_attention_decode_shared_prefix",
-           "pkv_copy_blocks", "pkv_debug_gather",
+           "pkv_paged_attention_prefill", "pkv_copy_blocks", "pkv_debug_gather",
            # host block manager (pkv_blocks.h; bound in blocks.py)
            "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_num_free_blocks", "pkv_bm_add_request",
            "pkv_bm_can_append", "pkv_bm_append", "pkv_bm_fork", "pkv_bm_free_request",
@@ -87,6 +87,9 @@ def lib():
         L.pkv_paged_attention_decode_shared_prefix.argtypes = [
             vp, i32, i32, i32, vp, vp, descp, vp, i32, vp, i32, vp, vp, f32, i32, vp, sz, vp, vp]
         L.pkv_paged_attention_decode_shared_prefix.restype = ctypes.c_int
+        L.pkv_paged_attention_prefill.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, descp, vp,
+                                                  i32, vp, f32, vp, vp]
+        L.pkv_paged_attention_prefill.restype = ctypes.c_int
         L.pkv_copy_blocks.argtypes = [vp, vp, descp, vp, i32, vp]
         L.pkv_copy_blocks.restype = ctypes.c_int
         L.pkv_debug_gather.argtypes = [vp, vp, descp, vp, i32, vp, i32, i32, vp, vp, vp]
@@ -263,6 +266,29 @@ def pkv_paged_attention_decode_shared_prefix(
         _ptr(group_prefix_blocks), float(scale), num_workers, _ptr(workspace), ws_bytes,
         _ptr(out), _stream(stream))
     _check("pkv_paged_attention_decode_shared_prefix", rc)
+
+
+def pkv_paged_attention_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                desc: pkv_cache_desc, block_tables: torch.Tensor,
+                                context_lens: torch.Tensor, query_start: torch.Tensor,
+                                scale: float, out: torch.Tensor, stream=None) -> None:
+    """q, out: [T][H_q][d]; query_start: int32 [S + 1] (sequence s owns rows
+    [query_start[s], query_start[s + 1])); block_tables, context_lens as for decode."""
+    T, Hq, d = q.shape
+    S = context_lens.numel()
+    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    _need(query_start.dtype == torch.int32 and query_start.numel() == S + 1,
+          "query_start must be int32 [S + 1]")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+          and block_tables.shape[0] == S, "block_tables must be int32 [S][max_blocks]")
+    _need(context_lens.dtype == torch.int32, "context_lens must be int32 [S]")
+    for t in (q, k_cache, v_cache, block_tables, context_lens, query_start, out):
+        _need(t.is_contiguous() and t.is_cuda, "all tensors must be contiguous device tensors")
+    rc = lib().pkv_paged_attention_prefill(
+        _ptr(q), _dtype_of(q), S, T, Hq, _ptr(query_start), _ptr(k_cache), _ptr(v_cache),
+        ctypes.byref(desc), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+        float(scale), _ptr(out), _stream(stream))
+    _check("pkv_paged_attention_prefill", rc)
 
 
 def pkv_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, desc: pkv_cache_desc,

@@ -101,13 +101,14 @@ PKV_EXPORT size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_hea
 
 namespace {
 
-// Checks shared by the two decode entry points (all but the workspace size),
-// filling the launch arguments.
+// Checks shared by the attention entry points (all but the workspace size),
+// filling the decode launch arguments. with_workspace: the call takes one.
 int decode_args(pkv::DecodeArgs& a, const void* q, int32_t q_dtype, int32_t num_seqs,
                 int32_t num_q_heads, const void* k_cache, const void* v_cache,
                 const pkv_cache_desc* cache, const int32_t* block_tables,
                 int32_t max_blocks_per_seq, const int32_t* context_lens, float scale,
-                int32_t num_workers, void* workspace, void* out, hipStream_t stream) {
+                int32_t num_workers, bool with_workspace, void* workspace, void* out,
+                hipStream_t stream) {
     int rc = check_cache(cache);
     if (rc != PKV_OK) return rc;
     if (num_seqs <= 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0)
@@ -130,7 +131,8 @@ int decode_args(pkv::DecodeArgs& a, const void* q, int32_t q_dtype, int32_t num_
     if (!(scale == scale)) return PKV_ERR_INVALID_ARG;
     if (num_workers < 0) return PKV_ERR_INVALID_ARG;
     if (num_workers > pkv::kMaxWorkers) return PKV_ERR_UNSUPPORTED;
-    if (workspace == nullptr || ((uintptr_t)workspace & 255u) != 0) return PKV_ERR_WORKSPACE;
+    if (with_workspace && (workspace == nullptr || ((uintptr_t)workspace & 255u) != 0))
+        return PKV_ERR_WORKSPACE;
 
     a = pkv::DecodeArgs{};
     a.q = q;
@@ -171,7 +173,7 @@ PKV_EXPORT int pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_
     pkv::DecodeArgs a;
     const int rc = decode_args(a, q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, cache,
                                block_tables, max_blocks_per_seq, context_lens, scale, num_workers,
-                               workspace, out, stream);
+                               true, workspace, out, stream);
     if (rc != PKV_OK) return rc;
     if (workspace_bytes < pkv_decode_workspace_bytes(num_seqs, num_q_heads, cache->num_kv_heads,
                                                      cache->head_dim, num_workers))
@@ -203,7 +205,7 @@ PKV_EXPORT int pkv_paged_attention_decode_shared_prefix(
     pkv::DecodeArgs a;
     const int rc = decode_args(a, q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, cache,
                                block_tables, max_blocks_per_seq, context_lens, scale, num_workers,
-                               workspace, out, stream);
+                               true, workspace, out, stream);
     if (rc != PKV_OK) return rc;
     if (num_groups < 0 || num_groups > num_seqs) return PKV_ERR_INVALID_ARG;
     if (num_groups > 0 && (group_starts == nullptr || group_prefix_blocks == nullptr))
@@ -231,6 +233,54 @@ PKV_EXPORT int pkv_paged_attention_decode_shared_prefix(
         a.prefix_counters = reinterpret_cast<int*>(ws + dctr - l.prefix_counter_bytes);
         err = pkv::launch_shared_prefix(a);
     }
+    return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+PKV_EXPORT int pkv_paged_attention_prefill(const void* q, int32_t q_dtype, int32_t num_seqs,
+                                           int32_t num_tokens, int32_t num_q_heads,
+                                           const int32_t* query_start, const void* k_cache,
+                                           const void* v_cache, const pkv_cache_desc* cache,
+                                           const int32_t* block_tables,
+                                           int32_t max_blocks_per_seq,
+                                           const int32_t* context_lens, float scale, void* out,
+                                           hipStream_t stream) {
+    if (num_tokens < 0 || query_start == nullptr) return PKV_ERR_INVALID_ARG;
+    if (num_tokens == 0) {  // nothing to compute: q and out may be NULL
+        const int rc0 = check_cache(cache);
+        if (rc0 != PKV_OK) return rc0;
+        return num_seqs > 0 && num_q_heads > 0 ? PKV_OK : PKV_ERR_INVALID_ARG;
+    }
+    // the same checks as decode (no workspace)
+    pkv::DecodeArgs d;
+    const int rc = decode_args(d, q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, cache,
+                               block_tables, max_blocks_per_seq, context_lens, scale, 0,
+                               false, nullptr, out, stream);
+    if (rc != PKV_OK) return rc;
+    if (pkv::prefill_task_bound(num_seqs, num_tokens, d.group, cache->num_kv_heads) > INT32_MAX)
+        return PKV_ERR_UNSUPPORTED;
+    pkv::PrefillArgs a{};
+    a.q = q;
+    a.q_dtype = q_dtype;
+    a.kv_dtype = cache->dtype;
+    a.num_seqs = num_seqs;
+    a.num_tokens = num_tokens;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = cache->num_kv_heads;
+    a.group = d.group;
+    a.head_dim = cache->head_dim;
+    a.num_blocks = cache->num_blocks;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.query_start = query_start;
+    a.block_tables = block_tables;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.context_lens = context_lens;
+    a.scale = scale;
+    a.k_scale = cache->k_scale;
+    a.v_scale = cache->v_scale;
+    a.out = out;
+    a.stream = stream;
+    hipError_t err = pkv::launch_paged_prefill(a);
     return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

@@ -126,6 +126,34 @@ struct DecodeArgs {
     float* prefix_slots = nullptr;          // prefix pass: partial slots
 };
 
+// Paged chunked-prefill attention (paged_prefill.hip).
+struct PrefillArgs {
+    const void* q;
+    int q_dtype;
+    int kv_dtype;
+    int num_seqs;
+    int num_tokens;  // rows of q and out
+    int num_q_heads;
+    int num_kv_heads;
+    int group;
+    int head_dim;
+    int num_blocks;
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* query_start;  // [S + 1] (device)
+    const int32_t* block_tables;
+    int max_blocks_per_seq;
+    const int32_t* context_lens;
+    float scale;
+    float k_scale;
+    float v_scale;
+    void* out;
+    hipStream_t stream;
+};
+hipError_t launch_paged_prefill(const PrefillArgs& a);
+// Workgroups one prefill launch starts at most (its grid).
+int64_t prefill_task_bound(int num_seqs, int num_tokens, int group, int num_kv_heads);
+
 hipError_t launch_kv_append(const void* k, const void* v, int elem_bytes,
                             const int64_t* slot_mapping, int num_tokens, void* k_cache,
                             void* v_cache, int num_blocks, int num_kv_heads, int head_dim,
