@@ -36,6 +36,15 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "fp8": 2500.0, "f32": 157.3}
+# (fp8 KV is widened to the 16-bit query type before the matrix cores: its
+# products run at the 16-bit rate; float32 caches use the float32 MFMA)
+
+# Chunked-prefill step: one 2048-token chunk (the pages' deployment token
+# budget) for each of four sequences at different stages of their prompts,
+# in the 40-layer GQA head shape.
+PREFILL_CONTEXTS = [2048, 4096, 6144, 8192]
+PREFILL_CHUNK = 2048
 
 
 def parse():
@@ -44,7 +53,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gqa40",
-                    choices=["gqa40", "qwen", "prefix", "prefix_shared", "fp8", "tiny"])
+                    choices=["gqa40", "qwen", "prefix", "prefix_shared", "fp8", "tiny", "prefill"])
     ap.add_argument("--workers", type=int, default=0, help="worker waves (0 = fill the device)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -161,6 +170,97 @@ def cpu_baseline(layer, target_s: float):
     }
 
 
+def prefill_flops(contexts, chunk, num_q_heads, head_dim) -> int:
+    """4 * d * H_q flops per (query token, visible key): QK and P.V, a
+    multiply and an add each."""
+    total = 0
+    for n in contexts:
+        base = n - chunk
+        total += sum(base + i + 1 for i in range(chunk))
+    return 4 * head_dim * num_q_heads * total
+
+
+def bench_prefill(args):
+    import numpy as np
+    import torch
+    from paged_kv_cache_101_amd import binding as B
+    from paged_kv_cache_101_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    Hq, H, d, dt = 32, 8, 128, "f16"
+    b = W.make_batch("prefill-step", 6, PREFILL_CONTEXTS, Hq, H, d, dt, dt, device=dev)
+    desc = B.desc_for(b.k_cache, dt)
+    kc, vc = B.fill_cache(b.k_cache, b.v_cache, desc)
+    S = len(PREFILL_CONTEXTS)
+    T = S * PREFILL_CHUNK
+    g = torch.Generator(device=dev)
+    g.manual_seed(66)
+    q = torch.randn((T, Hq, d), generator=g, device=dev).to(torch.float16)
+    qs = torch.arange(0, T + 1, PREFILL_CHUNK, dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        B.pkv_paged_attention_prefill(q, kc, vc, desc, b.block_tables, b.context_lens, qs,
+                                      b.scale, out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(c) for a, c in evs]
+    avg = statistics.fmean(ms)
+    flops = prefill_flops(PREFILL_CONTEXTS, PREFILL_CHUNK, Hq, d)
+    tflops = flops / (avg * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        # sample: the first k rows of the last chunk (the longest contexts)
+        kh, vh = W.to_numpy(b.k_cache), W.to_numpy(b.v_cache)
+        bt, cl = b.block_tables.cpu().numpy(), b.context_lens.cpu().numpy()
+        qh = W.to_numpy(q)
+        k = 1
+        while True:
+            rows = np.arange(T - PREFILL_CHUNK, T - PREFILL_CHUNK + k)
+            pos = cl[-1] - PREFILL_CHUNK + (rows - (T - PREFILL_CHUNK))
+            t0 = time.perf_counter()
+            oracle.paged_prefill(np.ascontiguousarray(qh[rows]), kh, vh,
+                                 np.ascontiguousarray(bt[[S - 1] * k]), (pos + 1).astype(np.int32),
+                                 np.arange(k + 1, dtype=np.int32), b.scale)
+            el = time.perf_counter() - t0
+            if el > args.cpu_seconds / 4 or k >= PREFILL_CHUNK:
+                break
+            k = min(PREFILL_CHUNK, k * 4)
+        sample_flops = 4 * d * Hq * int((pos + 1).sum())
+        cpu = {"value": round(sample_flops / el / 1e12, 6), "unit": "TFLOP/s",
+               "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": f"rows {int(rows[0])}..{int(rows[-1])} of the last chunk (context "
+                         f"{int(cl[-1])}), all {Hq} query heads, {el:.2f} s"}
+    line = {
+        "metric": "paged chunked-prefill attention: TFLOP/s (% of MFMA peak)",
+        "value": round(tflops, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(avg, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": dt, "data": "synthetic",
+        "config": {"workload": f"chunked prefill: {S} sequences x {PREFILL_CHUNK}-token chunks "
+                               f"at contexts {PREFILL_CONTEXTS}", "q_heads": Hq, "kv_heads": H,
+                   "head_dim": d, "kv_dtype": dt, "block_size": 16},
+        "flops_per_step": flops,
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
+                     "peak": MFMA_PEAK_TFLOPS[dt], "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_PEAK_TFLOPS[dt], 4), "traffic": None,
+                     "kernel": "paged_prefill_kernel (one launch per call)",
+                     "launch_avg_us": round(avg * 1e3, 2)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -176,6 +276,10 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.workload == "prefill":
+        B.lib()
+        bench_prefill(args)
         return
     B.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")

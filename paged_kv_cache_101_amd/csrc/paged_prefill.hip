@@ -9,14 +9,15 @@
 // Unlike decode this is a real contraction: for one (sequence, KV head) the
 // chunk's q_len * G query rows all meet the same K/V tiles. The kernel is
 // tiled for the matrix cores accordingly:
-//   * A workgroup of 4 waves owns 256 query rows of one (sequence, KV head),
-//     stacked token-major (row = token * G + head), 64 per wave as four
-//     16-row MFMA column sets.
-//   * The sequence's 16-token tiles stream through LDS, double-buffered: the
-//     workgroup loads tile j+1 from L2 (one 16-byte piece per thread for a
-//     16-bit d 128 tile) while computing tile j. Each wave reads a tile's K
-//     and V operands from LDS once and applies them to its 64 rows, so a tile
-//     costs one L2 read per 256 rows and one LDS read per 64 rows.
+//   * A workgroup of 8 waves owns 256 query rows of one (sequence, KV head),
+//     stacked token-major (row = token * G + head), 32 per wave as two 16-row
+//     MFMA column sets; two waves share each SIMD, so one wave's softmax
+//     overlaps the other's matrix work.
+//   * The sequence's 16-token tiles stream through a 4-stage LDS ring, three
+//     tiles ahead of the one computed, moved from L2 straight into LDS by
+//     direct loads (no registers). Each wave reads a tile's K and V operands
+//     from LDS once per step and applies them to its 32 rows: a tile costs one
+//     L2 read per 256 rows.
 //   * Per 16-row block the arithmetic is decode's (TileMath): S^T = K . Q^T and
 //     O += P . V on MFMA, online softmax in log2 units with a lazily moved
 //     maximum. Tiles wholly before a row block's first position need no mask;
@@ -24,7 +25,8 @@
 //     position are skipped.
 //   * Workgroup index -> (sequence, row tile, KV head) with the KV head fastest,
 //     so the workgroups of one head land on one XCD (workgroups are dealt to
-//     the 8 XCDs round-robin) and share its L2.
+//     the 8 XCDs round-robin) and share its L2; within a sequence the row
+//     tiles with the most keys start first.
 #include "pkv_internal.h"
 #include "pkv_tile.h"
 
@@ -32,11 +34,35 @@ namespace pkv {
 
 namespace {
 
-constexpr int kPrefillWaves = 4;                    // waves per workgroup
-constexpr int kRowBlocks = 4;                       // 16-row blocks per wave
-constexpr int kWaveRows = 16 * kRowBlocks;          // 64
+constexpr int kPrefillWaves = 8;                    // waves per workgroup
+constexpr int kRowBlocks = 2;                       // 16-row blocks per wave
+constexpr int kWaveRows = 16 * kRowBlocks;          // 32
 constexpr int kGroupRows = kPrefillWaves * kWaveRows;  // 256
 constexpr int kPrefillThreads = kPrefillWaves * kWave;
+constexpr int kRing = 3;  // LDS ring of two-tile steps: kRing - 1 steps in flight
+
+// s_waitcnt operand that waits for the vector-memory counter to reach n
+// (expcnt and lgkmcnt left at their maxima; gfx9 encoding, vmcnt split
+// over bits 3:0 and 15:14).
+constexpr int vmcnt_wait(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+// SZ bytes per lane from global memory straight into LDS: lane l's bytes land
+// at lds_base + l * SZ (lds_base is the same for the whole wave).
+template <int SZ>
+__device__ __forceinline__ void load_to_lds(const uint8_t* src, uint8_t* lds_base) {
+    static_assert(SZ == 16, "load size");
+    __builtin_amdgcn_global_load_lds((const void*)src,
+                                     (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
+// All waves of the workgroup reach this point. A compiler barrier on both
+// sides keeps memory accesses from moving across it; unlike __syncthreads()
+// it does not wait for this wave's outstanding loads.
+__device__ __forceinline__ void workgroup_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 struct PrefillParams {
     const uint8_t* q;
@@ -69,18 +95,16 @@ __device__ __forceinline__ int row_tiles(const PrefillParams& p, int s) {
 }  // namespace
 
 template <int KT, int QT, int D>
-__global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(1)))
+__global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void paged_prefill_kernel(PrefillParams p) {
     using TM = TileMath<KT, QT, D>;
     constexpr int NK = TM::NK, NV = TM::NV, NVL = TM::NVL, KW = TM::KW, VLW = TM::VLW;
     constexpr int KB = Elem<KT>::bytes;
     constexpr int QB = Elem<QT>::bytes;
     constexpr uint32_t kTileBytes = (uint32_t)kBlock * D * KB;
-    constexpr int kPieceDwords = kTileBytes / 4 / kPrefillThreads;  // per thread and cache
-    static_assert(kPieceDwords >= 1 && kTileBytes % (4 * kPrefillThreads) == 0, "tile split");
 
-    // two stages of (K tile, V tile)
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kTileBytes];
+    // kRing stages of two tiles' (K, V)
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kRing * 4 * kTileBytes];
 
     const int tid = threadIdx.x;
     const int lane = lane_id();
@@ -109,7 +133,7 @@ void paged_prefill_kernel(PrefillParams p) {
     }
     if (s < 0) return;  // the grid is an upper bound on the tasks
     const int g = local % H;
-    const int rt = local / H;
+    const int rt = row_tiles(p, s) - 1 - local / H;  // the longest row tiles first
     const int q0 = p.query_start[s];
     const int q_len = p.query_start[s + 1] - q0;
     const int n = p.context_lens[s];
@@ -145,37 +169,63 @@ void paged_prefill_kernel(PrefillParams p) {
         rb_last[rb] = r0 < nrows ? base_pos + r1 / G : -1;
     }
 
-    // ---- the tile stream through LDS ----
+    // ---- the tile stream: an LDS ring of two-tile steps, filled by direct loads ----
+    // A step is tiles 2 * sp (A) and 2 * sp + 1 (B); it goes to ring stage
+    // sp % kRing, kRing - 1 steps ahead of the one computed. A step is moved
+    // from L2 straight into LDS (no registers) in 1 KiB pieces, 16 bytes per
+    // lane: piece c (A's K, A's V, B's K, B's V, in that order) is carried by
+    // wave c % 8. A wave waits for its own loads of step sp (the counter counts
+    // its loads in issue order), then the barrier makes every wave's pieces
+    // visible; the stage refilled after that barrier was last read before it.
+    // A tile B past the last one reads the null block (it is masked out), so
+    // every step issues the same loads.
+    constexpr int kPieces = 2 * (int)kTileBytes / 1024;  // of one tile: its K, then its V
+    constexpr int kStepPieces = 2 * kPieces;
+    constexpr uint32_t kStepBytes = 4 * kTileBytes;
+    static_assert(kTileBytes % 1024 == 0 && kStepPieces <= 4 * kPrefillWaves, "piece split");
+    const int my_pieces = (kStepPieces - wv + kPrefillWaves - 1) / kPrefillWaves;  // 0 .. 4
+    const int steps = (tiles + 1) / 2;
     bool bad = false;
-    auto tile_ref = [&](int j, uint32_t& bytes) -> size_t {
-        bytes = 0;
-        if (j >= tiles) return 0;
-        const int id = uniform_read(p.block_tables, bt_row + j);
-        if (id < 0 || id >= p.num_blocks) {
-            bad = true;
-            return 0;
-        }
-        bytes = kTileBytes;
-        return tile_elem_offset(id, g, H, D) * KB;
-    };
-    uint32_t sk[kPieceDwords], sv[kPieceDwords];
-    const uint32_t piece = (uint32_t)tid * kPieceDwords * 4;
-    auto fetch = [&](int j) {
-        uint32_t bytes;
-        const size_t off = tile_ref(j, bytes);
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k_cache + off, bytes);
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_cache + off, bytes);
-        load_dwords<kPieceDwords, kLoadCached>(rk, piece, sk);
-        load_dwords<kPieceDwords, kLoadCached>(rv, piece, sv);
-    };
-    auto stage = [&](int buf) {
+    auto issue = [&](int sp) {
+        const uint32_t st = (uint32_t)(sp % kRing) * kStepBytes;
+        size_t off[2];
 #pragma unroll
-        for (int i = 0; i < kPieceDwords; ++i) {
-            reinterpret_cast<uint32_t*>(lds[buf][0] + piece)[i] = sk[i];
-            reinterpret_cast<uint32_t*>(lds[buf][1] + piece)[i] = sv[i];
+        for (int h2 = 0; h2 < 2; ++h2) {
+            const int j = 2 * sp + h2;
+            int id = 0;  // past the last tile: the null block, masked out
+            if (j < tiles) {
+                id = uniform_read(p.block_tables, bt_row + j);
+                if (id < 0 || id >= p.num_blocks) {
+                    bad = true;  // its rows become NaN; the null block is read instead
+                    id = 0;
+                }
+            }
+            off[h2] = tile_elem_offset(id, g, H, D) * KB;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = wv + i * kPrefillWaves;
+            if (c < kStepPieces) {
+                const int th = c / kPieces;  // 0: tile A, 1: tile B
+                const int cc = c % kPieces;
+                const bool is_v = cc >= kPieces / 2;
+                const uint32_t pc = (uint32_t)(is_v ? cc - kPieces / 2 : cc) * 1024;
+                load_to_lds<16>((is_v ? p.v_cache : p.k_cache) + off[th] + pc + (uint32_t)lane * 16,
+                                lds + st + (uint32_t)th * 2 * kTileBytes + (is_v ? kTileBytes : 0) + pc);
+            }
         }
     };
-
+    // wait until at most `later` steps' loads of this wave are in flight
+    auto wait_steps = [&](int later) {
+        static_assert(kRing == 3, "later is 0 or 1");
+        switch (later > 0 ? my_pieces : 0) {
+        case 0: __builtin_amdgcn_s_waitcnt(vmcnt_wait(0)); break;
+        case 1: __builtin_amdgcn_s_waitcnt(vmcnt_wait(1)); break;
+        case 2: __builtin_amdgcn_s_waitcnt(vmcnt_wait(2)); break;
+        case 3: __builtin_amdgcn_s_waitcnt(vmcnt_wait(3)); break;
+        default: __builtin_amdgcn_s_waitcnt(vmcnt_wait(4)); break;
+        }
+    };
     const uint32_t k_off = (uint32_t)((g4 * kBlock + t) * 8 * KB);
     const uint32_t v_off = (uint32_t)((t * 4 + g4) * 8 * KB);
     const int x16 = (lane ^ 16) << 2, x32 = (lane ^ 32) << 2;
@@ -194,75 +244,107 @@ void paged_prefill_kernel(PrefillParams p) {
         for (int j = 0; j < NV; ++j) o[rb][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    fetch(0);
-    stage(0);
-    __syncthreads();
-    for (int j = 0; j < tiles; ++j) {
-        const int buf = j & 1;
-        fetch(j + 1);  // in flight while tile j is computed
-        const int key0 = j * kBlock;
-        // the wave's row blocks that see any key of tile j
-        bool any = false;
+    auto read_k = [&](uint32_t base, uint32_t (&kr)[NK][KW]) {
+#pragma unroll
+        for (int i = 0; i < NK; ++i)
+#pragma unroll
+            for (int c = 0; c < KW; ++c)
+                kr[i][c] = reinterpret_cast<const uint32_t*>(lds + base + k_off + i * 4 * kBlock * 8 * KB)[c];
+    };
+    auto read_v = [&](uint32_t base, uint32_t (&vr)[NVL][VLW]) {
+#pragma unroll
+        for (int i = 0; i < NVL; ++i)
+#pragma unroll
+            for (int c = 0; c < VLW; ++c)
+                vr[i][c] = reinterpret_cast<const uint32_t*>(lds + base + v_off + i * 32 * kBlock * KB)[c];
+    };
+
+    for (int sp = 0; sp < kRing - 1 && sp < steps; ++sp) issue(sp);
+    for (int sp = 0; sp < steps; ++sp) {
+        const uint32_t st = (uint32_t)(sp % kRing) * kStepBytes;
+        wait_steps(min(kRing - 2, steps - 1 - sp));
+        workgroup_barrier();
+        if (sp + kRing - 1 < steps) issue(sp + kRing - 1);
+        const int key0 = 2 * sp * kBlock;  // first key of tile A; tile B starts at key0 + 16
+        const bool has_b = 2 * sp + 1 < tiles;
+        bool any = false;  // a row block of this wave sees a key of the step
 #pragma unroll
         for (int rb = 0; rb < kRowBlocks; ++rb) any |= rb_last[rb] >= key0;
-        if (any) {
-            uint32_t kr[NK][KW], vr[NVL][VLW];
+        if (!any) continue;
+        // scores of both tiles for every row block
+        f32x4_t sa[kRowBlocks], sb[kRowBlocks];
+        {
+            uint32_t kr[NK][KW];
+            read_k(st, kr);
 #pragma unroll
-            for (int i = 0; i < NK; ++i)
+            for (int rb = 0; rb < kRowBlocks; ++rb) sa[rb] = TM::qk(kr, q[rb]);
+            read_k(st + 2 * kTileBytes, kr);
 #pragma unroll
-                for (int c = 0; c < KW; ++c)
-                    kr[i][c] = reinterpret_cast<const uint32_t*>(
-                        lds[buf][0] + k_off + i * 4 * kBlock * 8 * KB)[c];
+            for (int rb = 0; rb < kRowBlocks; ++rb) sb[rb] = TM::qk(kr, q[rb]);
+        }
+        uint32_t va[NVL][VLW], vb[NVL][VLW];
+        read_v(st + kTileBytes, va);
+        read_v(st + 3 * kTileBytes, vb);
+        // Keys at or past n (the unused rows of the last block), and a tile B
+        // past the workgroup's last tile (which the causal limit, not n, can
+        // end), are seen by no row: their V elements are zeroed, so that
+        // whatever those rows hold cannot reach P . V (their scores are
+        // excluded by select below).
+        if (key0 + kBlock > n) TM::mask_v(va, n - key0 - 4 * g4);
+        if (!has_b) TM::mask_v(vb, 0);  // the null block stands in for a missing tile B
+        else if (key0 + 2 * kBlock > n) TM::mask_v(vb, n - key0 - kBlock - 4 * g4);
 #pragma unroll
-            for (int i = 0; i < NVL; ++i)
+        for (int rb = 0; rb < kRowBlocks; ++rb) {
+            if (rb_last[rb] < key0) continue;  // no row of the block sees this step
+            float xa[4], xb[4];
+            if (key0 + 2 * kBlock - 1 <= rb_first[rb]) {
 #pragma unroll
-                for (int c = 0; c < VLW; ++c)
-                    vr[i][c] = reinterpret_cast<const uint32_t*>(
-                        lds[buf][1] + v_off + i * 32 * kBlock * KB)[c];
-            // Keys at or past n (the unused rows of the last block) are seen by
-            // no row: their V elements are zeroed, so that whatever those rows
-            // hold cannot reach P . V (their scores are excluded by select).
-            if (key0 + kBlock > n) TM::mask_v(vr, n - key0 - 4 * g4);
-#pragma unroll
-            for (int rb = 0; rb < kRowBlocks; ++rb) {
-                if (rb_last[rb] < key0) continue;  // no row of the block sees tile j
-                const f32x4_t sc = TM::qk(kr, q[rb]);
-                float x[4];
-                if (key0 + kBlock - 1 <= rb_first[rb]) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) x[e] = sc[e] * qk_scale;
-                } else {
-                    // diagonal tile: key k of this lane is key0 + 4 * g4 + e
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        x[e] = key0 + 4 * g4 + e <= pos[rb] ? sc[e] * qk_scale : -INFINITY;
+                for (int e = 0; e < 4; ++e) {
+                    xa[e] = sa[rb][e] * qk_scale;
+                    xb[e] = sb[rb][e] * qk_scale;
                 }
-                const float xm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-                if (__any(xm > m_run[rb] + kLazyRescale)) {
-                    float tm = fmaxf(xm, lane_fetch(x16, xm));
-                    tm = fmaxf(tm, lane_fetch(x32, tm));
-                    const float mn = fmaxf(m_run[rb], tm);
-                    const float cf = __builtin_amdgcn_exp2f(m_run[rb] - mn);
-                    l_run[rb] *= cf;
+            } else {
+                // a diagonal step: key k of this lane is key0 + 4 * g4 + e (A)
+                // and key0 + 16 + 4 * g4 + e (B)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float cr = lane_fetch(head_lane[r], cf);
-#pragma unroll
-                        for (int e = 0; e < NV; ++e) o[rb][e][r] *= cr;
-                    }
-                    m_run[rb] = mn;
+                for (int e = 0; e < 4; ++e) {
+                    xa[e] = key0 + 4 * g4 + e <= pos[rb] ? sa[rb][e] * qk_scale : -INFINITY;
+                    xb[e] = has_b && key0 + kBlock + 4 * g4 + e <= pos[rb] ? sb[rb][e] * qk_scale
+                                                                           : -INFINITY;
                 }
-                float pr[4];
+            }
+            const float xm = fmaxf(fmaxf(fmaxf(xa[0], xa[1]), fmaxf(xa[2], xa[3])),
+                                   fmaxf(fmaxf(xb[0], xb[1]), fmaxf(xb[2], xb[3])));
+            if (__any(xm > m_run[rb] + kLazyRescale)) {
+                float tm = fmaxf(xm, lane_fetch(x16, xm));
+                tm = fmaxf(tm, lane_fetch(x32, tm));
+                const float mn = fmaxf(m_run[rb], tm);
+                const float cf = __builtin_amdgcn_exp2f(m_run[rb] - mn);
+                l_run[rb] *= cf;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(x[e] - m_run[rb]);
-                l_run[rb] += TM::pv(pr, vr, o[rb]);
+                for (int r = 0; r < 4; ++r) {
+                    const float cr = lane_fetch(head_lane[r], cf);
+#pragma unroll
+                    for (int e = 0; e < NV; ++e) o[rb][e][r] *= cr;
+                }
+                m_run[rb] = mn;
+            }
+            float pa[4], pb[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                pa[e] = __builtin_amdgcn_exp2f(xa[e] - m_run[rb]);
+                pb[e] = __builtin_amdgcn_exp2f(xb[e] - m_run[rb]);
+            }
+            if constexpr (TM::kF32) {
+                l_run[rb] += TM::pv(pa, va, o[rb]);
+                l_run[rb] += TM::pv(pb, vb, o[rb]);
+            } else {
+                l_run[rb] += TM::pv2(pa, pb, va, vb, o[rb]);
             }
         }
-        if (j + 1 < tiles) {
-            stage(buf ^ 1);  // the other buffer was last read before the previous barrier
-        }
-        __syncthreads();
     }
+
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));  // no load into LDS outlives the workgroup
 
     // ---- normalise and store the wave's rows ----
     const float nan = __builtin_nanf("");

@@ -215,6 +215,59 @@ struct TileMath {
             return ((float)a[0] + (float)a[1]) + ((float)a[2] + (float)a[3]);
         }
     }
+
+    // Two tiles A and B in one P.V: O += P (16 x 32 keys) . V (32 keys x D)
+    // as D/16 MFMA 16x16x32 (16-bit types; not for float32 caches). The key
+    // order of the contraction is A's keys 4*(l/16) .. +3, then B's: exactly
+    // the four scores a lane holds for each tile, and the matching halves of
+    // the two tiles' V loads. Returns the sum of this lane's eight weights as
+    // they entered the product.
+    __device__ static float pv2(const float (&pa)[4], const float (&pb)[4],
+                                const uint32_t (&va)[NVL][VLW], const uint32_t (&vb)[NVL][VLW],
+                                f32x4_t (&o)[NV]) {
+        static_assert(!kF32, "16-bit operands only");
+        if constexpr (QT == PKV_F16) {
+            const f16x8_t a = {(_Float16)pa[0], (_Float16)pa[1], (_Float16)pa[2], (_Float16)pa[3],
+                               (_Float16)pb[0], (_Float16)pb[1], (_Float16)pb[2], (_Float16)pb[3]};
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                o[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, v_operand<f16x8_t>(va, vb, j), o[j],
+                                                              0, 0, 0);
+            }
+            float l = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) l += (float)a[i];
+            return l;
+        } else {
+            const bf16x8_t a = {(__bf16)pa[0], (__bf16)pa[1], (__bf16)pa[2], (__bf16)pa[3],
+                                (__bf16)pb[0], (__bf16)pb[1], (__bf16)pb[2], (__bf16)pb[3]};
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, v_operand<bf16x8_t>(va, vb, j),
+                                                               o[j], 0, 0, 0);
+            }
+            float l = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) l += (float)a[i];
+            return l;
+        }
+    }
+
+    // B operand of element block j for pv2: tile A's 4 tokens, then tile B's.
+    template <typename V8>
+    __device__ static V8 v_operand(const uint32_t (&va)[NVL][VLW], const uint32_t (&vb)[NVL][VLW],
+                                   int j) {
+        const uint32_t* xa = &va[j / 2][(j % 2) * VW];
+        const uint32_t* xb = &vb[j / 2][(j % 2) * VW];
+        if constexpr (KT == PKV_FP8_E4M3) {
+            const u32x4_t u = {widen_fp8_pair<false>(xa[0]), widen_fp8_pair<true>(xa[0]),
+                               widen_fp8_pair<false>(xb[0]), widen_fp8_pair<true>(xb[0])};
+            return __builtin_bit_cast(V8, u);
+        } else {
+            const u32x4_t u = {xa[0], xa[1], xb[0], xb[1]};
+            return __builtin_bit_cast(V8, u);
+        }
+    }
 };
 
 // Value of `v` in lane addr / 4 (addr a byte address, as the LDS crossbar

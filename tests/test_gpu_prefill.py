@@ -70,6 +70,18 @@ def test_mixed_chunks_match_oracle(gpu, kv, qd, Hq, H, d):
     assert_close(got, oracle_rows(b, q, qs), kv, f"prefill {kv} G={Hq // H} d={d}")
 
 
+@pytest.mark.parametrize("G", [3, 5, 6, 7])
+def test_odd_tile_counts_with_canaries(gpu, G):
+    """With G not dividing 256 rows into whole 32-token steps, a workgroup's
+    causal range can end on the first tile of a step; the second tile then
+    stands in from the null block, which the canaries fill with NaN."""
+    ctx = [100, 333, 64, 47]
+    q_lens = [100, 200, 64, 47]
+    b, q, qs = make(66, ctx, q_lens, "f16", "f16", 2 * G, 2, 128, gpu)
+    got = out_to_f64(gpu_prefill(b, q, qs))
+    assert_close(got, oracle_rows(b, q, qs), "f16", f"G={G}")
+
+
 def test_long_chunks_sampled(gpu):
     """Two sequences with 1536- and 700-token chunks over 3000- and 700-token
     contexts: many row tiles of 256 rows per KV head."""
