@@ -9,15 +9,17 @@
 // Unlike decode this is a real contraction: for one (sequence, KV head) the
 // chunk's q_len * G query rows all meet the same K/V tiles. The kernel is
 // tiled for the matrix cores accordingly:
-//   * A workgroup of 8 waves owns 256 query rows of one (sequence, KV head),
+//   * A workgroup of 4 waves owns 128 query rows of one (sequence, KV head),
 //     stacked token-major (row = token * G + head), 32 per wave as two 16-row
-//     MFMA column sets; two waves share each SIMD, so one wave's softmax
-//     overlaps the other's matrix work.
-//   * The sequence's 16-token tiles stream through a 4-stage LDS ring, three
-//     tiles ahead of the one computed, moved from L2 straight into LDS by
-//     direct loads (no registers). Each wave reads a tile's K and V operands
-//     from LDS once per step and applies them to its 32 rows: a tile costs one
-//     L2 read per 256 rows.
+//     MFMA column sets. Two workgroups share a CU (two waves per SIMD), and
+//     their barriers are independent, so one's softmax and LDS reads overlap
+//     the other's matrix work.
+//   * The sequence's 16-token tiles stream through an LDS ring of three
+//     two-tile steps, two steps ahead of the one computed, moved from L2
+//     straight into LDS by direct loads (no registers). Each wave reads a
+//     step's K and V operands from LDS once and applies them to its 32 rows:
+//     a tile costs one L2 read per 128 rows. P.V contracts both tiles of a
+//     step in one 16x16x32 MFMA per 16 output columns.
 //   * Per 16-row block the arithmetic is decode's (TileMath): S^T = K . Q^T and
 //     O += P . V on MFMA, online softmax in log2 units with a lazily moved
 //     maximum. Tiles wholly before a row block's first position need no mask;
@@ -34,10 +36,10 @@ namespace pkv {
 
 namespace {
 
-constexpr int kPrefillWaves = 8;                    // waves per workgroup
+constexpr int kPrefillWaves = 4;                    // waves per workgroup
 constexpr int kRowBlocks = 2;                       // 16-row blocks per wave
 constexpr int kWaveRows = 16 * kRowBlocks;          // 32
-constexpr int kGroupRows = kPrefillWaves * kWaveRows;  // 256
+constexpr int kGroupRows = kPrefillWaves * kWaveRows;  // 128
 constexpr int kPrefillThreads = kPrefillWaves * kWave;
 constexpr int kRing = 3;  // LDS ring of two-tile steps: kRing - 1 steps in flight
 
@@ -53,6 +55,22 @@ __device__ __forceinline__ void load_to_lds(const uint8_t* src, uint8_t* lds_bas
     static_assert(SZ == 16, "load size");
     __builtin_amdgcn_global_load_lds((const void*)src,
                                      (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
+// Wait until at most n (0..8, wave-uniform) of this wave's vector-memory
+// operations are in flight: s_waitcnt takes its count as an immediate.
+__device__ __forceinline__ void wait_vmcnt(int n) {
+    switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(vmcnt_wait(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(vmcnt_wait(1)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(vmcnt_wait(2)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(vmcnt_wait(3)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(vmcnt_wait(4)); break;
+    case 5: __builtin_amdgcn_s_waitcnt(vmcnt_wait(5)); break;
+    case 6: __builtin_amdgcn_s_waitcnt(vmcnt_wait(6)); break;
+    case 7: __builtin_amdgcn_s_waitcnt(vmcnt_wait(7)); break;
+    default: __builtin_amdgcn_s_waitcnt(vmcnt_wait(8)); break;
+    }
 }
 
 // All waves of the workgroup reach this point. A compiler barrier on both
@@ -83,7 +101,7 @@ struct PrefillParams {
     void* out;
 };
 
-// Row tiles of 256 rows of a sequence (0 for an invalid chunk).
+// Row tiles of kGroupRows rows of a sequence (0 for an invalid chunk).
 __device__ __forceinline__ int row_tiles(const PrefillParams& p, int s) {
     const int a = p.query_start[s], b = p.query_start[s + 1];
     const int n = p.context_lens[s];
@@ -182,9 +200,26 @@ void paged_prefill_kernel(PrefillParams p) {
     constexpr int kPieces = 2 * (int)kTileBytes / 1024;  // of one tile: its K, then its V
     constexpr int kStepPieces = 2 * kPieces;
     constexpr uint32_t kStepBytes = 4 * kTileBytes;
-    static_assert(kTileBytes % 1024 == 0 && kStepPieces <= 4 * kPrefillWaves, "piece split");
-    const int my_pieces = (kStepPieces - wv + kPrefillWaves - 1) / kPrefillWaves;  // 0 .. 4
+    constexpr int kWavePieces = (kStepPieces + kPrefillWaves - 1) / kPrefillWaves;  // at most
+    static_assert(kTileBytes % 1024 == 0 && kWavePieces <= 8, "piece split");
+    const int my_pieces = (kStepPieces - wv + kPrefillWaves - 1) / kPrefillWaves;
     const int steps = (tiles + 1) / 2;
+    // V pieces are stored permuted so that the V operand reads are
+    // lane-contiguous (free of LDS bank conflicts): a lane's V load i is
+    // kVChunks 16-byte chunks (tokens 4 * g4 .. + 3 of its element columns),
+    // found at chunk 4 * t + g4 (times kVChunks) of their region of the tile;
+    // the piece's lane L fetches the chunk that reading lane L needs. fp8 V
+    // loads are 8 bytes per lane and are stored as they are.
+    constexpr int kVChunks = VLW / 4;
+    auto v_piece_src = [&](int pc) -> uint32_t {
+        if constexpr (kVChunks > 0) {
+            const int i = pc / kVChunks, h = pc % kVChunks;
+            const int sigma = 4 * (lane & 15) + (lane >> 4);  // 4 * t + g4 of reading lane L
+            return (uint32_t)(i * 1024 * kVChunks + (kVChunks * sigma + h) * 16);
+        } else {
+            return (uint32_t)pc * 1024 + (uint32_t)lane * 16;
+        }
+    };
     bool bad = false;
     auto issue = [&](int sp) {
         const uint32_t st = (uint32_t)(sp % kRing) * kStepBytes;
@@ -203,28 +238,24 @@ void paged_prefill_kernel(PrefillParams p) {
             off[h2] = tile_elem_offset(id, g, H, D) * KB;
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kWavePieces; ++i) {
             const int c = wv + i * kPrefillWaves;
             if (c < kStepPieces) {
                 const int th = c / kPieces;  // 0: tile A, 1: tile B
                 const int cc = c % kPieces;
                 const bool is_v = cc >= kPieces / 2;
-                const uint32_t pc = (uint32_t)(is_v ? cc - kPieces / 2 : cc) * 1024;
-                load_to_lds<16>((is_v ? p.v_cache : p.k_cache) + off[th] + pc + (uint32_t)lane * 16,
-                                lds + st + (uint32_t)th * 2 * kTileBytes + (is_v ? kTileBytes : 0) + pc);
+                const int pc = is_v ? cc - kPieces / 2 : cc;
+                const uint32_t src = is_v ? v_piece_src(pc) : (uint32_t)pc * 1024 + (uint32_t)lane * 16;
+                load_to_lds<16>((is_v ? p.v_cache : p.k_cache) + off[th] + src,
+                                lds + st + (uint32_t)th * 2 * kTileBytes + (is_v ? kTileBytes : 0) +
+                                    (uint32_t)pc * 1024);
             }
         }
     };
     // wait until at most `later` steps' loads of this wave are in flight
     auto wait_steps = [&](int later) {
         static_assert(kRing == 3, "later is 0 or 1");
-        switch (later > 0 ? my_pieces : 0) {
-        case 0: __builtin_amdgcn_s_waitcnt(vmcnt_wait(0)); break;
-        case 1: __builtin_amdgcn_s_waitcnt(vmcnt_wait(1)); break;
-        case 2: __builtin_amdgcn_s_waitcnt(vmcnt_wait(2)); break;
-        case 3: __builtin_amdgcn_s_waitcnt(vmcnt_wait(3)); break;
-        default: __builtin_amdgcn_s_waitcnt(vmcnt_wait(4)); break;
-        }
+        wait_vmcnt(later > 0 ? my_pieces : 0);
     };
     const uint32_t k_off = (uint32_t)((g4 * kBlock + t) * 8 * KB);
     const uint32_t v_off = (uint32_t)((t * 4 + g4) * 8 * KB);
@@ -252,11 +283,23 @@ void paged_prefill_kernel(PrefillParams p) {
                 kr[i][c] = reinterpret_cast<const uint32_t*>(lds + base + k_off + i * 4 * kBlock * 8 * KB)[c];
     };
     auto read_v = [&](uint32_t base, uint32_t (&vr)[NVL][VLW]) {
+        if constexpr (kVChunks > 0) {
+            // the permuted store: this lane's 16-byte chunks sit at lane * 16
 #pragma unroll
-        for (int i = 0; i < NVL; ++i)
+            for (int i = 0; i < NVL; ++i)
 #pragma unroll
-            for (int c = 0; c < VLW; ++c)
-                vr[i][c] = reinterpret_cast<const uint32_t*>(lds + base + v_off + i * 32 * kBlock * KB)[c];
+                for (int h = 0; h < kVChunks; ++h)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        vr[i][4 * h + c] = reinterpret_cast<const uint32_t*>(
+                            lds + base + (kVChunks * i + h) * 1024 + lane * 16)[c];
+        } else {
+#pragma unroll
+            for (int i = 0; i < NVL; ++i)
+#pragma unroll
+                for (int c = 0; c < VLW; ++c)
+                    vr[i][c] = reinterpret_cast<const uint32_t*>(lds + base + v_off + i * 32 * kBlock * KB)[c];
+        }
     };
 
     for (int sp = 0; sp < kRing - 1 && sp < steps; ++sp) issue(sp);
@@ -369,7 +412,7 @@ void paged_prefill_kernel(PrefillParams p) {
 // ---- dispatch ------------------------------------------------------------------
 
 int64_t prefill_task_bound(int num_seqs, int num_tokens, int group, int num_kv_heads) {
-    // sum over sequences of H * ceil(q_len * G / 256) <= H * (T * G / 256 + S)
+    // sum over sequences of H * ceil(q_len * G / R) <= H * (T * G / R + S), R = kGroupRows
     return (int64_t)num_kv_heads * (((int64_t)num_tokens * group) / kGroupRows + num_seqs);
 }
 

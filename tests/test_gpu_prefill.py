@@ -4,7 +4,7 @@ the oracle's plain causal definition (oracle_paged_prefill).
 Small chunks are compared row for row; long ones on sampled rows, each
 checked as a one-token chunk with the context up to its own position (the
 same definition). Cases: chunks of 1, 15, 16, 17 tokens and several row tiles
-of 256 rows, chunks shorter than their context, empty chunks, every cache type,
+of 128 rows, chunks shorter than their context, empty chunks, every cache type,
 G = 1..8 and d 64/128, one-token chunks equal to decode, a prompt fed whole or
 in chunks, and invalid chunks (skipped) or block ids (NaN rows)."""
 import numpy as np
@@ -72,7 +72,7 @@ def test_mixed_chunks_match_oracle(gpu, kv, qd, Hq, H, d):
 
 @pytest.mark.parametrize("G", [3, 5, 6, 7])
 def test_odd_tile_counts_with_canaries(gpu, G):
-    """With G not dividing 256 rows into whole 32-token steps, a workgroup's
+    """With G not dividing a workgroup's 128 rows into whole 32-token steps, its
     causal range can end on the first tile of a step; the second tile then
     stands in from the null block, which the canaries fill with NaN."""
     ctx = [100, 333, 64, 47]
@@ -84,12 +84,12 @@ def test_odd_tile_counts_with_canaries(gpu, G):
 
 def test_long_chunks_sampled(gpu):
     """Two sequences with 1536- and 700-token chunks over 3000- and 700-token
-    contexts: many row tiles of 256 rows per KV head."""
+    contexts: many row tiles of 128 rows per KV head."""
     ctx, q_lens = [3000, 700], [1536, 700]
     b, q, qs = make(62, ctx, q_lens, "bf16", "bf16", 32, 8, 128, gpu, canary=False)
     got = out_to_f64(gpu_prefill(b, q, qs))
     rng = np.random.default_rng(3)
-    rows = np.unique(np.concatenate([[0, 1, 255, 256, 1535, 1536, 2235],
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, 255, 256, 1535, 1536, 2235],
                                      rng.integers(0, 2236, 40)]))
     assert_close(got[rows], oracle_rows(b, q, qs, rows), "bf16", "long chunks, sampled rows")
 
