@@ -68,7 +68,7 @@ def kernel_hash() -> str:
     the build they were taken on."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("paged_decode.hip", "pkv_device.h"):
+    for f in ("paged_decode.hip", "pkv_tile.h", "pkv_device.h"):
         with open(os.path.join(ROOT, "paged_kv_cache_101_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
