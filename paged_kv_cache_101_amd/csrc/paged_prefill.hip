@@ -41,37 +41,34 @@ constexpr int kRowBlocks = 2;                       // 16-row blocks per wave
 constexpr int kWaveRows = 16 * kRowBlocks;          // 32
 constexpr int kGroupRows = kPrefillWaves * kWaveRows;  // 128
 constexpr int kPrefillThreads = kPrefillWaves * kWave;
-constexpr int kRing = 3;  // LDS ring of two-tile steps: kRing - 1 steps in flight
 
 // s_waitcnt operand that waits for the vector-memory counter to reach n
 // (expcnt and lgkmcnt left at their maxima; gfx9 encoding, vmcnt split
 // over bits 3:0 and 15:14).
 constexpr int vmcnt_wait(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
-// SZ bytes per lane from global memory straight into LDS: lane l's bytes land
-// at lds_base + l * SZ (lds_base is the same for the whole wave).
-template <int SZ>
-__device__ __forceinline__ void load_to_lds(const uint8_t* src, uint8_t* lds_base) {
-    static_assert(SZ == 16, "load size");
-    __builtin_amdgcn_global_load_lds((const void*)src,
-                                     (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes, read at
+// byte voff of the buffer, land at lds_base + l * 16 (lds_base is the same
+// for the whole wave). The address is a uniform resource plus a 32-bit lane
+// offset, so no 64-bit per-lane address is kept.
+__device__ __forceinline__ void load_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint8_t* lds_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16,
+                                             voff, 0, 0, 0);
 }
 
-// Wait until at most n (0..8, wave-uniform) of this wave's vector-memory
-// operations are in flight: s_waitcnt takes its count as an immediate.
-__device__ __forceinline__ void wait_vmcnt(int n) {
-    switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(vmcnt_wait(0)); break;
-    case 1: __builtin_amdgcn_s_waitcnt(vmcnt_wait(1)); break;
-    case 2: __builtin_amdgcn_s_waitcnt(vmcnt_wait(2)); break;
-    case 3: __builtin_amdgcn_s_waitcnt(vmcnt_wait(3)); break;
-    case 4: __builtin_amdgcn_s_waitcnt(vmcnt_wait(4)); break;
-    case 5: __builtin_amdgcn_s_waitcnt(vmcnt_wait(5)); break;
-    case 6: __builtin_amdgcn_s_waitcnt(vmcnt_wait(6)); break;
-    case 7: __builtin_amdgcn_s_waitcnt(vmcnt_wait(7)); break;
-    default: __builtin_amdgcn_s_waitcnt(vmcnt_wait(8)); break;
+// Wait until at most n (0..16, wave-uniform; larger n waits for 16) of this
+// wave's vector-memory operations are in flight: s_waitcnt takes its count
+// as an immediate.
+template <int N = 0>
+__device__ __forceinline__ void wait_vmcnt_from(int n) {
+    if constexpr (N >= 16) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_wait(16));
+    } else {
+        if (n <= N) __builtin_amdgcn_s_waitcnt(vmcnt_wait(N));
+        else wait_vmcnt_from<N + 1>(n);
     }
 }
+__device__ __forceinline__ void wait_vmcnt(int n) { wait_vmcnt_from<0>(n); }
 
 // All waves of the workgroup reach this point. A compiler barrier on both
 // sides keeps memory accesses from moving across it; unlike __syncthreads()
@@ -110,6 +107,50 @@ __device__ __forceinline__ int row_tiles(const PrefillParams& p, int s) {
     return ((b - a) * p.group + kGroupRows - 1) / kGroupRows;
 }
 
+// Ring depth in two-tile steps: four when a step is at most 16 KiB, else three
+// (two workgroups of a CU then fit in its LDS for every 16-bit and fp8 shape).
+template <int KT, int D>
+constexpr int ring_depth() {
+    return 4 * kBlock * D * Elem<KT>::bytes <= 16384 ? 4 : 3;
+}
+
+// The 16-bit compute type of a query type (f32 queries never use it).
+template <int QT>
+struct Compute16 {
+    typedef _Float16 E;
+    typedef _Float16 V2 __attribute__((ext_vector_type(2)));
+    typedef f16x8_t V8;
+};
+template <>
+struct Compute16<PKV_BF16> {
+    typedef __bf16 E;
+    typedef __bf16 V2 __attribute__((ext_vector_type(2)));
+    typedef bf16x8_t V8;
+};
+
+// The largest of its operands, NaN if any is NaN: no operand quieting is
+// needed, and three operands take one instruction (v_maximum3_f32).
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float vmax(float a, float b, float c) { return vmax(vmax(a, b), c); }
+
+// Four float results, elements idx .. idx + 3 of an output (idx a multiple of
+// four, the base 16-byte aligned), in the output type.
+template <int DT>
+__device__ __forceinline__ void store4_as(void* base, size_t idx, float a, float b, float c, float d) {
+    if constexpr (DT == PKV_F32) {
+        *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(base) + idx) = f32x4_t{a, b, c, d};
+    } else if constexpr (DT == PKV_F16) {
+        const f16x4_t h = {(_Float16)a, (_Float16)b, (_Float16)c, (_Float16)d};
+        *reinterpret_cast<u32x2_t*>(reinterpret_cast<_Float16*>(base) + idx) =
+            __builtin_bit_cast(u32x2_t, h);
+    } else {
+        static_assert(DT == PKV_BF16, "output type");
+        const u32x2_t w = {(uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16),
+                           (uint32_t)f32_to_bf16_rne(c) | ((uint32_t)f32_to_bf16_rne(d) << 16)};
+        *reinterpret_cast<u32x2_t*>(reinterpret_cast<uint16_t*>(base) + idx) = w;
+    }
+}
+
 }  // namespace
 
 template <int KT, int QT, int D>
@@ -117,14 +158,20 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
 void paged_prefill_kernel(PrefillParams p) {
     using TM = TileMath<KT, QT, D>;
     constexpr int NK = TM::NK, NV = TM::NV, NVL = TM::NVL, KW = TM::KW, VLW = TM::VLW;
+    constexpr int VW = TM::VW;
     constexpr int KB = Elem<KT>::bytes;
     constexpr int QB = Elem<QT>::bytes;
     constexpr uint32_t kTileBytes = (uint32_t)kBlock * D * KB;
+    constexpr int kRing = ring_depth<KT, D>();
+    constexpr uint32_t kStepBytes = 4 * kTileBytes;
+    constexpr bool kDirectV = (KB == 2);
+    typedef typename Compute16<QT>::E E16;
+    typedef typename Compute16<QT>::V2 V2;
+    typedef typename Compute16<QT>::V8 V8;
 
-    // kRing stages of two tiles' (K, V)
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kRing * 4 * kTileBytes];
+    // kRing stages of two tiles' (K, V): tile A's K, A's V, B's K, B's V
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kRing * kStepBytes];
 
-    const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wv = wave_id();
     const int S = p.num_seqs, H = p.num_kv_heads, G = p.group, Hq = p.num_q_heads;
@@ -160,9 +207,16 @@ void paged_prefill_kernel(PrefillParams p) {
     const int row_wg = rt * kGroupRows;
     const int last_row = min(nrows, row_wg + kGroupRows) - 1;
     const int tiles = (base_pos + last_row / G) / kBlock + 1;  // keys 0 .. last position
+    const int steps = (tiles + 1) / 2;
     const size_t bt_row = (size_t)s * p.max_blocks_per_seq;
 
-    // ---- per lane: its query row in each of the wave's four row blocks ----
+    // The score scale in log2 units, made non-negative: a negative scale
+    // flips the sign of q instead (exact), so that the running maximum can be
+    // taken on the raw scores.
+    const float c = fabsf(p.qk_scale_log2);
+    const uint32_t q_flip = p.qk_scale_log2 < 0.f ? (QB == 4 ? 0x80000000u : 0x80008000u) : 0u;
+
+    // ---- per lane: its query row (column t of the MFMA tiles) in each row block ----
     const int t = lane & 15;
     const int g4 = lane >> 4;
     const int row_w = row_wg + wv * kWaveRows;
@@ -176,40 +230,41 @@ void paged_prefill_kernel(PrefillParams p) {
         pos[rb] = base_pos + tok;
         const int h = g * G + (ok ? row % G : 0);
         TM::load_q(q[rb], p.q + ((size_t)(q0 + tok) * Hq + h) * D * QB, ok, g4);
+#pragma unroll
+        for (int i = 0; i < NK; ++i)
+#pragma unroll
+            for (int x = 0; x < TM::QW; ++x) q[rb].w[i][x] ^= q_flip;
     }
     // row-block extents (wave-uniform): first and last valid position
     int rb_first[kRowBlocks], rb_last[kRowBlocks];
+    int wave_last = -1;  // the last position any row of the wave has
 #pragma unroll
     for (int rb = 0; rb < kRowBlocks; ++rb) {
         const int r0 = row_w + rb * 16;
         const int r1 = min(nrows, r0 + 16) - 1;
         rb_first[rb] = r0 < nrows ? base_pos + r0 / G : INT32_MAX;
         rb_last[rb] = r0 < nrows ? base_pos + r1 / G : -1;
+        wave_last = max(wave_last, rb_last[rb]);
     }
 
     // ---- the tile stream: an LDS ring of two-tile steps, filled by direct loads ----
-    // A step is tiles 2 * sp (A) and 2 * sp + 1 (B); it goes to ring stage
-    // sp % kRing, kRing - 1 steps ahead of the one computed. A step is moved
-    // from L2 straight into LDS (no registers) in 1 KiB pieces, 16 bytes per
-    // lane: piece c (A's K, A's V, B's K, B's V, in that order) is carried by
-    // wave c % 8. A wave waits for its own loads of step sp (the counter counts
-    // its loads in issue order), then the barrier makes every wave's pieces
-    // visible; the stage refilled after that barrier was last read before it.
-    // A tile B past the last one reads the null block (it is masked out), so
-    // every step issues the same loads.
+    // Step sp (tiles 2 sp and 2 sp + 1) goes to ring stage sp % kRing. It is
+    // moved from L2 straight into LDS (no registers) in 1 KiB pieces, 16 bytes
+    // per lane, piece c carried by wave c % 4, kRing - 1 steps ahead of the
+    // step whose P . V is computed. A wave waits for its own loads (the
+    // counter counts them in issue order), then the barrier makes every
+    // wave's pieces visible. A tile past the last one reads the null block.
     constexpr int kPieces = 2 * (int)kTileBytes / 1024;  // of one tile: its K, then its V
     constexpr int kStepPieces = 2 * kPieces;
-    constexpr uint32_t kStepBytes = 4 * kTileBytes;
     constexpr int kWavePieces = (kStepPieces + kPrefillWaves - 1) / kPrefillWaves;  // at most
-    static_assert(kTileBytes % 1024 == 0 && kWavePieces <= 8, "piece split");
-    const int my_pieces = (kStepPieces - wv + kPrefillWaves - 1) / kPrefillWaves;
-    const int steps = (tiles + 1) / 2;
+    static_assert(kTileBytes % 1024 == 0, "piece split");
+    static_assert((kRing - 2) * kWavePieces <= 16, "wait count");
     // V pieces are stored permuted so that the V operand reads are
-    // lane-contiguous (free of LDS bank conflicts): a lane's V load i is
-    // kVChunks 16-byte chunks (tokens 4 * g4 .. + 3 of its element columns),
-    // found at chunk 4 * t + g4 (times kVChunks) of their region of the tile;
-    // the piece's lane L fetches the chunk that reading lane L needs. fp8 V
-    // loads are 8 bytes per lane and are stored as they are.
+    // lane-contiguous: a lane's V load i (tokens 4 * g4 .. + 3 of its element
+    // columns, kVChunks 16-byte chunks) sits at chunk 4 * t + g4 (times
+    // kVChunks) of its region of the tile, so the piece's lane L fetches the
+    // chunk that reading lane L needs. fp8 V loads are 8 bytes per lane and
+    // are stored as they are.
     constexpr int kVChunks = VLW / 4;
     auto v_piece_src = [&](int pc) -> uint32_t {
         if constexpr (kVChunks > 0) {
@@ -220,51 +275,95 @@ void paged_prefill_kernel(PrefillParams p) {
             return (uint32_t)pc * 1024 + (uint32_t)lane * 16;
         }
     };
+    // What this wave carries of every step (the same pieces each step): the
+    // cache and this lane's 16 bytes inside the tile, the tile (A or B), and
+    // the piece's place in the stage. Fixed before the loop, so that issuing
+    // a step takes no look-up of the kernel arguments.
+    uint32_t pc_src[kWavePieces];  // this lane's offset in the tile (per lane)
+    uint32_t pc_dst[kWavePieces];
+    bool pc_b[kWavePieces], pc_v[kWavePieces];
+    bool pc_ok[kWavePieces];  // the wave carries piece i (the last may be absent)
+    const int my_pieces = (kStepPieces - wv + kPrefillWaves - 1) / kPrefillWaves;
+#pragma unroll
+    for (int i = 0; i < kWavePieces; ++i) {
+        const int c2 = min(wv + i * kPrefillWaves, kStepPieces - 1);
+        pc_ok[i] = wv + i * kPrefillWaves < kStepPieces;
+        const int th = c2 / kPieces;  // 0: tile A, 1: tile B
+        const int cc = c2 % kPieces;
+        const bool is_v = cc >= kPieces / 2;
+        const int pc = is_v ? cc - kPieces / 2 : cc;
+        pc_src[i] = is_v ? v_piece_src(pc) : (uint32_t)pc * 1024 + (uint32_t)lane * 16;
+        pc_v[i] = is_v;
+        pc_dst[i] = (uint32_t)th * 2 * kTileBytes + (is_v ? kTileBytes : 0) + (uint32_t)pc * 1024;
+        pc_b[i] = th == 1;
+    }
     bool bad = false;
-    auto issue = [&](int sp) {
+    // Block-table entries of step sp's two tiles as read (0, the null block,
+    // past the last tile). They are read an iteration before the step is
+    // issued and checked only then, so the scalar loads are not waited for
+    // at once.
+    auto step_ids = [&](int sp, int& ia, int& ib) {
+        ia = 2 * sp < tiles ? uniform_read(p.block_tables, bt_row + 2 * sp) : 0;
+        ib = 2 * sp + 1 < tiles ? uniform_read(p.block_tables, bt_row + 2 * sp + 1) : 0;
+    };
+    auto checked = [&](int id) -> int {
+        if (id < 0 || id >= p.num_blocks) {
+            bad = true;  // its rows become NaN; the null block is read instead
+            return 0;
+        }
+        return id;
+    };
+    auto issue = [&](int sp, int ia, int ib) {
         const uint32_t st = (uint32_t)(sp % kRing) * kStepBytes;
-        size_t off[2];
+        const size_t off_a = tile_elem_offset(checked(ia), g, H, D) * KB;
+        const size_t off_b = tile_elem_offset(checked(ib), g, H, D) * KB;
+        const __amdgpu_buffer_rsrc_t rka = make_rsrc(p.k_cache + off_a, kTileBytes);
+        const __amdgpu_buffer_rsrc_t rva = make_rsrc(p.v_cache + off_a, kTileBytes);
+        const __amdgpu_buffer_rsrc_t rkb = make_rsrc(p.k_cache + off_b, kTileBytes);
+        const __amdgpu_buffer_rsrc_t rvb = make_rsrc(p.v_cache + off_b, kTileBytes);
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-            const int j = 2 * sp + h2;
-            int id = 0;  // past the last tile: the null block, masked out
-            if (j < tiles) {
-                id = uniform_read(p.block_tables, bt_row + j);
-                if (id < 0 || id >= p.num_blocks) {
-                    bad = true;  // its rows become NaN; the null block is read instead
-                    id = 0;
-                }
-            }
-            off[h2] = tile_elem_offset(id, g, H, D) * KB;
-        }
-#pragma unroll
-        for (int i = 0; i < kWavePieces; ++i) {
-            const int c = wv + i * kPrefillWaves;
-            if (c < kStepPieces) {
-                const int th = c / kPieces;  // 0: tile A, 1: tile B
-                const int cc = c % kPieces;
-                const bool is_v = cc >= kPieces / 2;
-                const int pc = is_v ? cc - kPieces / 2 : cc;
-                const uint32_t src = is_v ? v_piece_src(pc) : (uint32_t)pc * 1024 + (uint32_t)lane * 16;
-                load_to_lds<16>((is_v ? p.v_cache : p.k_cache) + off[th] + src,
-                                lds + st + (uint32_t)th * 2 * kTileBytes + (is_v ? kTileBytes : 0) +
-                                    (uint32_t)pc * 1024);
-            }
-        }
+        for (int i = 0; i < kWavePieces; ++i)
+            if (pc_ok[i])
+                load_to_lds(pc_v[i] ? (pc_b[i] ? rvb : rva) : (pc_b[i] ? rkb : rka), pc_src[i],
+                            lds + st + pc_dst[i]);
     };
     // wait until at most `later` steps' loads of this wave are in flight
-    auto wait_steps = [&](int later) {
-        static_assert(kRing == 3, "later is 0 or 1");
-        wait_vmcnt(later > 0 ? my_pieces : 0);
-    };
+    auto wait_steps = [&](int later) { wait_vmcnt(later * my_pieces); };
+
     const uint32_t k_off = (uint32_t)((g4 * kBlock + t) * 8 * KB);
     const uint32_t v_off = (uint32_t)((t * 4 + g4) * 8 * KB);
     const int x16 = (lane ^ 16) << 2, x32 = (lane ^ 32) << 2;
-    int head_lane[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) head_lane[j] = (4 * g4 + j) << 2;
-    const float qk_scale = p.qk_scale_log2;
 
+    auto read_k = [&](uint32_t base, uint32_t (&kr)[NK][KW]) {
+#pragma unroll
+        for (int i = 0; i < NK; ++i)
+#pragma unroll
+            for (int x = 0; x < KW; ++x)
+                kr[i][x] = reinterpret_cast<const uint32_t*>(lds + base + k_off + i * 4 * kBlock * 8 * KB)[x];
+    };
+    auto read_v = [&](uint32_t base, uint32_t (&vr)[NVL][VLW]) {
+        if constexpr (kVChunks > 0) {
+            // the permuted store: this lane's 16-byte chunks sit at lane * 16
+#pragma unroll
+            for (int i = 0; i < NVL; ++i)
+#pragma unroll
+                for (int h = 0; h < kVChunks; ++h)
+#pragma unroll
+                    for (int x = 0; x < 4; ++x)
+                        vr[i][4 * h + x] = reinterpret_cast<const uint32_t*>(
+                            lds + base + (kVChunks * i + h) * 1024 + lane * 16)[x];
+        } else {
+#pragma unroll
+            for (int i = 0; i < NVL; ++i)
+#pragma unroll
+                for (int x = 0; x < VLW; ++x)
+                    vr[i][x] = reinterpret_cast<const uint32_t*>(lds + base + v_off + i * 32 * kBlock * KB)[x];
+        }
+    };
+    // Running state per row block, for this lane's row t: the maximum m (log2
+    // units, scaled), the lane's part of the weight sum, and O^T: o[rb][j]
+    // holds elements 16 j + 4 g4 + r of row t (O^T = V^T P^T puts the query
+    // row in the MFMA column, so every row statistic stays in its lanes).
     float m_run[kRowBlocks], l_run[kRowBlocks];
     f32x4_t o[kRowBlocks][NV];
 #pragma unroll
@@ -275,136 +374,278 @@ void paged_prefill_kernel(PrefillParams p) {
         for (int j = 0; j < NV; ++j) o[rb][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    auto read_k = [&](uint32_t base, uint32_t (&kr)[NK][KW]) {
+    // S^T of both tiles of a stage for every row block: the NK-slab chains of
+    // the four (tile, row block) pairs interleaved.
+    auto qk_products = [&](const uint32_t (&kr)[2][NK][KW], f32x4_t (&sc)[2][kRowBlocks]) {
+#pragma unroll
+        for (int th = 0; th < 2; ++th)
+#pragma unroll
+            for (int rb = 0; rb < kRowBlocks; ++rb) sc[th][rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < NK; ++i)
 #pragma unroll
-            for (int c = 0; c < KW; ++c)
-                kr[i][c] = reinterpret_cast<const uint32_t*>(lds + base + k_off + i * 4 * kBlock * 8 * KB)[c];
+            for (int th = 0; th < 2; ++th)
+#pragma unroll
+                for (int rb = 0; rb < kRowBlocks; ++rb) {
+                    if constexpr (TM::kF32) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            sc[th][rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                __builtin_bit_cast(float, kr[th][i][e]),
+                                __builtin_bit_cast(float, q[rb].w[i][e]), sc[th][rb], 0, 0, 0);
+                    } else if constexpr (QT == PKV_F16) {
+                        const u32x4_t qu = {q[rb].w[i][0], q[rb].w[i][1], q[rb].w[i][2], q[rb].w[i][3]};
+                        sc[th][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            TM::template k_operand<f16x8_t>(kr[th][i]), __builtin_bit_cast(f16x8_t, qu),
+                            sc[th][rb], 0, 0, 0);
+                    } else {
+                        const u32x4_t qu = {q[rb].w[i][0], q[rb].w[i][1], q[rb].w[i][2], q[rb].w[i][3]};
+                        sc[th][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            TM::template k_operand<bf16x8_t>(kr[th][i]),
+                            __builtin_bit_cast(bf16x8_t, qu), sc[th][rb], 0, 0, 0);
+                    }
+                }
     };
-    auto read_v = [&](uint32_t base, uint32_t (&vr)[NVL][VLW]) {
-        if constexpr (kVChunks > 0) {
-            // the permuted store: this lane's 16-byte chunks sit at lane * 16
+    auto scores = [&](uint32_t st, f32x4_t (&sc)[2][kRowBlocks]) {
+        uint32_t kr[2][NK][KW];
+        read_k(st, kr[0]);
+        read_k(st + 2 * kTileBytes, kr[1]);
+        qk_products(kr, sc);
+    };
+    // V of the step in stage st: for 16-bit caches the P . V operands
+    // themselves (operand j = tile A's 4 tokens of element column 16 j + t,
+    // then tile B's: two 8-byte reads, 2 * kTileBytes apart), else the loads.
+    auto read_vops = [&](uint32_t st, u32x4_t (&vop)[NV], uint32_t (&va)[NVL][VLW],
+                         uint32_t (&vb)[NVL][VLW]) {
+        if constexpr (kDirectV) {
+            const uint8_t* la = lds + st + kTileBytes + lane * 16;
 #pragma unroll
             for (int i = 0; i < NVL; ++i)
 #pragma unroll
-                for (int h = 0; h < kVChunks; ++h)
-#pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        vr[i][4 * h + c] = reinterpret_cast<const uint32_t*>(
-                            lds + base + (kVChunks * i + h) * 1024 + lane * 16)[c];
+                for (int hh = 0; hh < 2; ++hh) {
+                    const u32x2_t a2 = *reinterpret_cast<const u32x2_t*>(la + i * 1024 + hh * 8);
+                    const u32x2_t b2 =
+                        *reinterpret_cast<const u32x2_t*>(la + 2 * kTileBytes + i * 1024 + hh * 8);
+                    vop[2 * i + hh] = __builtin_shufflevector(a2, b2, 0, 1, 2, 3);
+                }
         } else {
+            read_v(st + kTileBytes, va);
+            read_v(st + 3 * kTileBytes, vb);
+        }
+    };
+    // Zero the V elements of keys that no row sees: na and nb live keys
+    // among this lane's four of tile A and of tile B.
+    auto mask_vops = [&](int na, int nb, u32x4_t (&vop)[NV], uint32_t (&va)[NVL][VLW],
+                         uint32_t (&vb)[NVL][VLW]) {
+        if constexpr (kDirectV) {
+            // dword d of a lane's four tokens holds tokens 2 d and 2 d + 1
+            auto m2 = [](int live, int d) -> uint32_t {
+                return live >= 2 * d + 2 ? ~0u : live == 2 * d + 1 ? 0xFFFFu : 0u;
+            };
+            const u32x4_t m = {m2(na, 0), m2(na, 1), m2(nb, 0), m2(nb, 1)};
 #pragma unroll
-            for (int i = 0; i < NVL; ++i)
+            for (int j = 0; j < NV; ++j) vop[j] &= m;
+        } else {
+            TM::mask_v(va, na);
+            TM::mask_v(vb, nb);
+        }
+    };
+    // The largest of a row block's eight scores held by this lane.
+    auto max8 = [](const float (&x)[8]) -> float {
+        return vmax(vmax(vmax(x[0], x[1]), x[2]), vmax(vmax(x[3], x[4]), x[5]), vmax(x[6], x[7]));
+    };
+    // Move row block rb's running maximum when a score (this lane's largest:
+    // xm, raw) exceeds it by more than the lazy margin in any lane.
+    auto rescale = [&](int rb, float xm) {
+        if (__any(xm * c > m_run[rb] + kLazyRescale)) {
+            float tm = vmax(xm, lane_fetch(x16, xm));
+            tm = vmax(tm, lane_fetch(x32, tm));
+            const float mn = vmax(m_run[rb], tm * c);
+            const float cf = __builtin_amdgcn_exp2f(m_run[rb] - mn);
+            l_run[rb] *= cf;
 #pragma unroll
-                for (int c = 0; c < VLW; ++c)
-                    vr[i][c] = reinterpret_cast<const uint32_t*>(lds + base + v_off + i * 32 * kBlock * KB)[c];
+            for (int j = 0; j < NV; ++j) o[rb][j] *= cf;
+            m_run[rb] = mn;
+        }
+    };
+    // The weights of a row block's eight raw scores, rounded to the 16-bit
+    // type in pairs and packed as the P^T operand; l_run gains their sum as
+    // rounded (dot products with ones).
+    auto weights16 = [&](int rb, const float (&x)[8]) -> V8 {
+        V2 h[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            h[i] = V2{(E16)__builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * i], c, -m_run[rb])),
+                      (E16)__builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * i + 1], c, -m_run[rb]))};
+        const V2 one = {(E16)1.f, (E16)1.f};
+        float l = l_run[rb];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (QT == PKV_F16) l = __builtin_amdgcn_fdot2(h[i], one, l, false);
+            else l = __builtin_amdgcn_fdot2_f32_bf16(h[i], one, l, false);
+        }
+        l_run[rb] = l;
+        return __builtin_shufflevector(__builtin_shufflevector(h[0], h[1], 0, 1, 2, 3),
+                                       __builtin_shufflevector(h[2], h[3], 0, 1, 2, 3), 0, 1, 2, 3, 4,
+                                       5, 6, 7);
+    };
+    // O^T += V^T P^T for row block rb (16-bit operands).
+    auto pv16 = [&](int rb, V8 pk, const u32x4_t (&vop)[NV], const uint32_t (&va)[NVL][VLW],
+                    const uint32_t (&vb)[NVL][VLW]) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            V8 vj;
+            if constexpr (kDirectV) vj = __builtin_bit_cast(V8, vop[j]);
+            else vj = TM::template v_operand<V8>(va, vb, j);
+            if constexpr (QT == PKV_F16)
+                o[rb][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vj, pk, o[rb][j], 0, 0, 0);
+            else
+                o[rb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vj, pk, o[rb][j], 0, 0, 0);
         }
     };
 
-    for (int sp = 0; sp < kRing - 1 && sp < steps; ++sp) issue(sp);
+    int nia = 0, nib = 0;  // blocks of the next step to issue
+    for (int sp = 0; sp < kRing - 1 && sp < steps; ++sp) {
+        int ia, ib;
+        step_ids(sp, ia, ib);
+        issue(sp, ia, ib);
+    }
+    if (kRing - 1 < steps) step_ids(kRing - 1, nia, nib);
+    wait_steps(min(kRing - 2, steps - 1));
+    workgroup_barrier();
+    f32x4_t s_cur[2][kRowBlocks];
+    scores(0, s_cur);
+    const bool rows_full = rb_last[kRowBlocks - 1] >= 0;  // every row block of the wave has rows
+
     for (int sp = 0; sp < steps; ++sp) {
+        const bool has_next = sp + 1 < steps;
+        if (has_next) {
+            // step sp + 1 in LDS for every wave; stage (sp - 1) % kRing free
+            wait_steps(min(kRing - 3, steps - 2 - sp));
+            workgroup_barrier();
+            if (sp + kRing - 1 < steps) issue(sp + kRing - 1, nia, nib);
+        }
         const uint32_t st = (uint32_t)(sp % kRing) * kStepBytes;
-        wait_steps(min(kRing - 2, steps - 1 - sp));
-        workgroup_barrier();
-        if (sp + kRing - 1 < steps) issue(sp + kRing - 1);
+        const uint32_t st_next = (uint32_t)((sp + 1) % kRing) * kStepBytes;
         const int key0 = 2 * sp * kBlock;  // first key of tile A; tile B starts at key0 + 16
         const bool has_b = 2 * sp + 1 < tiles;
-        bool any = false;  // a row block of this wave sees a key of the step
+        bool done = false;
+        if constexpr (!TM::kF32) {
+            if (has_next && rows_full && key0 + 2 * kBlock - 1 <= rb_first[0]) {
+                // A full step: every row of the wave sees all 32 keys (no
+                // causal mask, no key past n) and a next step exists. After
+                // the rare rescale, one straight-line block that the compiler
+                // schedules as a whole: the next step's QK products, this
+                // step's weights, the V reads and P . V.
+                uint32_t kr[2][NK][KW];
+                read_k(st_next, kr[0]);
+                read_k(st_next + 2 * kTileBytes, kr[1]);
+                float x[kRowBlocks][8], xm[kRowBlocks];
+                bool trig = false;
 #pragma unroll
-        for (int rb = 0; rb < kRowBlocks; ++rb) any |= rb_last[rb] >= key0;
-        if (!any) continue;
-        // scores of both tiles for every row block
-        f32x4_t sa[kRowBlocks], sb[kRowBlocks];
-        {
-            uint32_t kr[NK][KW];
-            read_k(st, kr);
+                for (int rb = 0; rb < kRowBlocks; ++rb) {
 #pragma unroll
-            for (int rb = 0; rb < kRowBlocks; ++rb) sa[rb] = TM::qk(kr, q[rb]);
-            read_k(st + 2 * kTileBytes, kr);
-#pragma unroll
-            for (int rb = 0; rb < kRowBlocks; ++rb) sb[rb] = TM::qk(kr, q[rb]);
-        }
-        uint32_t va[NVL][VLW], vb[NVL][VLW];
-        read_v(st + kTileBytes, va);
-        read_v(st + 3 * kTileBytes, vb);
-        // Keys at or past n (the unused rows of the last block), and a tile B
-        // past the workgroup's last tile (which the causal limit, not n, can
-        // end), are seen by no row: their V elements are zeroed, so that
-        // whatever those rows hold cannot reach P . V (their scores are
-        // excluded by select below).
-        if (key0 + kBlock > n) TM::mask_v(va, n - key0 - 4 * g4);
-        if (!has_b) TM::mask_v(vb, 0);  // the null block stands in for a missing tile B
-        else if (key0 + 2 * kBlock > n) TM::mask_v(vb, n - key0 - kBlock - 4 * g4);
-#pragma unroll
-        for (int rb = 0; rb < kRowBlocks; ++rb) {
-            if (rb_last[rb] < key0) continue;  // no row of the block sees this step
-            float xa[4], xb[4];
-            if (key0 + 2 * kBlock - 1 <= rb_first[rb]) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    xa[e] = sa[rb][e] * qk_scale;
-                    xb[e] = sb[rb][e] * qk_scale;
+                    for (int e = 0; e < 4; ++e) {
+                        x[rb][e] = s_cur[0][rb][e];
+                        x[rb][4 + e] = s_cur[1][rb][e];
+                    }
+                    xm[rb] = max8(x[rb]);
+                    trig = trig || xm[rb] * c > m_run[rb] + kLazyRescale;
                 }
-            } else {
-                // a diagonal step: key k of this lane is key0 + 4 * g4 + e (A)
-                // and key0 + 16 + 4 * g4 + e (B)
+                if (__any(trig)) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    xa[e] = key0 + 4 * g4 + e <= pos[rb] ? sa[rb][e] * qk_scale : -INFINITY;
-                    xb[e] = has_b && key0 + kBlock + 4 * g4 + e <= pos[rb] ? sb[rb][e] * qk_scale
-                                                                           : -INFINITY;
+                    for (int rb = 0; rb < kRowBlocks; ++rb) rescale(rb, xm[rb]);
                 }
-            }
-            const float xm = fmaxf(fmaxf(fmaxf(xa[0], xa[1]), fmaxf(xa[2], xa[3])),
-                                   fmaxf(fmaxf(xb[0], xb[1]), fmaxf(xb[2], xb[3])));
-            if (__any(xm > m_run[rb] + kLazyRescale)) {
-                float tm = fmaxf(xm, lane_fetch(x16, xm));
-                tm = fmaxf(tm, lane_fetch(x32, tm));
-                const float mn = fmaxf(m_run[rb], tm);
-                const float cf = __builtin_amdgcn_exp2f(m_run[rb] - mn);
-                l_run[rb] *= cf;
+                qk_products(kr, s_cur);
+                V8 pk[kRowBlocks];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float cr = lane_fetch(head_lane[r], cf);
+                for (int rb = 0; rb < kRowBlocks; ++rb) pk[rb] = weights16(rb, x[rb]);
+                // V is read once the K operands are consumed (their registers
+                // are reused)
+                u32x4_t vop[NV];
+                uint32_t va[NVL][VLW], vb[NVL][VLW];
+                read_vops(st, vop, va, vb);
 #pragma unroll
-                    for (int e = 0; e < NV; ++e) o[rb][e][r] *= cr;
-                }
-                m_run[rb] = mn;
-            }
-            float pa[4], pb[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                pa[e] = __builtin_amdgcn_exp2f(xa[e] - m_run[rb]);
-                pb[e] = __builtin_amdgcn_exp2f(xb[e] - m_run[rb]);
-            }
-            if constexpr (TM::kF32) {
-                l_run[rb] += TM::pv(pa, va, o[rb]);
-                l_run[rb] += TM::pv(pb, vb, o[rb]);
-            } else {
-                l_run[rb] += TM::pv2(pa, pb, va, vb, o[rb]);
+                for (int rb = 0; rb < kRowBlocks; ++rb) pv16(rb, pk[rb], vop, va, vb);
+                done = true;
             }
         }
+        if (!done && wave_last >= key0) {  // else every row of the wave is complete
+            // A step on the causal diagonal, past n, or in the last position:
+            // this step's softmax and P . V, then the next step's scores
+            // (sequential: such steps are few).
+            // Keys at or past n (the unused rows of the last block), and a tile B
+            // past the workgroup's last tile (which the causal limit, not n, can
+            // end), are seen by no row: their V elements are zeroed, so that
+            // whatever those rows hold cannot reach P . V (their scores are
+            // excluded by select below).
+            u32x4_t vop[NV];
+            uint32_t va[NVL][VLW], vb[NVL][VLW];
+            read_vops(st, vop, va, vb);
+            const int na = n - key0 - 4 * g4;          // live keys among this lane's four of tile A
+            const int nb = has_b ? na - kBlock : 0;  // and of tile B (the null block: none)
+            if (key0 + 2 * kBlock > n || !has_b) mask_vops(na, nb, vop, va, vb);
+#pragma unroll
+            for (int rb = 0; rb < kRowBlocks; ++rb) {
+                if (rb_last[rb] < key0) continue;  // no row of the block sees this step
+                // raw scores: tile A keys key0 + 4 g4 + e, tile B keys key0 + 16 + 4 g4 + e
+                float x[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x[e] = s_cur[0][rb][e];
+                    x[4 + e] = s_cur[1][rb][e];
+                }
+                if (key0 + 2 * kBlock - 1 > rb_first[rb]) {  // a diagonal step: causal select
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        x[e] = key0 + 4 * g4 + e <= pos[rb] ? x[e] : -INFINITY;
+                        x[4 + e] = key0 + kBlock + 4 * g4 + e <= pos[rb] ? x[4 + e] : -INFINITY;
+                    }
+                }
+                rescale(rb, max8(x));
+                if constexpr (TM::kF32) {
+                    float pw[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        pw[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], c, -m_run[rb]));
+                    // O^T += V^T P^T per tile on 16x16x4: k index = key 4 g4 + kk
+#pragma unroll
+                    for (int j = 0; j < NV; ++j)
+#pragma unroll
+                        for (int kk = 0; kk < 4; ++kk) {
+                            o[rb][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                __builtin_bit_cast(float, va[j / 2][(j % 2) * VW + kk]), pw[kk],
+                                o[rb][j], 0, 0, 0);
+                            o[rb][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                __builtin_bit_cast(float, vb[j / 2][(j % 2) * VW + kk]), pw[4 + kk],
+                                o[rb][j], 0, 0, 0);
+                        }
+                    l_run[rb] += ((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7]));
+                } else {
+                    pv16(rb, weights16(rb, x), vop, va, vb);
+                }
+            }
+            if (has_next && wave_last >= key0 + 2 * kBlock) scores(st_next, s_cur);
+        }
+        if (sp + kRing < steps) step_ids(sp + kRing, nia, nib);
     }
 
     __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));  // no load into LDS outlives the workgroup
 
-    // ---- normalise and store the wave's rows ----
+    // ---- normalise and store: lane (t, g4) holds elements 16 j + 4 g4 .. + 3 of row t ----
     const float nan = __builtin_nanf("");
 #pragma unroll
     for (int rb = 0; rb < kRowBlocks; ++rb) {
         float lt = l_run[rb] + lane_fetch(x16, l_run[rb]);
         lt += lane_fetch(x32, lt);
+        const float sc = bad ? nan : p.v_scale / lt;
+        const int row = row_w + rb * 16 + t;
+        if (row < nrows) {
+            const size_t orow = (size_t)(q0 + row / G) * Hq + g * G + row % G;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float sc = p.v_scale / lane_fetch(head_lane[r], lt);
-            const int row = row_w + rb * 16 + 4 * g4 + r;
-            if (row < nrows) {
-                const size_t orow = (size_t)(q0 + row / G) * Hq + g * G + row % G;
-#pragma unroll
-                for (int e = 0; e < NV; ++e)
-                    store_f32_as<QT>(p.out, orow * D + 16 * e + t, bad ? nan : o[rb][e][r] * sc);
-            }
+            for (int j = 0; j < NV; ++j)
+                store4_as<QT>(p.out, orow * D + 16 * j + 4 * g4, o[rb][j][0] * sc, o[rb][j][1] * sc,
+                              o[rb][j][2] * sc, o[rb][j][3] * sc);
         }
     }
 }
