@@ -362,7 +362,7 @@ def main():
     roofline = {
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-        "kernel": ("paged_decode_kernel suffix pass + shared_prefix_kernel (two launches per "
+        "kernel": ("paged_decode_kernel suffix pass + paged_prefill_kernel prefix mode (two launches per "
                    "pkv_paged_attention_decode_shared_prefix call)" if shared else
                    "paged_decode_kernel (one launch per pkv_paged_attention_decode call)"),
         "algorithmic_bytes_per_launch": kv_bytes_launch,

@@ -222,9 +222,8 @@ int pkv_paged_attention_decode(const void *q, int32_t q_dtype, int32_t num_seqs,
 /* Workspace bytes pkv_paged_attention_decode_shared_prefix needs. Front:
  * the decode slots for the worker count, float32 suffix results
  * (num_seqs * num_q_heads * head_dim, then num_seqs * num_q_heads floats) and
- * 2048 prefix partial slots of 16 * head_dim + 32 floats. End: int32 prefix
- * counters (num_kv_heads * (ceil(num_seqs * G / 16) + num_groups)), then the
- * decode counters [num_seqs][num_kv_heads]. Each part is rounded up to 256
+ * 4096 prefix partial slots of 16 * head_dim + 32 floats. End: the decode
+ * counters [num_seqs][num_kv_heads]. Each part is rounded up to 256
  * bytes. Returns 0 where pkv_decode_workspace_bytes does, or for
  * num_groups < 0 or > num_seqs. */
 size_t pkv_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
@@ -256,13 +255,15 @@ size_t pkv_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  * outside [0, max_blocks_per_seq], it is ignored and every sequence is
  * decoded plainly (still the same result).
  *
- * How: two launches on the stream. The suffix pass is the decode kernel over
- * each member's blocks after its group's prefix; it leaves the members' rows
- * as float32 (normalised output, log2-sum-exp) in the workspace. The prefix
- * pass stacks the (member, query head) rows of a group 16 at a time against
- * each shared tile, splits the prefix into chunks when there are few rows,
- * and merges the chunk partials with the suffix results by the log-sum-exp
- * rule into out.
+ * How: three launches on the stream. The suffix pass is the decode kernel
+ * over each member's blocks after its group's prefix; it leaves the members'
+ * rows as float32 (normalised output, log2-sum-exp) in the workspace. The
+ * prefix pass stacks the (member, query head) rows of a group 128 to a
+ * workgroup against the shared tiles, read once per workgroup through LDS,
+ * and splits the prefix into chunks when there are few rows. A group with
+ * one chunk is merged with its suffix results at once; otherwise the chunk
+ * partials go to the workspace and the merge launch combines them with the
+ * suffix results by the log-sum-exp rule into out.
  *
  *  num_groups   0..num_seqs (0: plain decode; the arrays may then be NULL)
  *  workspace    at least pkv_shared_prefix_workspace_bytes(...) bytes,

@@ -18,7 +18,7 @@ LIB = os.path.join(PKG, "libpkv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["pkv_api.hip", "kv_append.hip", "paged_decode.hip", "shared_prefix.hip",
+SOURCES = ["pkv_api.hip", "kv_append.hip", "paged_decode.hip",
            "paged_prefill.hip"]
 HOST_SOURCES = ["block_manager.cpp"]  # plain host C++ (g++)
 CXX = os.environ.get("CXX", "g++")

@@ -47,7 +47,7 @@
 // streams only the blocks after its group's shared ones, and its rows go to a
 // float32 result (the normalised output without v_scale, and the
 // log2-sum-exp of its scores) that the prefix pass merges with the prefix's
-// partials (shared_prefix.hip). Other sequences are decoded as usual.
+// partials (paged_prefill.hip, prefix mode). Other sequences are decoded as usual.
 #include <atomic>
 
 #include "pkv_internal.h"

@@ -14,21 +14,27 @@
 //     MFMA column sets. Two workgroups share a CU (two waves per SIMD), and
 //     their barriers are independent, so one's softmax and LDS reads overlap
 //     the other's matrix work.
-//   * The sequence's 16-token tiles stream through an LDS ring of three
-//     two-tile steps, two steps ahead of the one computed, moved from L2
-//     straight into LDS by direct loads (no registers). Each wave reads a
-//     step's K and V operands from LDS once and applies them to its 32 rows:
-//     a tile costs one L2 read per 128 rows. P.V contracts both tiles of a
-//     step in one 16x16x32 MFMA per 16 output columns.
-//   * Per 16-row block the arithmetic is decode's (TileMath): S^T = K . Q^T and
-//     O += P . V on MFMA, online softmax in log2 units with a lazily moved
-//     maximum. Tiles wholly before a row block's first position need no mask;
-//     the diagonal tiles mask key k > p per row by select; tiles after its last
-//     position are skipped.
+//   * The sequence's 16-token tiles stream through an LDS ring of two-tile
+//     steps (four stages for 16-bit and fp8 tiles), issued three steps ahead
+//     and moved from L2 straight into LDS by buffer loads (no registers).
+//     Each wave reads a step's K and V operands from LDS once and applies
+//     them to its 32 rows: a tile costs one L2 read per 128 rows.
+//   * Per 16-row block: S^T = K . Q^T and O^T = V^T . P^T on MFMA, so the
+//     query row is the MFMA column and every row statistic stays in the
+//     row's lanes; online softmax in log2 units with a lazily moved maximum.
+//     P^T . V contracts both tiles of a step in one 16x16x32 MFMA per 16
+//     output columns. Tiles wholly before a row block's first position need
+//     no mask; the diagonal tiles mask key k > p per row by select; tiles
+//     after its last position are skipped.
 //   * Workgroup index -> (sequence, row tile, KV head) with the KV head fastest,
 //     so the workgroups of one head land on one XCD (workgroups are dealt to
 //     the 8 XCDs round-robin) and share its L2; within a sequence the row
 //     tiles with the most keys start first.
+//
+// The same kernel in prefix mode is the prefix pass of the shared-prefix
+// decode (see the end of this file): a prefix group's member sequences take
+// the place of a chunk's tokens, every row sees every key of its part of the
+// shared prefix, and the result is merged with the suffix pass's.
 #include "pkv_internal.h"
 #include "pkv_tile.h"
 
@@ -96,6 +102,13 @@ struct PrefillParams {
     float qk_scale_log2;
     float v_scale;
     void* out;
+    // the prefix pass of the shared-prefix decode only
+    int num_groups;
+    const int32_t* group_starts;  // [num_groups + 1]
+    const int32_t* group_prefix;  // [num_groups]
+    float* slots;                 // [kPrefixSlots][prefix_slot_floats(D)]
+    const float* res_o;           // suffix results [S][H_q][D] and [S][H_q]
+    const float* res_lse;
 };
 
 // Row tiles of kGroupRows rows of a sequence (0 for an invalid chunk).
@@ -151,9 +164,25 @@ __device__ __forceinline__ void store4_as(void* base, size_t idx, float a, float
     }
 }
 
+// The prefix pass's common chunk count for groups whose rows fill rt_total
+// row tiles of 128 and rb_total row blocks of 16 (per KV head): about
+// kPrefixTargetWorkgroups workgroups, and the chunked groups' 16-row partials
+// within kPrefixSlots. Both kernels of the pass derive it the same way.
+__device__ __forceinline__ int prefix_chunks(int H, int rt_total, int rb_total) {
+    const int per_chunk = H * rt_total;
+    const int cg = per_chunk >= kPrefixTargetWorkgroups
+                       ? 1 : (kPrefixTargetWorkgroups + per_chunk - 1) / per_chunk;
+    return min(cg, max(1, kPrefixSlots / (H * rb_total)));
+}
+
 }  // namespace
 
-template <int KT, int QT, int D>
+// PFX = false: chunked prefill, one (sequence, row tile, KV head) per
+// workgroup, causal. PFX = true: the prefix pass of the shared-prefix decode
+// -- one (prefix group, row tile, KV head, chunk of the prefix blocks) per
+// workgroup, every row seeing every key of the chunk, the partial merged with
+// the suffix results.
+template <int KT, int QT, int D, bool PFX>
 __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void paged_prefill_kernel(PrefillParams p) {
     using TM = TileMath<KT, QT, D>;
@@ -176,39 +205,100 @@ void paged_prefill_kernel(PrefillParams p) {
     const int wv = wave_id();
     const int S = p.num_seqs, H = p.num_kv_heads, G = p.group, Hq = p.num_q_heads;
 
-    // ---- this workgroup's (sequence, row tile, KV head) ----
-    const int task = blockIdx.x;
-    int s = -1, local = 0;
-    {
+    // ---- this workgroup's task ----
+    // (row tiles of 128 rows stacked token-major, row = token * G + head; in
+    // the prefix pass a group's members take the place of the chunk's tokens)
+    int g = 0, q0 = 0, q_len = 0, n = 0, base_pos = 0, row_wg = 0, tiles = 0, tile0 = 0;
+    size_t bt_row = 0;
+    int pf_chunks = 1, pf_chunk = 0, rb_total = 0;  // prefix pass
+    int64_t pf_task16 = 0;
+    if constexpr (PFX) {
+        const int mb = p.max_blocks_per_seq;
+        const int ng = usable_groups(p.group_starts, p.group_prefix, p.num_groups, S, mb, lane);
+        if (ng == 0) return;
+        auto rows_of = [&](int j) {
+            return p.group_prefix[j] > 0 ? (p.group_starts[j + 1] - p.group_starts[j]) * G : 0;
+        };
+        // 16-row blocks and 128-row tiles over the groups with a prefix
+        int rt_total = 0;
+        for (int base = 0; base < ng; base += kWave) {
+            const int j = base + lane;
+            const int rows = j < ng ? rows_of(j) : 0;
+            rb_total += wave_sum_int((rows + 15) / 16);
+            rt_total += wave_sum_int((rows + kGroupRows - 1) / kGroupRows);
+        }
+        if (rt_total == 0) return;
+        const int cg = prefix_chunks(H, rt_total, rb_total);
+        // the group holding this workgroup (wave-uniform)
+        const int task = blockIdx.x;
+        int wg_before = 0;
+        int64_t t16_before = 0;
+        int jj = -1, local = 0;
+        for (int base = 0; base < ng; base += kWave) {
+            const int j = base + lane;
+            const int rows = j < ng ? rows_of(j) : 0;
+            const int cj = j < ng ? min(p.group_prefix[j], cg) : 0;
+            const int rts = (rows + kGroupRows - 1) / kGroupRows, rbs = (rows + 15) / 16;
+            const int wgs = H * rts * cj;
+            const int incl = wave_inclusive_scan(wgs, lane);
+            const int tincl = wave_inclusive_scan(H * rbs * cj, lane);
+            const unsigned long long hit =
+                __ballot(wgs > 0 && wg_before + incl - wgs <= task && task < wg_before + incl);
+            if (hit) {
+                const int L = __ffsll(hit) - 1;
+                jj = base + L;
+                local = task - wg_before - __builtin_amdgcn_readlane(incl - wgs, L);
+                pf_task16 = t16_before + __builtin_amdgcn_readlane(tincl - H * rbs * cj, L);
+                break;
+            }
+            wg_before += __builtin_amdgcn_readlane(incl, kWave - 1);
+            t16_before += __builtin_amdgcn_readlane(tincl, kWave - 1);
+        }
+        if (jj < 0) return;  // the grid is an upper bound on the tasks
+        const int pre = p.group_prefix[jj];
+        pf_chunks = min(pre, cg);
+        g = local % H;
+        pf_chunk = (local / H) % pf_chunks;
+        const int rt = local / H / pf_chunks;
+        q0 = p.group_starts[jj];
+        q_len = p.group_starts[jj + 1] - q0;
+        tile0 = (int)((int64_t)pf_chunk * pre / pf_chunks);
+        tiles = (int)((int64_t)(pf_chunk + 1) * pre / pf_chunks) - tile0;
+        n = tiles * kBlock;  // every prefix block is full
+        row_wg = rt * kGroupRows;
+        bt_row = (size_t)q0 * mb;  // the group's blocks: its first member's table
+    } else {
+        const int task = blockIdx.x;
+        int s = -1, local = 0;
         int before = 0;
         for (int base = 0; base < S; base += kWave) {
             const int ss = base + lane;
-            const int c = ss < S ? row_tiles(p, ss) * H : 0;
-            const int incl = wave_inclusive_scan(c, lane);
-            const unsigned long long hit = __ballot(c > 0 && before + incl - c <= task &&
+            const int cnt = ss < S ? row_tiles(p, ss) * H : 0;
+            const int incl = wave_inclusive_scan(cnt, lane);
+            const unsigned long long hit = __ballot(cnt > 0 && before + incl - cnt <= task &&
                                                     task < before + incl);
             if (hit) {
                 const int L = __ffsll(hit) - 1;
                 s = base + L;
-                local = task - before - __builtin_amdgcn_readlane(incl - c, L);
+                local = task - before - __builtin_amdgcn_readlane(incl - cnt, L);
                 break;
             }
             before += __builtin_amdgcn_readlane(incl, kWave - 1);
         }
+        if (s < 0) return;  // the grid is an upper bound on the tasks
+        g = local % H;
+        const int rt = row_tiles(p, s) - 1 - local / H;  // the longest row tiles first
+        q0 = p.query_start[s];
+        q_len = p.query_start[s + 1] - q0;
+        n = p.context_lens[s];
+        base_pos = n - q_len;  // position of the chunk's first token
+        row_wg = rt * kGroupRows;
+        const int last_row = min(q_len * G, row_wg + kGroupRows) - 1;
+        tiles = (base_pos + last_row / G) / kBlock + 1;  // keys 0 .. last position
+        bt_row = (size_t)s * p.max_blocks_per_seq;
     }
-    if (s < 0) return;  // the grid is an upper bound on the tasks
-    const int g = local % H;
-    const int rt = row_tiles(p, s) - 1 - local / H;  // the longest row tiles first
-    const int q0 = p.query_start[s];
-    const int q_len = p.query_start[s + 1] - q0;
-    const int n = p.context_lens[s];
     const int nrows = q_len * G;
-    const int base_pos = n - q_len;  // position of the chunk's first token
-    const int row_wg = rt * kGroupRows;
-    const int last_row = min(nrows, row_wg + kGroupRows) - 1;
-    const int tiles = (base_pos + last_row / G) / kBlock + 1;  // keys 0 .. last position
     const int steps = (tiles + 1) / 2;
-    const size_t bt_row = (size_t)s * p.max_blocks_per_seq;
 
     // The score scale in log2 units, made non-negative: a negative scale
     // flips the sign of q instead (exact), so that the running maximum can be
@@ -227,7 +317,9 @@ void paged_prefill_kernel(PrefillParams p) {
         const int row = row_w + rb * 16 + t;
         const bool ok = row < nrows;
         const int tok = ok ? row / G : q_len - 1;
-        pos[rb] = base_pos + tok;
+        // prefix pass: every row sees all keys of the chunk, as if it sat at
+        // the chunk's last key (so a stand-in second tile is masked)
+        pos[rb] = PFX ? n - 1 : base_pos + tok;
         const int h = g * G + (ok ? row % G : 0);
         TM::load_q(q[rb], p.q + ((size_t)(q0 + tok) * Hq + h) * D * QB, ok, g4);
 #pragma unroll
@@ -242,8 +334,8 @@ void paged_prefill_kernel(PrefillParams p) {
     for (int rb = 0; rb < kRowBlocks; ++rb) {
         const int r0 = row_w + rb * 16;
         const int r1 = min(nrows, r0 + 16) - 1;
-        rb_first[rb] = r0 < nrows ? base_pos + r0 / G : INT32_MAX;
-        rb_last[rb] = r0 < nrows ? base_pos + r1 / G : -1;
+        rb_first[rb] = r0 < nrows ? (PFX ? n - 1 : base_pos + r0 / G) : INT32_MAX;
+        rb_last[rb] = r0 < nrows ? (PFX ? n - 1 : base_pos + r1 / G) : -1;
         wave_last = max(wave_last, rb_last[rb]);
     }
 
@@ -303,8 +395,8 @@ void paged_prefill_kernel(PrefillParams p) {
     // issued and checked only then, so the scalar loads are not waited for
     // at once.
     auto step_ids = [&](int sp, int& ia, int& ib) {
-        ia = 2 * sp < tiles ? uniform_read(p.block_tables, bt_row + 2 * sp) : 0;
-        ib = 2 * sp + 1 < tiles ? uniform_read(p.block_tables, bt_row + 2 * sp + 1) : 0;
+        ia = 2 * sp < tiles ? uniform_read(p.block_tables, bt_row + tile0 + 2 * sp) : 0;
+        ib = 2 * sp + 1 < tiles ? uniform_read(p.block_tables, bt_row + tile0 + 2 * sp + 1) : 0;
     };
     auto checked = [&](int id) -> int {
         if (id < 0 || id >= p.num_blocks) {
@@ -632,22 +724,163 @@ void paged_prefill_kernel(PrefillParams p) {
 
     __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));  // no load into LDS outlives the workgroup
 
-    // ---- normalise and store: lane (t, g4) holds elements 16 j + 4 g4 .. + 3 of row t ----
+    // ---- lane (t, g4) holds elements 16 j + 4 g4 .. + 3 of row t ----
     const float nan = __builtin_nanf("");
+    if constexpr (PFX) {
+        // The prefix pass: merge with the suffix results (one chunk), or park
+        // the partial in the row block's slot.
+        constexpr int SLOT = prefix_slot_floats(D);
 #pragma unroll
-    for (int rb = 0; rb < kRowBlocks; ++rb) {
-        float lt = l_run[rb] + lane_fetch(x16, l_run[rb]);
-        lt += lane_fetch(x32, lt);
-        const float sc = bad ? nan : p.v_scale / lt;
-        const int row = row_w + rb * 16 + t;
-        if (row < nrows) {
-            const size_t orow = (size_t)(q0 + row / G) * Hq + g * G + row % G;
+        for (int rb = 0; rb < kRowBlocks; ++rb) {
+            const int r0 = row_w + rb * 16;
+            if (r0 >= nrows) continue;  // wave-uniform
+            const int rb16 = r0 / 16;
+            float lt = l_run[rb] + lane_fetch(x16, l_run[rb]);
+            lt += lane_fetch(x32, lt);  // weight sum of row t over the chunk
+            const float m = bad ? nan : m_run[rb];
+            const int row = r0 + t;
+            if (pf_chunks == 1) {
+                if (row < nrows) {
+                    const size_t orow = (size_t)(q0 + row / G) * Hq + g * G + row % G;
+                    const float lse = p.res_lse[orow];
+                    const float M = fmaxf(m, lse);
+                    const float wp = __builtin_amdgcn_exp2f(m - M);
+                    const float ws = __builtin_amdgcn_exp2f(lse - M);
+                    const float sc = p.v_scale / (wp * lt + ws);
+#pragma unroll
+                    for (int j = 0; j < NV; ++j) {
+                        const f32x4_t so = *reinterpret_cast<const f32x4_t*>(p.res_o + orow * D + 16 * j + 4 * g4);
+                        store4_as<QT>(p.out, orow * D + 16 * j + 4 * g4, (wp * o[rb][j][0] + ws * so[0]) * sc,
+                                      (wp * o[rb][j][1] + ws * so[1]) * sc, (wp * o[rb][j][2] + ws * so[2]) * sc,
+                                      (wp * o[rb][j][3] + ws * so[3]) * sc);
+                    }
+                }
+                continue;
+            }
+            // several chunks: the partial goes to its slot; the merge launch
+            // that follows combines the chunks
+            const int64_t f = pf_task16 + (int64_t)rb16 * (H * pf_chunks) + g * pf_chunks + pf_chunk;
+            float* slotp = p.slots + (size_t)f * SLOT;
 #pragma unroll
             for (int j = 0; j < NV; ++j)
-                store4_as<QT>(p.out, orow * D + 16 * j + 4 * g4, o[rb][j][0] * sc, o[rb][j][1] * sc,
-                              o[rb][j][2] * sc, o[rb][j][3] * sc);
+                *reinterpret_cast<f32x4_t*>(slotp + t * D + 16 * j + 4 * g4) = o[rb][j];
+            if (g4 == 0) {
+                slotp[16 * D + t] = m;
+                slotp[16 * D + 16 + t] = lt;
+            }
+        }
+    } else {
+        // normalise and store
+#pragma unroll
+        for (int rb = 0; rb < kRowBlocks; ++rb) {
+            float lt = l_run[rb] + lane_fetch(x16, l_run[rb]);
+            lt += lane_fetch(x32, lt);
+            const float sc = bad ? nan : p.v_scale / lt;
+            const int row = row_w + rb * 16 + t;
+            if (row < nrows) {
+                const size_t orow = (size_t)(q0 + row / G) * Hq + g * G + row % G;
+#pragma unroll
+                for (int j = 0; j < NV; ++j)
+                    store4_as<QT>(p.out, orow * D + 16 * j + 4 * g4, o[rb][j][0] * sc, o[rb][j][1] * sc,
+                                  o[rb][j][2] * sc, o[rb][j][3] * sc);
+            }
         }
     }
+}
+
+// The merge launch of the prefix pass: one workgroup of 256 threads per
+// (16-row block, KV head) of the groups whose prefix was split into chunks;
+// thread i takes row i / 16 of the block and elements (i % 16) * D / 16 ..
+// of it. With the block's slots f0 .. f0 + C - 1 (as the prefix kernel
+// placed them) and the suffix result (o_s, lse_s) of the row:
+//   M = max(m_1..m_C, lse_s),
+//   out = v_scale * (sum_c 2^(m_c - M) acc_c + 2^(lse_s - M) o_s)
+//                  / (sum_c 2^(m_c - M) l_c + 2^(lse_s - M)).
+constexpr int kMergeThreads = 256;
+
+template <int QT, int D>
+__global__ __launch_bounds__(kMergeThreads) void prefix_merge_kernel(PrefillParams p) {
+    constexpr int SLOT = prefix_slot_floats(D);
+    constexpr int EPT = D / 16;  // elements per thread: 8 (d 128) or 4 (d 64)
+    const int lane = lane_id();
+    const int S = p.num_seqs, H = p.num_kv_heads, G = p.group, Hq = p.num_q_heads;
+    const int ng = usable_groups(p.group_starts, p.group_prefix, p.num_groups, S,
+                                 p.max_blocks_per_seq, lane);
+    if (ng == 0) return;
+    auto rows_of = [&](int j) {
+        return p.group_prefix[j] > 0 ? (p.group_starts[j + 1] - p.group_starts[j]) * G : 0;
+    };
+    int rt_total = 0, rb_total = 0;
+    for (int base = 0; base < ng; base += kWave) {
+        const int j = base + lane;
+        const int rows = j < ng ? rows_of(j) : 0;
+        rb_total += wave_sum_int((rows + 15) / 16);
+        rt_total += wave_sum_int((rows + kGroupRows - 1) / kGroupRows);
+    }
+    if (rt_total == 0) return;
+    const int cg = prefix_chunks(H, rt_total, rb_total);
+    if (cg == 1) return;  // every group was merged by the prefix kernel
+    const int g = blockIdx.x % H;
+    const int rbg = blockIdx.x / H;  // 16-row block over all groups
+    if (rbg >= rb_total) return;
+    // the block's group (every wave finds the same)
+    int rb_before = 0, jj = -1, rb16 = 0;
+    int64_t t16_before = 0, t16 = 0;
+    for (int base = 0; base < ng && jj < 0; base += kWave) {
+        const int j = base + lane;
+        const int rows = j < ng ? rows_of(j) : 0;
+        const int cj = j < ng ? min(p.group_prefix[j], cg) : 0;
+        const int rbs = (rows + 15) / 16;
+        const int rincl = wave_inclusive_scan(rbs, lane);
+        const int tincl = wave_inclusive_scan(H * rbs * cj, lane);
+        const unsigned long long hit =
+            __ballot(rbs > 0 && rb_before + rincl - rbs <= rbg && rbg < rb_before + rincl);
+        if (hit) {
+            const int L = __ffsll(hit) - 1;
+            jj = base + L;
+            rb16 = rbg - rb_before - __builtin_amdgcn_readlane(rincl - rbs, L);
+            t16 = t16_before + __builtin_amdgcn_readlane(tincl - H * rbs * cj, L);
+        }
+        rb_before += __builtin_amdgcn_readlane(rincl, kWave - 1);
+        t16_before += __builtin_amdgcn_readlane(tincl, kWave - 1);
+    }
+    if (jj < 0) return;  // not reached for rbg < rb_total
+    const int C = min(p.group_prefix[jj], cg);
+    if (C <= 1) return;  // merged by the prefix kernel
+    const int r = threadIdx.x >> 4, e0 = (threadIdx.x & 15) * EPT;
+    const int row = rb16 * 16 + r;
+    if (row >= rows_of(jj)) return;
+    const size_t orow = (size_t)(p.group_starts[jj] + row / G) * Hq + g * G + row % G;
+    const float* slot0 = p.slots + (size_t)(t16 + (int64_t)rb16 * (H * C) + g * C) * SLOT;
+    const float lse = p.res_lse[orow];
+    float M = lse;
+    for (int cc = 0; cc < C; ++cc) M = fmaxf(M, slot0[(size_t)cc * SLOT + 16 * D + r]);
+    const float ws = __builtin_amdgcn_exp2f(lse - M);
+    float L = ws;
+    float acc[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; i += 4) {
+        const f32x4_t so = *reinterpret_cast<const f32x4_t*>(p.res_o + orow * D + e0 + i);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) acc[i + x] = ws * so[x];
+    }
+#pragma unroll 4
+    for (int cc = 0; cc < C; ++cc) {
+        const float* sl = slot0 + (size_t)cc * SLOT;
+        const float w = __builtin_amdgcn_exp2f(sl[16 * D + r] - M);
+        L += w * sl[16 * D + 16 + r];
+#pragma unroll
+        for (int i = 0; i < EPT; i += 4) {
+            const f32x4_t a = *reinterpret_cast<const f32x4_t*>(sl + r * D + e0 + i);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) acc[i + x] = fmaf(w, a[x], acc[i + x]);
+        }
+    }
+    const float sc = p.v_scale / L;
+#pragma unroll
+    for (int i = 0; i < EPT; i += 4)
+        store4_as<QT>(p.out, orow * D + e0 + i, acc[i] * sc, acc[i + 1] * sc, acc[i + 2] * sc,
+                      acc[i + 3] * sc);
 }
 
 // ---- dispatch ------------------------------------------------------------------
@@ -659,7 +892,7 @@ int64_t prefill_task_bound(int num_seqs, int num_tokens, int group, int num_kv_h
 
 template <int KT, int QT, int D>
 static hipError_t launch_prefill_typed(const PrefillArgs& a) {
-    PrefillParams p;
+    PrefillParams p{};
     p.q = static_cast<const uint8_t*>(a.q);
     p.k_cache = static_cast<const uint8_t*>(a.k_cache);
     p.v_cache = static_cast<const uint8_t*>(a.v_cache);
@@ -678,7 +911,7 @@ static hipError_t launch_prefill_typed(const PrefillArgs& a) {
     p.out = a.out;
     const int64_t grid = prefill_task_bound(a.num_seqs, a.num_tokens, a.group, a.num_kv_heads);
     if (grid <= 0) return hipSuccess;
-    auto kernel = paged_prefill_kernel<KT, QT, D>;
+    auto kernel = paged_prefill_kernel<KT, QT, D, false>;
     hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kPrefillThreads), 0, a.stream, p);
     return hipGetLastError();
 }
@@ -694,6 +927,71 @@ hipError_t launch_paged_prefill(const PrefillArgs& a) {
     if (a.kv_dtype == PKV_BF16) return launch_prefill_dim<PKV_BF16, PKV_BF16>(a);
     if (a.q_dtype == PKV_F16) return launch_prefill_dim<PKV_FP8_E4M3, PKV_F16>(a);
     return launch_prefill_dim<PKV_FP8_E4M3, PKV_BF16>(a);
+}
+
+// ---- the shared-prefix decode -------------------------------------------------
+//
+// Sequences that share a prefix reference one physical copy of its blocks
+// (drpranayjha page, "How PagedAttention pages the KV cache"; ttlab page,
+// section 4). Plain paged decode still reads such a block once per sequence.
+// Here the suffix pass (the decode kernel in result mode, over each member's
+// blocks after its group's prefix) leaves every member row's normalised
+// output and log2-sum-exp in the workspace; the prefix pass is the kernel
+// above in prefix mode: a group's (member, query head) rows are stacked like
+// a prefill chunk's (token, head) rows, 128 to a workgroup, against the
+// group's prefix blocks read once per workgroup through LDS. The prefix is
+// split into chunks so that about kPrefixTargetWorkgroups workgroups run;
+// chunk partials (16-row slots) are merged by a third launch, by the
+// log-sum-exp rule, together with the suffix result.
+
+template <int KT, int QT, int D>
+static hipError_t launch_prefix_typed(const DecodeArgs& a) {
+    PrefillParams p{};
+    p.q = static_cast<const uint8_t*>(a.q);
+    p.k_cache = static_cast<const uint8_t*>(a.k_cache);
+    p.v_cache = static_cast<const uint8_t*>(a.v_cache);
+    p.block_tables = a.block_tables;
+    p.num_seqs = a.num_seqs;
+    p.num_q_heads = a.num_q_heads;
+    p.num_kv_heads = a.num_kv_heads;
+    p.group = a.group;
+    p.num_blocks = a.num_blocks;
+    p.max_blocks_per_seq = a.max_blocks_per_seq;
+    p.qk_scale_log2 = a.scale * (KT == PKV_FP8_E4M3 ? a.k_scale : 1.f) * 1.44269504088896340736f;
+    p.v_scale = KT == PKV_FP8_E4M3 ? a.v_scale : 1.f;
+    p.out = a.out;
+    p.num_groups = a.num_groups;
+    p.group_starts = a.group_starts;
+    p.group_prefix = a.group_prefix;
+    p.slots = a.prefix_slots;
+    p.res_o = a.res_o;
+    p.res_lse = a.res_lse;
+    const int64_t grid = prefix_workgroup_bound(a.num_seqs, a.group, a.num_kv_heads, a.num_groups);
+    auto kernel = paged_prefill_kernel<KT, QT, D, true>;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kPrefillThreads), 0, a.stream, p);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int64_t merge_grid =
+        (int64_t)a.num_kv_heads * prefix_row_blocks_bound(a.num_seqs, a.group, a.num_groups);
+    auto merge = prefix_merge_kernel<QT, D>;
+    hipLaunchKernelGGL(merge, dim3((unsigned)merge_grid), dim3(kMergeThreads), 0, a.stream, p);
+    return hipGetLastError();
+}
+
+template <int KT, int QT>
+static hipError_t launch_prefix_dim(const DecodeArgs& a) {
+    return a.head_dim == 64 ? launch_prefix_typed<KT, QT, 64>(a) : launch_prefix_typed<KT, QT, 128>(a);
+}
+
+hipError_t launch_shared_prefix(const DecodeArgs& a) {
+    // the suffix pass (decode kernel, result mode), then the prefix pass
+    hipError_t err = launch_paged_decode(a);
+    if (err != hipSuccess) return err;
+    if (a.kv_dtype == PKV_F32) return launch_prefix_dim<PKV_F32, PKV_F32>(a);
+    if (a.kv_dtype == PKV_F16) return launch_prefix_dim<PKV_F16, PKV_F16>(a);
+    if (a.kv_dtype == PKV_BF16) return launch_prefix_dim<PKV_BF16, PKV_BF16>(a);
+    if (a.q_dtype == PKV_F16) return launch_prefix_dim<PKV_FP8_E4M3, PKV_F16>(a);
+    return launch_prefix_dim<PKV_FP8_E4M3, PKV_BF16>(a);
 }
 
 }  // namespace pkv

@@ -230,7 +230,6 @@ PKV_EXPORT int pkv_paged_attention_decode_shared_prefix(
         a.res_o = reinterpret_cast<float*>(ws + l.res_o);
         a.res_lse = reinterpret_cast<float*>(ws + l.res_lse);
         a.prefix_slots = reinterpret_cast<float*>(ws + l.prefix_slots);
-        a.prefix_counters = reinterpret_cast<int*>(ws + dctr - l.prefix_counter_bytes);
         err = pkv::launch_shared_prefix(a);
     }
     return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;

@@ -45,9 +45,13 @@ inline size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_h
 inline size_t tail_offset(size_t ws_bytes, size_t bytes) { return (ws_bytes & ~(size_t)255) - bytes; }
 
 // ---- shared-prefix decode ----------------------------------------------------
-// The prefix pass aims at about this many tasks (KV head x row block of 16
-// query rows x chunk of the prefix): four waves per CU of a 256-CU device.
-constexpr int kPrefixTargetTasks = 1024;
+// The prefix pass runs workgroups of 128 (member, query head) rows of one
+// prefix group and KV head over one chunk of the prefix blocks; the chunk
+// count aims at this many workgroups.
+constexpr int kPrefixTargetWorkgroups = 512;
+// Partial slots of 16 rows in the workspace. The chunk count is capped so
+// that the slots of chunked groups fit; an unchunked group needs none.
+constexpr int kPrefixSlots = 4096;
 
 // One prefix partial: accumulators [16 rows][D], then 16 maxima and 16 sums.
 constexpr int prefix_slot_floats(int d) { return 16 * d + 32; }
@@ -56,20 +60,20 @@ constexpr int prefix_slot_floats(int d) { return 16 * d + 32; }
 inline int64_t prefix_row_blocks_bound(int num_seqs, int group, int num_groups) {
     return ((int64_t)num_seqs * group + 15) / 16 + num_groups;
 }
-// Prefix tasks, at most: H * row blocks with one chunk, else fewer than
-// 2 * target (the chunk count is ceil(target / (H * row blocks))).
-inline int64_t prefix_task_bound(int num_seqs, int group, int num_kv_heads, int num_groups) {
-    const int64_t one = (int64_t)num_kv_heads * prefix_row_blocks_bound(num_seqs, group, num_groups);
-    return one > 2 * kPrefixTargetTasks ? one : 2 * kPrefixTargetTasks;
+// Prefix workgroups, at most: H * (128-row tiles) with one chunk; with more
+// chunks (ceil(target / (H * tiles)) of them) fewer than target + H * tiles.
+inline int64_t prefix_workgroup_bound(int num_seqs, int group, int num_kv_heads, int num_groups) {
+    const int64_t tiles = ((int64_t)num_seqs * group + 127) / 128 + num_groups;
+    return (int64_t)num_kv_heads * tiles + kPrefixTargetWorkgroups;
 }
 
 // Byte offsets in the shared-prefix workspace. Front: the suffix pass's
 // decode slots, the float32 suffix results [S][H_q][D] and [S][H_q], and
-// 2 * target prefix partial slots. End: the prefix pass's counters
-// [H_kv][row blocks], then the suffix pass's counters [S][H_kv].
+// kPrefixSlots prefix partial slots. End: the suffix pass's counters
+// [S][H_kv].
 struct SharedPrefixLayout {
     size_t res_o, res_lse, prefix_slots, floats;   // float part (from the start)
-    size_t prefix_counter_bytes, decode_counter_bytes;
+    size_t decode_counter_bytes;
     size_t total;
 };
 inline SharedPrefixLayout shared_prefix_layout(int num_seqs, int num_q_heads, int num_kv_heads,
@@ -81,13 +85,10 @@ inline SharedPrefixLayout shared_prefix_layout(int num_seqs, int num_q_heads, in
     l.res_lse = off;
     off += round256((size_t)num_seqs * num_q_heads * sizeof(float));
     l.prefix_slots = off;
-    off += round256((size_t)2 * kPrefixTargetTasks * prefix_slot_floats(head_dim) * sizeof(float));
+    off += round256((size_t)kPrefixSlots * prefix_slot_floats(head_dim) * sizeof(float));
     l.floats = off;
-    l.prefix_counter_bytes = round256(
-        (size_t)num_kv_heads * prefix_row_blocks_bound(num_seqs, num_q_heads / num_kv_heads, num_groups) *
-        sizeof(int32_t));
     l.decode_counter_bytes = decode_counter_bytes(num_seqs, num_kv_heads);
-    l.total = l.floats + l.prefix_counter_bytes + l.decode_counter_bytes;
+    l.total = l.floats + l.decode_counter_bytes;
     return l;
 }
 
@@ -122,7 +123,6 @@ struct DecodeArgs {
     const int32_t* group_prefix = nullptr;  // [num_groups] (device)
     float* res_o = nullptr;                 // [S][H_q][D]
     float* res_lse = nullptr;               // [S][H_q]
-    int* prefix_counters = nullptr;         // prefix pass: [H_kv][row blocks], zero on entry
     float* prefix_slots = nullptr;          // prefix pass: partial slots
 };
 

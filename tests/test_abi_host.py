@@ -149,11 +149,10 @@ def test_shared_prefix_workspace_bytes_formula():
     S, Hq, H, d, ng, W = 256, 32, 8, 128, 3, 768
     base = B.pkv_decode_workspace_bytes(S, Hq, H, d, W)  # decode slots + decode counters
     res = r256(S * Hq * d * 4) + r256(S * Hq * 4)
-    ctr = r256(H * (-(-S * (Hq // H) // 16) + ng) * 4)
-    slots = r256(2 * 1024 * (16 * d + 32) * 4)
-    assert B.pkv_shared_prefix_workspace_bytes(S, Hq, H, d, ng, W) == base + res + ctr + slots
+    slots = r256(4096 * (16 * d + 32) * 4)
+    assert B.pkv_shared_prefix_workspace_bytes(S, Hq, H, d, ng, W) == base + res + slots
     assert B.pkv_shared_prefix_workspace_bytes(S, Hq, H, d, ng, 0) == \
-        B.pkv_decode_workspace_bytes(S, Hq, H, d, 0) + res + ctr + slots
+        B.pkv_decode_workspace_bytes(S, Hq, H, d, 0) + res + slots
     assert B.pkv_shared_prefix_workspace_bytes(S, Hq, H, d, -1, W) == 0
     assert B.pkv_shared_prefix_workspace_bytes(S, Hq, H, d, S + 1, W) == 0
     assert B.pkv_shared_prefix_workspace_bytes(4, 18, 2, 64, 1, 1) == 0  # G = 9
