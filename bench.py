@@ -16,12 +16,16 @@ kernel (the decode kernel, one launch per layer) timed with HIP events on the
 stream it runs on, plus the CPU oracle timed on a bounded sample of the same
 workload on this host's cores.
 
-Other workloads (--workload qwen|prefix|prefix_shared|fp8|tiny) time the
-decode call alone and print the same fields; they are for profiling, not the
-headline line. prefix_shared is the prefix workload through the shared-prefix
-decode (each shared block read once per KV head): its value and roofline
-count the unique KV bytes (the shared prefix once, every suffix), and it also
-reports the logical bytes plain decode would read.
+Other workloads (--workload gqa40_tp8|qwen|prefix|prefix_shared|fp8|tiny)
+print the same fields; they are for profiling, not the headline line.
+gqa40_tp8 is the same 40-layer step at one GPU's share under 8-way KV-head
+parallelism (4 query / 1 KV head). The others time the decode call alone.
+prefix_shared is the prefix workload through the shared-prefix decode (each
+shared block read once per KV head): its value and roofline count the unique
+KV bytes (the shared prefix once, every suffix), and it also reports the
+logical bytes plain decode would read. --cold adds launches timed after a
+1 GiB write that evicts the caches (a small layer such as qwen's otherwise
+stays in the 256 MB MALL between iterations).
 """
 import argparse
 import json
@@ -53,9 +57,14 @@ def parse():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gqa40",
-                    choices=["gqa40", "qwen", "prefix", "prefix_shared", "fp8", "tiny", "prefill"])
+                    choices=["gqa40", "gqa40_tp8", "qwen", "prefix", "prefix_shared", "fp8", "tiny",
+                             "prefill"])
     ap.add_argument("--workers", type=int, default=0, help="worker waves (0 = fill the device)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time decode launches that each follow a 1 GiB device write, "
+                         "which evicts the L2 caches and the 256 MB MALL (the timed launch then "
+                         "reads its KV from HBM)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -107,6 +116,8 @@ def build_layers(workload: str, device):
     from paged_kv_cache_101_amd import workloads as W
     if workload == "gqa40":
         layers = [W.gqa40_layer(device=device, layer=l, append_last=True) for l in range(40)]
+    elif workload == "gqa40_tp8":
+        layers = [W.gqa40_tp8_layer(device=device, layer=l, append_last=True) for l in range(40)]
     elif workload == "qwen":
         layers = [W.qwen_layer(device=device)]
     elif workload in ("prefix", "prefix_shared"):
@@ -123,6 +134,8 @@ def describe(workload: str, layers, workers: int) -> dict:
     return {
         "workload": {
             "gqa40": "40-layer GQA decode step: 40 layers x 40 seqs x 8192 ctx",
+            "gqa40_tp8": "40-layer GQA decode step, one GPU's share under 8-way head "
+                         "parallelism: 40 layers x 40 seqs x 8192 ctx, 4 query / 1 KV head",
             "qwen": "Qwen2.5-1.5B-shaped layer decode: 64 seqs, ctx U[128,4096]",
             "prefix": "prefix sharing decode: 256 seqs, 2048 shared + U[64,512] ctx",
             "prefix_shared": "prefix sharing decode, shared-prefix path: 256 seqs, "
@@ -305,9 +318,20 @@ def main():
     else:
         ws = B.decode_workspace(b0.num_seqs, b0.num_q_heads, b0.num_kv_heads, b0.head_dim,
                                 args.workers, dev)
-    do_append = args.workload == "gqa40"
+    do_append = args.workload in ("gqa40", "gqa40_tp8")
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
+
+    def decode(i):
+        b = layers[i]
+        if shared:
+            B.pkv_paged_attention_decode_shared_prefix(
+                b.q, *caches[i], descs[i], b.block_tables, b.context_lens, b.group_starts,
+                b.group_prefix, b.scale, outs[i], num_workers=args.workers, workspace=ws)
+        else:
+            B.pkv_paged_attention_decode(b.q, *caches[i], descs[i], b.block_tables,
+                                         b.context_lens, b.scale, outs[i],
+                                         num_workers=args.workers, workspace=ws)
 
     def step(evs=None):
         for i, b in enumerate(layers):
@@ -315,14 +339,7 @@ def main():
                 B.pkv_kv_append(b.new_k, b.new_v, b.slot_mapping, *caches[i], descs[i])
             if evs is not None:
                 evs[i][0].record(stream)
-            if shared:
-                B.pkv_paged_attention_decode_shared_prefix(
-                    b.q, *caches[i], descs[i], b.block_tables, b.context_lens, b.group_starts,
-                    b.group_prefix, b.scale, outs[i], num_workers=args.workers, workspace=ws)
-            else:
-                B.pkv_paged_attention_decode(b.q, *caches[i], descs[i], b.block_tables,
-                                             b.context_lens, b.scale, outs[i],
-                                             num_workers=args.workers, workspace=ws)
+            decode(i)
             if evs is not None:
                 evs[i][1].record(stream)
 
@@ -370,6 +387,29 @@ def main():
         "launch_p10_us": round(sorted(decode_ms)[len(decode_ms) // 10] * 1e3, 2),
         "launch_p90_us": round(sorted(decode_ms)[(9 * len(decode_ms)) // 10] * 1e3, 2),
     }
+    cold = None
+    if args.cold:
+        # a 1 GiB write before every decode launch, outside its events
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        cold_ms = []
+        for s in range(args.steps):
+            for i in range(len(layers)):
+                scratch.fill_(s & 0xFF)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                decode(i)
+                e1.record(stream)
+                cold_ms.append((e0, e1))
+        torch.cuda.synchronize()
+        cms = sorted(a.elapsed_time(b) for a, b in cold_ms)
+        cavg = statistics.fmean(cms)
+        del scratch
+        cold = {"launch_avg_us": round(cavg * 1e3, 2),
+                "launch_p10_us": round(cms[len(cms) // 10] * 1e3, 2),
+                "launch_p90_us": round(cms[(9 * len(cms)) // 10] * 1e3, 2),
+                "achieved_gbps": round(kv_bytes_launch / (cavg * 1e-3) / 1e9, 1),
+                "frac": round(kv_bytes_launch / (cavg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(b0, args.cpu_seconds)
@@ -384,6 +424,8 @@ def main():
         "kv_bytes_per_step": kv_bytes_step,
         "roofline": roofline, "cpu_baseline": cpu,
     }
+    if cold is not None:
+        line["cold"] = cold
     if shared:
         line["logical_kv_bytes_per_launch"] = logical_launch
         line["logical_kv_gbps"] = round(logical_launch / (decode_avg_ms * 1e-3) / 1e9, 1)

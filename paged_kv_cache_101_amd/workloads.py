@@ -332,6 +332,16 @@ def gqa40_layer(device="cpu", layer=0, num_seqs=40, ctx=8192, canary=False,
                       layer=layer, canary=canary, append_last=append_last, structure_layer=0)
 
 
+def gqa40_tp8_layer(device="cpu", layer=0, num_seqs=40, ctx=8192, canary=False,
+                    append_last=False) -> DecodeBatch:
+    """One GPU's share of a layer of the 40-layer GQA shape when its 8 KV heads
+    are split over 8 GPUs (tensor parallel over heads): 4 query / 1 KV head,
+    d 128, fp16 KV, 40 sequences of 8192 tokens; all layers share one block
+    table."""
+    return make_batch("gqa40-8k-tp8", 6, [ctx] * num_seqs, 4, 1, 128, "f16", "f16", device=device,
+                      layer=layer, canary=canary, append_last=append_last, structure_layer=0)
+
+
 def prefix_shared_lengths(num_seqs=256, prefix=2048, lo=64, hi=512, case_id=4):
     rng = np.random.default_rng([case_id, 0, 0])
     suf = rng.integers(lo, hi + 1, size=num_seqs)

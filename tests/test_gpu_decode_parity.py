@@ -74,6 +74,14 @@ def test_gqa40_full_layer_sampled(gpu):
     _check(W.gqa40_layer(device=gpu, layer=3), seqs=[0, 17, 39], what="gqa40 full (sampled)")
 
 
+def test_gqa40_tp8_share_sampled(gpu):
+    """One GPU's share of the 40-layer workload under 8-way KV-head
+    parallelism (40 x 8192, 4 query / 1 KV head, fp16), the bench's gqa40_tp8
+    layer at full size; the oracle recomputes sequences 0, 21 and 39."""
+    _check(W.gqa40_tp8_layer(device=gpu, layer=5, canary=True), seqs=[0, 21, 39],
+           what="gqa40 tp8 share (sampled)")
+
+
 def test_prefix_shared_reduced(gpu):
     _check(W.prefix_shared(device=gpu, num_seqs=24, canary=True), what="prefix 24 seqs")
 

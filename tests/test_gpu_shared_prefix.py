@@ -7,8 +7,8 @@ sequence's own block table, shared blocks included) and the bar is the
 decode tolerance. Cases cover several groups with different prefix lengths,
 sequences outside every group, a one-member group, a group with no shared
 blocks, a member whose context is exactly its prefix (empty suffix), both
-prefix-pass merge paths (one chunk per row block, and several chunks parked
-in the workspace), every supported cache type and head grouping, an unusable
+prefix-pass merge paths (one chunk per row block, merged in registers, and
+several chunks combined by the merge launch), every supported cache type and head grouping, an unusable
 group description (ignored: the plain result), and a member too short to
 hold its prefix (NaN rows)."""
 import numpy as np
@@ -84,8 +84,9 @@ def test_prefix_workload_reduced(gpu):
 
 
 def test_one_chunk_merge_path(gpu):
-    """Many rows (300 members x 8 heads per KV head): one chunk per row block,
-    merged from registers; and P = 1 groups, which cannot be split."""
+    """A large group (300 members x 8 heads per KV head, split into chunks that
+    the merge launch combines) beside a P = 1 group, which cannot be split and
+    is merged from registers by the prefix kernel."""
     rng = np.random.default_rng(54)
     groups = [(0, 300, 3), (300, 310, 1)]
     ctx = grouped_lengths(rng, 310, groups, 1, 40)
@@ -93,6 +94,19 @@ def test_one_chunk_merge_path(gpu):
                      prefix_groups=groups, canary=True)
     got = out_to_f64(gpu_shared_decode(b))
     assert_close(got, oracle_decode(b), "bf16", "one chunk")
+
+
+def test_no_group_is_chunked(gpu):
+    """1024 members x 8 heads per KV head fill 64 row tiles per head, 512
+    workgroups at one chunk each: every row is merged from registers and the
+    merge launch has nothing to do."""
+    rng = np.random.default_rng(57)
+    groups = [(0, 1024, 2)]
+    ctx = grouped_lengths(rng, 1024, groups, 1, 24)
+    b = W.make_batch("no-chunks", 57, ctx, 64, 8, 64, "bf16", "bf16", device=gpu,
+                     prefix_groups=groups, canary=True)
+    got = out_to_f64(gpu_shared_decode(b))
+    assert_close(got, oracle_decode(b), "bf16", "one chunk everywhere")
 
 
 def test_prefix_workload_full_size(gpu):
