@@ -49,6 +49,13 @@ MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "fp8": 2500.0, "f32": 157.3}
 # in the 40-layer GQA head shape.
 PREFILL_CONTEXTS = [2048, 4096, 6144, 8192]
 PREFILL_CHUNK = 2048
+# Few-row prefill: 16-token chunks (a chunked prefill's tail, or a few draft
+# tokens checked at once) of eight sequences at 8192-token contexts. Each KV
+# head has one 128-row tile per sequence, so the keys are split over
+# workgroups (the prefill workspace); the step reads each sequence's KV once
+# and is bound by HBM.
+PREFILL_SMALL_CONTEXTS = [8192] * 8
+PREFILL_SMALL_CHUNK = 16
 
 
 def parse():
@@ -58,7 +65,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gqa40",
                     choices=["gqa40", "gqa40_tp8", "qwen", "prefix", "prefix_shared", "fp8", "tiny",
-                             "prefill"])
+                             "prefill", "prefill_small"])
     ap.add_argument("--workers", type=int, default=0, help="worker waves (0 = fill the device)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold", action="store_true",
@@ -201,36 +208,43 @@ def bench_prefill(args):
 
     dev = torch.device("cuda:0")
     Hq, H, d, dt = 32, 8, 128, "f16"
-    b = W.make_batch("prefill-step", 6, PREFILL_CONTEXTS, Hq, H, d, dt, dt, device=dev)
+    small = args.workload == "prefill_small"
+    contexts = PREFILL_SMALL_CONTEXTS if small else PREFILL_CONTEXTS
+    chunk = PREFILL_SMALL_CHUNK if small else PREFILL_CHUNK
+    b = W.make_batch("prefill-small" if small else "prefill-step", 8 if small else 6, contexts, Hq, H,
+                     d, dt, dt, device=dev)
     desc = B.desc_for(b.k_cache, dt)
     kc, vc = B.fill_cache(b.k_cache, b.v_cache, desc)
-    S = len(PREFILL_CONTEXTS)
-    T = S * PREFILL_CHUNK
+    S = len(contexts)
+    T = S * chunk
     g = torch.Generator(device=dev)
     g.manual_seed(66)
     q = torch.randn((T, Hq, d), generator=g, device=dev).to(torch.float16)
-    qs = torch.arange(0, T + 1, PREFILL_CHUNK, dtype=torch.int32, device=dev)
+    qs = torch.arange(0, T + 1, chunk, dtype=torch.int32, device=dev)
     out = torch.empty_like(q)
+    ws = B.prefill_workspace(d, dev)
     stream = torch.cuda.current_stream()
 
-    def step():
-        B.pkv_paged_attention_prefill(q, kc, vc, desc, b.block_tables, b.context_lens, qs,
-                                      b.scale, out)
+    def timed(workspace):
+        def step():
+            B.pkv_paged_attention_prefill(q, kc, vc, desc, b.block_tables, b.context_lens, qs,
+                                          b.scale, out, workspace=workspace)
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            step()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return statistics.fmean(a.elapsed_time(c) for a, c in evs)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for e0, e1 in evs:
-        e0.record(stream)
-        step()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    ms = [a.elapsed_time(c) for a, c in evs]
-    avg = statistics.fmean(ms)
-    flops = prefill_flops(PREFILL_CONTEXTS, PREFILL_CHUNK, Hq, d)
+    avg = timed(ws)
+    flops = prefill_flops(contexts, chunk, Hq, d)
     tflops = flops / (avg * 1e-3) / 1e12
+    kv_bytes = sum(contexts) * H * 2 * d * 2  # each sequence's K and V, read once per KV head
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -240,16 +254,16 @@ def bench_prefill(args):
         qh = W.to_numpy(q)
         k = 1
         while True:
-            rows = np.arange(T - PREFILL_CHUNK, T - PREFILL_CHUNK + k)
-            pos = cl[-1] - PREFILL_CHUNK + (rows - (T - PREFILL_CHUNK))
+            rows = np.arange(T - chunk, T - chunk + k)
+            pos = cl[-1] - chunk + (rows - (T - chunk))
             t0 = time.perf_counter()
             oracle.paged_prefill(np.ascontiguousarray(qh[rows]), kh, vh,
                                  np.ascontiguousarray(bt[[S - 1] * k]), (pos + 1).astype(np.int32),
                                  np.arange(k + 1, dtype=np.int32), b.scale)
             el = time.perf_counter() - t0
-            if el > args.cpu_seconds / 4 or k >= PREFILL_CHUNK:
+            if el > args.cpu_seconds / 4 or k >= chunk:
                 break
-            k = min(PREFILL_CHUNK, k * 4)
+            k = min(chunk, k * 4)
         sample_flops = 4 * d * Hq * int((pos + 1).sum())
         cpu = {"value": round(sample_flops / el / 1e12, 6), "unit": "TFLOP/s",
                "cores": oracle.num_threads(), "kind": "oracle",
@@ -260,17 +274,26 @@ def bench_prefill(args):
         "value": round(tflops, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(avg, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": dt, "data": "synthetic",
-        "config": {"workload": f"chunked prefill: {S} sequences x {PREFILL_CHUNK}-token chunks "
-                               f"at contexts {PREFILL_CONTEXTS}", "q_heads": Hq, "kv_heads": H,
+        "config": {"workload": f"chunked prefill: {S} sequences x {chunk}-token chunks "
+                               f"at contexts {contexts}", "q_heads": Hq, "kv_heads": H,
                    "head_dim": d, "kv_dtype": dt, "block_size": 16},
-        "flops_per_step": flops,
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
-                     "peak": MFMA_PEAK_TFLOPS[dt], "unit": "TFLOP/s",
-                     "frac": round(tflops / MFMA_PEAK_TFLOPS[dt], 4), "traffic": None,
-                     "kernel": "paged_prefill_kernel (one launch per call)",
-                     "launch_avg_us": round(avg * 1e3, 2)},
+        "flops_per_step": flops, "kv_bytes_per_step": kv_bytes,
         "cpu_baseline": cpu,
     }
+    if flops / kv_bytes < MFMA_PEAK_TFLOPS[dt] * 1e12 / (HBM_PEAK_GBS * 1e9):
+        # below the ridge (few query rows per key): bound by reading the KV once
+        gbs = kv_bytes / (avg * 1e-3) / 1e9
+        line["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                            "kernel": "paged_prefill_kernel (split keys) + chunk_merge_kernel",
+                            "launch_avg_us": round(avg * 1e3, 2)}
+        line["unsplit_avg_us"] = round(timed(None) * 1e3, 2)  # the same call without a workspace
+    else:
+        line["roofline"] = {"bound": "mfma", "achieved": round(tflops, 1),
+                            "peak": MFMA_PEAK_TFLOPS[dt], "unit": "TFLOP/s",
+                            "frac": round(tflops / MFMA_PEAK_TFLOPS[dt], 4), "traffic": None,
+                            "kernel": "paged_prefill_kernel (one launch per call)",
+                            "launch_avg_us": round(avg * 1e3, 2)}
     print(json.dumps(line), flush=True)
 
 
@@ -290,7 +313,7 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
-    if args.workload == "prefill":
+    if args.workload in ("prefill", "prefill_small"):
         B.lib()
         bench_prefill(args)
         return

@@ -301,15 +301,31 @@ int pkv_paged_attention_decode_shared_prefix(
  * A sequence whose chunk is not inside [0, num_tokens], is longer than its
  * context, or whose context exceeds max_blocks_per_seq * 16 is skipped (its
  * rows are not written); one whose needed block ids fall outside the pool gets
- * NaN rows. No workspace. Errors: INVALID_ARG, UNSUPPORTED (as decode, or a
- * batch too large for one launch), HIP. */
+ * NaN rows.
+ *
+ *  workspace, workspace_bytes  NULL (each 128-row tile of a sequence is one
+ *                workgroup over all its keys), or at least
+ *                pkv_prefill_workspace_bytes(head_dim) bytes of device memory,
+ *                256-byte aligned (no zeroing needed). With a workspace, a
+ *                batch with few rows (short chunks over long contexts) splits
+ *                each row tile's keys into chunks computed by separate
+ *                workgroups, and a second launch merges the chunk partials
+ *                (float32 m, l and accumulators) by the log-sum-exp rule. One
+ *                call at a time per workspace.
+ * Errors: INVALID_ARG, UNSUPPORTED (as decode, or a batch too large for one
+ * launch), WORKSPACE (misaligned or too small), HIP. */
 int pkv_paged_attention_prefill(const void *q, int32_t q_dtype, int32_t num_seqs,
                                 int32_t num_tokens, int32_t num_q_heads,
                                 const int32_t *query_start, const void *k_cache,
                                 const void *v_cache, const pkv_cache_desc *cache,
                                 const int32_t *block_tables, int32_t max_blocks_per_seq,
-                                const int32_t *context_lens, float scale, void *out,
-                                hipStream_t stream);
+                                const int32_t *context_lens, float scale, void *workspace,
+                                size_t workspace_bytes, void *out, hipStream_t stream);
+
+/* Workspace bytes for pkv_paged_attention_prefill's key split: 4096 partial
+ * slots of 16 rows (16 * head_dim + 32 floats each), rounded up to 256. 0 for
+ * a head_dim other than 64 or 128. */
+size_t pkv_prefill_workspace_bytes(int32_t head_dim);
 
 /* Copy whole physical blocks, every KV head of K and V:
  *     block pairs[i][1] <- block pairs[i][0],   i < num_pairs.

@@ -34,7 +34,8 @@ _TORCH_CODES = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: 
 EXPORTS = ("pkv_status_string", "pkv_kv_bytes_per_token", "pkv_cache_tensor_bytes",
            "pkv_kv_append", "pkv_decode_workspace_bytes", "pkv_paged_attention_decode",
            "pkv_shared_prefix_workspace_bytes", "pkv_paged_attention_decode_shared_prefix",
-           "pkv_paged_attention_prefill", "pkv_copy_blocks", "pkv_debug_gather",
+           "pkv_paged_attention_prefill", "pkv_prefill_workspace_bytes", "pkv_copy_blocks",
+           "pkv_debug_gather",
            # host block manager (pkv_blocks.h; bound in blocks.py)
            "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_num_free_blocks", "pkv_bm_add_request",
            "pkv_bm_can_append", "pkv_bm_append", "pkv_bm_fork", "pkv_bm_free_request",
@@ -88,8 +89,10 @@ def lib():
             vp, i32, i32, i32, vp, vp, descp, vp, i32, vp, i32, vp, vp, f32, i32, vp, sz, vp, vp]
         L.pkv_paged_attention_decode_shared_prefix.restype = ctypes.c_int
         L.pkv_paged_attention_prefill.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, descp, vp,
-                                                  i32, vp, f32, vp, vp]
+                                                  i32, vp, f32, vp, sz, vp, vp]
         L.pkv_paged_attention_prefill.restype = ctypes.c_int
+        L.pkv_prefill_workspace_bytes.argtypes = [i32]
+        L.pkv_prefill_workspace_bytes.restype = sz
         L.pkv_copy_blocks.argtypes = [vp, vp, descp, vp, i32, vp]
         L.pkv_copy_blocks.restype = ctypes.c_int
         L.pkv_debug_gather.argtypes = [vp, vp, descp, vp, i32, vp, i32, i32, vp, vp, vp]
@@ -268,12 +271,26 @@ def pkv_paged_attention_decode_shared_prefix(
     _check("pkv_paged_attention_decode_shared_prefix", rc)
 
 
+def pkv_prefill_workspace_bytes(head_dim: int) -> int:
+    return int(lib().pkv_prefill_workspace_bytes(head_dim))
+
+
+def prefill_workspace(head_dim: int, device=None) -> torch.Tensor:
+    """A workspace that lets pkv_paged_attention_prefill split the keys of
+    batches with few query rows over several workgroups."""
+    n = pkv_prefill_workspace_bytes(head_dim)
+    _need(n > 0, "head_dim must be 64 or 128")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
 def pkv_paged_attention_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                                 desc: pkv_cache_desc, block_tables: torch.Tensor,
                                 context_lens: torch.Tensor, query_start: torch.Tensor,
-                                scale: float, out: torch.Tensor, stream=None) -> None:
+                                scale: float, out: torch.Tensor,
+                                workspace: Optional[torch.Tensor] = None, stream=None) -> None:
     """q, out: [T][H_q][d]; query_start: int32 [S + 1] (sequence s owns rows
-    [query_start[s], query_start[s + 1])); block_tables, context_lens as for decode."""
+    [query_start[s], query_start[s + 1])); block_tables, context_lens as for decode.
+    workspace: None, or prefill_workspace(d) to let few-row batches split their keys."""
     T, Hq, d = q.shape
     S = context_lens.numel()
     _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
@@ -284,10 +301,14 @@ def pkv_paged_attention_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache:
     _need(context_lens.dtype == torch.int32, "context_lens must be int32 [S]")
     for t in (q, k_cache, v_cache, block_tables, context_lens, query_start, out):
         _need(t.is_contiguous() and t.is_cuda, "all tensors must be contiguous device tensors")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _need(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a device tensor")
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
     rc = lib().pkv_paged_attention_prefill(
         _ptr(q), _dtype_of(q), S, T, Hq, _ptr(query_start), _ptr(k_cache), _ptr(v_cache),
         ctypes.byref(desc), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
-        float(scale), _ptr(out), _stream(stream))
+        float(scale), ws_ptr, ws_bytes, _ptr(out), _stream(stream))
     _check("pkv_paged_attention_prefill", rc)
 
 

@@ -31,6 +31,10 @@
 //     the 8 XCDs round-robin) and share its L2; within a sequence the row
 //     tiles with the most keys start first.
 //
+// Batches with few row tiles (short chunks over long contexts) may split a
+// row tile's keys into chunks, each a workgroup, when the caller passes a
+// partial-slot workspace; chunk_merge_kernel then combines the partials.
+//
 // The same kernel in prefix mode is the prefix pass of the shared-prefix
 // decode (see the end of this file): a prefix group's member sequences take
 // the place of a chunk's tokens, every row sees every key of its part of the
@@ -164,10 +168,24 @@ __device__ __forceinline__ void store4_as(void* base, size_t idx, float a, float
     }
 }
 
-// The prefix pass's common chunk count for groups whose rows fill rt_total
-// row tiles of 128 and rb_total row blocks of 16 (per KV head): about
-// kPrefixTargetWorkgroups workgroups, and the chunked groups' 16-row partials
-// within kPrefixSlots. Both kernels of the pass derive it the same way.
+// A prefill sequence's row tiles of 128 rows, 16-row blocks, and the key
+// tiles of its first row tile (the fewest of any of its row tiles); zeros for
+// an invalid or empty chunk.
+__device__ __forceinline__ void prefill_seq_shape(const PrefillParams& p, int s, int& rts, int& rbs,
+                                                  int& tmin) {
+    rts = row_tiles(p, s);
+    rbs = tmin = 0;
+    if (rts == 0) return;
+    const int q_len = p.query_start[s + 1] - p.query_start[s];
+    const int rows = q_len * p.group;
+    rbs = (rows + 15) / 16;
+    tmin = (p.context_lens[s] - q_len + (min(rows, kGroupRows) - 1) / p.group) / kBlock + 1;
+}
+
+// The common chunk count for work whose rows fill rt_total row tiles of 128
+// and rb_total row blocks of 16 (per KV head): about kPrefixTargetWorkgroups
+// workgroups, and the chunked rows' 16-row partials within kPrefixSlots. The
+// attention kernel and the merge launch derive it the same way.
 __device__ __forceinline__ int prefix_chunks(int H, int rt_total, int rb_total) {
     const int per_chunk = H * rt_total;
     const int cg = per_chunk >= kPrefixTargetWorkgroups
@@ -207,7 +225,8 @@ void paged_prefill_kernel(PrefillParams p) {
 
     // ---- this workgroup's task ----
     // (row tiles of 128 rows stacked token-major, row = token * G + head; in
-    // the prefix pass a group's members take the place of the chunk's tokens)
+    // the prefix pass a group's members take the place of the chunk's tokens;
+    // a row tile's keys may be split into chunks, each a workgroup of its own)
     int g = 0, q0 = 0, q_len = 0, n = 0, base_pos = 0, row_wg = 0, tiles = 0, tile0 = 0;
     size_t bt_row = 0;
     int pf_chunks = 1, pf_chunk = 0, rb_total = 0;  // prefix pass
@@ -268,37 +287,66 @@ void paged_prefill_kernel(PrefillParams p) {
         row_wg = rt * kGroupRows;
         bt_row = (size_t)q0 * mb;  // the group's blocks: its first member's table
     } else {
+        // Sequences with few row tiles split each row tile's keys into chunks
+        // when a partial-slot workspace is given (slots != nullptr).
+        int cg = 1;
+        if (p.slots != nullptr) {
+            int rt_total = 0;
+            for (int base = 0; base < S; base += kWave) {
+                const int ss = base + lane;
+                int rts = 0, rbs = 0, tmin = 0;
+                if (ss < S) prefill_seq_shape(p, ss, rts, rbs, tmin);
+                rt_total += wave_sum_int(rts);
+                rb_total += wave_sum_int(rbs);
+            }
+            if (rt_total > 0) cg = prefix_chunks(H, rt_total, rb_total);
+        }
         const int task = blockIdx.x;
         int s = -1, local = 0;
         int before = 0;
+        int64_t t16_before = 0;
         for (int base = 0; base < S; base += kWave) {
             const int ss = base + lane;
-            const int cnt = ss < S ? row_tiles(p, ss) * H : 0;
+            int rts = 0, rbs = 0, tmin = 0;
+            if (ss < S) prefill_seq_shape(p, ss, rts, rbs, tmin);
+            const int cs = min(cg, max(tmin, 1));
+            const int cnt = rts * H * cs;
             const int incl = wave_inclusive_scan(cnt, lane);
+            const int tincl = wave_inclusive_scan(H * rbs * cs, lane);
             const unsigned long long hit = __ballot(cnt > 0 && before + incl - cnt <= task &&
                                                     task < before + incl);
             if (hit) {
                 const int L = __ffsll(hit) - 1;
                 s = base + L;
                 local = task - before - __builtin_amdgcn_readlane(incl - cnt, L);
+                pf_task16 = t16_before + __builtin_amdgcn_readlane(tincl - H * rbs * cs, L);
+                pf_chunks = __builtin_amdgcn_readlane(cs, L);
                 break;
             }
             before += __builtin_amdgcn_readlane(incl, kWave - 1);
+            t16_before += __builtin_amdgcn_readlane(tincl, kWave - 1);
         }
         if (s < 0) return;  // the grid is an upper bound on the tasks
         g = local % H;
-        const int rt = row_tiles(p, s) - 1 - local / H;  // the longest row tiles first
+        pf_chunk = (local / H) % pf_chunks;
+        const int rt = row_tiles(p, s) - 1 - local / H / pf_chunks;  // the longest row tiles first
         q0 = p.query_start[s];
         q_len = p.query_start[s + 1] - q0;
         n = p.context_lens[s];
         base_pos = n - q_len;  // position of the chunk's first token
         row_wg = rt * kGroupRows;
         const int last_row = min(q_len * G, row_wg + kGroupRows) - 1;
-        tiles = (base_pos + last_row / G) / kBlock + 1;  // keys 0 .. last position
+        const int tiles_rt = (base_pos + last_row / G) / kBlock + 1;  // keys 0 .. last position
+        // this workgroup's chunk of them; positions are counted from its first key
+        tile0 = (int)((int64_t)pf_chunk * tiles_rt / pf_chunks);
+        tiles = (int)((int64_t)(pf_chunk + 1) * tiles_rt / pf_chunks) - tile0;
+        base_pos -= tile0 * kBlock;
+        n -= tile0 * kBlock;
         bt_row = (size_t)s * p.max_blocks_per_seq;
     }
     const int nrows = q_len * G;
     const int steps = (tiles + 1) / 2;
+    const int key_end = tiles * kBlock - 1;  // the chunk's last key (positions from its first)
 
     // The score scale in log2 units, made non-negative: a negative scale
     // flips the sign of q instead (exact), so that the running maximum can be
@@ -317,9 +365,11 @@ void paged_prefill_kernel(PrefillParams p) {
         const int row = row_w + rb * 16 + t;
         const bool ok = row < nrows;
         const int tok = ok ? row / G : q_len - 1;
-        // prefix pass: every row sees all keys of the chunk, as if it sat at
-        // the chunk's last key (so a stand-in second tile is masked)
-        pos[rb] = PFX ? n - 1 : base_pos + tok;
+        // A row sees keys up to its position, and only those of this
+        // workgroup's chunk of keys: as if it sat at most at the chunk's last
+        // key (so a stand-in second tile past the chunk is masked). In the
+        // prefix pass every row sees every key of the chunk.
+        pos[rb] = PFX ? key_end : min(base_pos + tok, key_end);
         const int h = g * G + (ok ? row % G : 0);
         TM::load_q(q[rb], p.q + ((size_t)(q0 + tok) * Hq + h) * D * QB, ok, g4);
 #pragma unroll
@@ -334,8 +384,8 @@ void paged_prefill_kernel(PrefillParams p) {
     for (int rb = 0; rb < kRowBlocks; ++rb) {
         const int r0 = row_w + rb * 16;
         const int r1 = min(nrows, r0 + 16) - 1;
-        rb_first[rb] = r0 < nrows ? (PFX ? n - 1 : base_pos + r0 / G) : INT32_MAX;
-        rb_last[rb] = r0 < nrows ? (PFX ? n - 1 : base_pos + r1 / G) : -1;
+        rb_first[rb] = r0 < nrows ? (PFX ? key_end : min(base_pos + r0 / G, key_end)) : INT32_MAX;
+        rb_last[rb] = r0 < nrows ? (PFX ? key_end : min(base_pos + r1 / G, key_end)) : -1;
         wave_last = max(wave_last, rb_last[rb]);
     }
 
@@ -553,22 +603,24 @@ void paged_prefill_kernel(PrefillParams p) {
             float tm = vmax(xm, lane_fetch(x16, xm));
             tm = vmax(tm, lane_fetch(x32, tm));
             const float mn = vmax(m_run[rb], tm * c);
-            const float cf = __builtin_amdgcn_exp2f(m_run[rb] - mn);
+            // a row that has seen no key yet (a chunk that starts past it)
+            // keeps its zero sums
+            const float cf = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[rb] - mn);
             l_run[rb] *= cf;
 #pragma unroll
             for (int j = 0; j < NV; ++j) o[rb][j] *= cf;
             m_run[rb] = mn;
         }
     };
-    // The weights of a row block's eight raw scores, rounded to the 16-bit
-    // type in pairs and packed as the P^T operand; l_run gains their sum as
-    // rounded (dot products with ones).
-    auto weights16 = [&](int rb, const float (&x)[8]) -> V8 {
+    // The weights of a row block's eight raw scores against the maximum m,
+    // rounded to the 16-bit type in pairs and packed as the P^T operand;
+    // l_run gains their sum as rounded (dot products with ones).
+    auto weights16 = [&](int rb, const float (&x)[8], float m) -> V8 {
         V2 h[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            h[i] = V2{(E16)__builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * i], c, -m_run[rb])),
-                      (E16)__builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * i + 1], c, -m_run[rb]))};
+            h[i] = V2{(E16)__builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * i], c, -m)),
+                      (E16)__builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * i + 1], c, -m))};
         const V2 one = {(E16)1.f, (E16)1.f};
         float l = l_run[rb];
 #pragma unroll
@@ -651,7 +703,7 @@ void paged_prefill_kernel(PrefillParams p) {
                 qk_products(kr, s_cur);
                 V8 pk[kRowBlocks];
 #pragma unroll
-                for (int rb = 0; rb < kRowBlocks; ++rb) pk[rb] = weights16(rb, x[rb]);
+                for (int rb = 0; rb < kRowBlocks; ++rb) pk[rb] = weights16(rb, x[rb], m_run[rb]);
                 // V is read once the K operands are consumed (their registers
                 // are reused)
                 u32x4_t vop[NV];
@@ -695,11 +747,12 @@ void paged_prefill_kernel(PrefillParams p) {
                     }
                 }
                 rescale(rb, max8(x));
+                // a row with no visible key so far has m = -inf and gets zero weights
+                const float m = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
                 if constexpr (TM::kF32) {
                     float pw[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        pw[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], c, -m_run[rb]));
+                    for (int e = 0; e < 8; ++e) pw[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], c, -m));
                     // O^T += V^T P^T per tile on 16x16x4: k index = key 4 g4 + kk
 #pragma unroll
                     for (int j = 0; j < NV; ++j)
@@ -714,7 +767,7 @@ void paged_prefill_kernel(PrefillParams p) {
                         }
                     l_run[rb] += ((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7]));
                 } else {
-                    pv16(rb, weights16(rb, x), vop, va, vb);
+                    pv16(rb, weights16(rb, x, m), vop, va, vb);
                 }
             }
             if (has_next && wave_last >= key0 + 2 * kBlock) scores(st_next, s_cur);
@@ -726,59 +779,48 @@ void paged_prefill_kernel(PrefillParams p) {
 
     // ---- lane (t, g4) holds elements 16 j + 4 g4 .. + 3 of row t ----
     const float nan = __builtin_nanf("");
-    if constexpr (PFX) {
-        // The prefix pass: merge with the suffix results (one chunk), or park
-        // the partial in the row block's slot.
-        constexpr int SLOT = prefix_slot_floats(D);
+    constexpr int SLOT = prefix_slot_floats(D);
 #pragma unroll
-        for (int rb = 0; rb < kRowBlocks; ++rb) {
-            const int r0 = row_w + rb * 16;
-            if (r0 >= nrows) continue;  // wave-uniform
-            const int rb16 = r0 / 16;
-            float lt = l_run[rb] + lane_fetch(x16, l_run[rb]);
-            lt += lane_fetch(x32, lt);  // weight sum of row t over the chunk
-            const float m = bad ? nan : m_run[rb];
-            const int row = r0 + t;
-            if (pf_chunks == 1) {
-                if (row < nrows) {
-                    const size_t orow = (size_t)(q0 + row / G) * Hq + g * G + row % G;
-                    const float lse = p.res_lse[orow];
-                    const float M = fmaxf(m, lse);
-                    const float wp = __builtin_amdgcn_exp2f(m - M);
-                    const float ws = __builtin_amdgcn_exp2f(lse - M);
-                    const float sc = p.v_scale / (wp * lt + ws);
-#pragma unroll
-                    for (int j = 0; j < NV; ++j) {
-                        const f32x4_t so = *reinterpret_cast<const f32x4_t*>(p.res_o + orow * D + 16 * j + 4 * g4);
-                        store4_as<QT>(p.out, orow * D + 16 * j + 4 * g4, (wp * o[rb][j][0] + ws * so[0]) * sc,
-                                      (wp * o[rb][j][1] + ws * so[1]) * sc, (wp * o[rb][j][2] + ws * so[2]) * sc,
-                                      (wp * o[rb][j][3] + ws * so[3]) * sc);
-                    }
-                }
-                continue;
-            }
-            // several chunks: the partial goes to its slot; the merge launch
-            // that follows combines the chunks
-            const int64_t f = pf_task16 + (int64_t)rb16 * (H * pf_chunks) + g * pf_chunks + pf_chunk;
+    for (int rb = 0; rb < kRowBlocks; ++rb) {
+        const int r0 = row_w + rb * 16;
+        if (r0 >= nrows) continue;  // wave-uniform
+        float lt = l_run[rb] + lane_fetch(x16, l_run[rb]);
+        lt += lane_fetch(x32, lt);  // weight sum of row t (over this chunk of keys)
+        const int row = r0 + t;
+        const size_t orow = (size_t)(q0 + min(row, nrows - 1) / G) * Hq + g * G + min(row, nrows - 1) % G;
+        if (pf_chunks > 1) {
+            // one chunk of several: the partial goes to its 16-row slot and
+            // the merge launch that follows combines the chunks
+            const int64_t f = pf_task16 + (int64_t)(r0 / 16) * (H * pf_chunks) + g * pf_chunks + pf_chunk;
             float* slotp = p.slots + (size_t)f * SLOT;
 #pragma unroll
             for (int j = 0; j < NV; ++j)
                 *reinterpret_cast<f32x4_t*>(slotp + t * D + 16 * j + 4 * g4) = o[rb][j];
             if (g4 == 0) {
-                slotp[16 * D + t] = m;
+                slotp[16 * D + t] = bad ? nan : m_run[rb];
                 slotp[16 * D + 16 + t] = lt;
             }
-        }
-    } else {
-        // normalise and store
-#pragma unroll
-        for (int rb = 0; rb < kRowBlocks; ++rb) {
-            float lt = l_run[rb] + lane_fetch(x16, l_run[rb]);
-            lt += lane_fetch(x32, lt);
-            const float sc = bad ? nan : p.v_scale / lt;
-            const int row = row_w + rb * 16 + t;
+        } else if constexpr (PFX) {
+            // the prefix pass in one chunk: merge with the suffix results
             if (row < nrows) {
-                const size_t orow = (size_t)(q0 + row / G) * Hq + g * G + row % G;
+                const float m = bad ? nan : m_run[rb];
+                const float lse = p.res_lse[orow];
+                const float M = fmaxf(m, lse);
+                const float wp = __builtin_amdgcn_exp2f(m - M);
+                const float ws = __builtin_amdgcn_exp2f(lse - M);
+                const float sc = p.v_scale / (wp * lt + ws);
+#pragma unroll
+                for (int j = 0; j < NV; ++j) {
+                    const f32x4_t so = *reinterpret_cast<const f32x4_t*>(p.res_o + orow * D + 16 * j + 4 * g4);
+                    store4_as<QT>(p.out, orow * D + 16 * j + 4 * g4, (wp * o[rb][j][0] + ws * so[0]) * sc,
+                                  (wp * o[rb][j][1] + ws * so[1]) * sc, (wp * o[rb][j][2] + ws * so[2]) * sc,
+                                  (wp * o[rb][j][3] + ws * so[3]) * sc);
+                }
+            }
+        } else {
+            // prefill in one chunk: normalise and store
+            if (row < nrows) {
+                const float sc = bad ? nan : p.v_scale / lt;
 #pragma unroll
                 for (int j = 0; j < NV; ++j)
                     store4_as<QT>(p.out, orow * D + 16 * j + 4 * g4, o[rb][j][0] * sc, o[rb][j][1] * sc,
@@ -788,49 +830,67 @@ void paged_prefill_kernel(PrefillParams p) {
     }
 }
 
-// The merge launch of the prefix pass: one workgroup of 256 threads per
-// (16-row block, KV head) of the groups whose prefix was split into chunks;
-// thread i takes row i / 16 of the block and elements (i % 16) * D / 16 ..
-// of it. With the block's slots f0 .. f0 + C - 1 (as the prefix kernel
-// placed them) and the suffix result (o_s, lse_s) of the row:
+// The merge launch: one workgroup of 256 threads per (16-row block, KV head)
+// of the rows whose keys were split into chunks (prefix groups in the prefix
+// pass, PFX; prefill sequences with few rows otherwise). Thread i takes row
+// i / 16 of the block and elements (i % 16) * D / 16 .. of it. With the
+// block's slots f0 .. f0 + C - 1 (as the attention kernel placed them) and,
+// in the prefix pass, the suffix result (o_s, lse_s) of the row (else
+// lse_s = -inf):
 //   M = max(m_1..m_C, lse_s),
 //   out = v_scale * (sum_c 2^(m_c - M) acc_c + 2^(lse_s - M) o_s)
 //                  / (sum_c 2^(m_c - M) l_c + 2^(lse_s - M)).
 constexpr int kMergeThreads = 256;
 
-template <int QT, int D>
-__global__ __launch_bounds__(kMergeThreads) void prefix_merge_kernel(PrefillParams p) {
+template <int QT, int D, bool PFX>
+__global__ __launch_bounds__(kMergeThreads) void chunk_merge_kernel(PrefillParams p) {
     constexpr int SLOT = prefix_slot_floats(D);
     constexpr int EPT = D / 16;  // elements per thread: 8 (d 128) or 4 (d 64)
     const int lane = lane_id();
     const int S = p.num_seqs, H = p.num_kv_heads, G = p.group, Hq = p.num_q_heads;
-    const int ng = usable_groups(p.group_starts, p.group_prefix, p.num_groups, S,
-                                 p.max_blocks_per_seq, lane);
-    if (ng == 0) return;
-    auto rows_of = [&](int j) {
-        return p.group_prefix[j] > 0 ? (p.group_starts[j + 1] - p.group_starts[j]) * G : 0;
+    // the units whose rows are stacked: prefix groups or prefill sequences
+    int nu = S;
+    if constexpr (PFX) {
+        nu = usable_groups(p.group_starts, p.group_prefix, p.num_groups, S, p.max_blocks_per_seq, lane);
+        if (nu == 0) return;
+    }
+    // unit j: its rows, row tiles, 16-row blocks and most chunks
+    auto shape = [&](int j, int& rows, int& rts, int& rbs, int& cmax) {
+        if constexpr (PFX) {
+            const int pre = p.group_prefix[j];
+            rows = pre > 0 ? (p.group_starts[j + 1] - p.group_starts[j]) * G : 0;
+            rts = (rows + kGroupRows - 1) / kGroupRows;
+            rbs = (rows + 15) / 16;
+            cmax = pre;
+        } else {
+            int tmin = 0;
+            prefill_seq_shape(p, j, rts, rbs, tmin);
+            rows = rts > 0 ? (p.query_start[j + 1] - p.query_start[j]) * G : 0;
+            cmax = max(tmin, 1);
+        }
     };
     int rt_total = 0, rb_total = 0;
-    for (int base = 0; base < ng; base += kWave) {
+    for (int base = 0; base < nu; base += kWave) {
         const int j = base + lane;
-        const int rows = j < ng ? rows_of(j) : 0;
-        rb_total += wave_sum_int((rows + 15) / 16);
-        rt_total += wave_sum_int((rows + kGroupRows - 1) / kGroupRows);
+        int rows = 0, rts = 0, rbs = 0, cmax = 0;
+        if (j < nu) shape(j, rows, rts, rbs, cmax);
+        rt_total += wave_sum_int(rts);
+        rb_total += wave_sum_int(rbs);
     }
     if (rt_total == 0) return;
     const int cg = prefix_chunks(H, rt_total, rb_total);
-    if (cg == 1) return;  // every group was merged by the prefix kernel
+    if (cg == 1) return;  // nothing was split: the attention kernel wrote every row
     const int g = blockIdx.x % H;
-    const int rbg = blockIdx.x / H;  // 16-row block over all groups
+    const int rbg = blockIdx.x / H;  // 16-row block over all units
     if (rbg >= rb_total) return;
-    // the block's group (every wave finds the same)
-    int rb_before = 0, jj = -1, rb16 = 0;
+    // the block's unit (every wave finds the same)
+    int rb_before = 0, jj = -1, rb16 = 0, C = 1, nrows = 0;
     int64_t t16_before = 0, t16 = 0;
-    for (int base = 0; base < ng && jj < 0; base += kWave) {
+    for (int base = 0; base < nu && jj < 0; base += kWave) {
         const int j = base + lane;
-        const int rows = j < ng ? rows_of(j) : 0;
-        const int cj = j < ng ? min(p.group_prefix[j], cg) : 0;
-        const int rbs = (rows + 15) / 16;
+        int rows = 0, rts = 0, rbs = 0, cmax = 0;
+        if (j < nu) shape(j, rows, rts, rbs, cmax);
+        const int cj = min(cmax, cg);
         const int rincl = wave_inclusive_scan(rbs, lane);
         const int tincl = wave_inclusive_scan(H * rbs * cj, lane);
         const unsigned long long hit =
@@ -840,34 +900,39 @@ __global__ __launch_bounds__(kMergeThreads) void prefix_merge_kernel(PrefillPara
             jj = base + L;
             rb16 = rbg - rb_before - __builtin_amdgcn_readlane(rincl - rbs, L);
             t16 = t16_before + __builtin_amdgcn_readlane(tincl - H * rbs * cj, L);
+            C = __builtin_amdgcn_readlane(cj, L);
+            nrows = __builtin_amdgcn_readlane(rows, L);
         }
         rb_before += __builtin_amdgcn_readlane(rincl, kWave - 1);
         t16_before += __builtin_amdgcn_readlane(tincl, kWave - 1);
     }
     if (jj < 0) return;  // not reached for rbg < rb_total
-    const int C = min(p.group_prefix[jj], cg);
-    if (C <= 1) return;  // merged by the prefix kernel
+    if (C <= 1) return;  // merged by the attention kernel
     const int r = threadIdx.x >> 4, e0 = (threadIdx.x & 15) * EPT;
     const int row = rb16 * 16 + r;
-    if (row >= rows_of(jj)) return;
-    const size_t orow = (size_t)(p.group_starts[jj] + row / G) * Hq + g * G + row % G;
+    if (row >= nrows) return;
+    const int start = PFX ? p.group_starts[jj] : p.query_start[jj];  // a row's token = start + row / G
+    const size_t orow = (size_t)(start + row / G) * Hq + g * G + row % G;
     const float* slot0 = p.slots + (size_t)(t16 + (int64_t)rb16 * (H * C) + g * C) * SLOT;
-    const float lse = p.res_lse[orow];
+    const float lse = PFX ? p.res_lse[orow] : -INFINITY;
     float M = lse;
     for (int cc = 0; cc < C; ++cc) M = fmaxf(M, slot0[(size_t)cc * SLOT + 16 * D + r]);
-    const float ws = __builtin_amdgcn_exp2f(lse - M);
+    const float ws = PFX ? __builtin_amdgcn_exp2f(lse - M) : 0.f;
     float L = ws;
     float acc[EPT];
 #pragma unroll
     for (int i = 0; i < EPT; i += 4) {
-        const f32x4_t so = *reinterpret_cast<const f32x4_t*>(p.res_o + orow * D + e0 + i);
+        f32x4_t so = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (PFX) so = *reinterpret_cast<const f32x4_t*>(p.res_o + orow * D + e0 + i);
 #pragma unroll
         for (int x = 0; x < 4; ++x) acc[i + x] = ws * so[x];
     }
 #pragma unroll 4
     for (int cc = 0; cc < C; ++cc) {
         const float* sl = slot0 + (size_t)cc * SLOT;
-        const float w = __builtin_amdgcn_exp2f(sl[16 * D + r] - M);
+        // a chunk where the row saw no key holds m = -inf, l = 0 and zeros
+        const float mc = sl[16 * D + r];
+        const float w = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc - M);
         L += w * sl[16 * D + 16 + r];
 #pragma unroll
         for (int i = 0; i < EPT; i += 4) {
@@ -909,10 +974,26 @@ static hipError_t launch_prefill_typed(const PrefillArgs& a) {
     p.qk_scale_log2 = a.scale * (KT == PKV_FP8_E4M3 ? a.k_scale : 1.f) * 1.44269504088896340736f;
     p.v_scale = KT == PKV_FP8_E4M3 ? a.v_scale : 1.f;
     p.out = a.out;
-    const int64_t grid = prefill_task_bound(a.num_seqs, a.num_tokens, a.group, a.num_kv_heads);
+    // The keys are split only when the row tiles (at least T * G / 128 per KV
+    // head) fall short of the workgroup target; otherwise the workspace is
+    // not touched and no merge launch is needed.
+    const bool may_split = a.slots != nullptr &&
+                           (int64_t)a.num_kv_heads * (((int64_t)a.num_tokens * a.group) / kGroupRows) <
+                               kPrefixTargetWorkgroups;
+    p.slots = may_split ? a.slots : nullptr;
+    // with the key split: at most target + H * (row tiles) workgroups
+    const int64_t grid = prefill_task_bound(a.num_seqs, a.num_tokens, a.group, a.num_kv_heads) +
+                         (may_split ? kPrefixTargetWorkgroups : 0);
     if (grid <= 0) return hipSuccess;
     auto kernel = paged_prefill_kernel<KT, QT, D, false>;
     hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kPrefillThreads), 0, a.stream, p);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || !may_split) return err;
+    // the merge of split sequences (16-row blocks: at most T * G / 16 + S per KV head)
+    const int64_t merge_grid = (int64_t)a.num_kv_heads *
+                               (((int64_t)a.num_tokens * a.group) / 16 + a.num_seqs);
+    auto merge = chunk_merge_kernel<QT, D, false>;
+    hipLaunchKernelGGL(merge, dim3((unsigned)merge_grid), dim3(kMergeThreads), 0, a.stream, p);
     return hipGetLastError();
 }
 
@@ -973,7 +1054,7 @@ static hipError_t launch_prefix_typed(const DecodeArgs& a) {
     if (err != hipSuccess) return err;
     const int64_t merge_grid =
         (int64_t)a.num_kv_heads * prefix_row_blocks_bound(a.num_seqs, a.group, a.num_groups);
-    auto merge = prefix_merge_kernel<QT, D>;
+    auto merge = chunk_merge_kernel<QT, D, true>;
     hipLaunchKernelGGL(merge, dim3((unsigned)merge_grid), dim3(kMergeThreads), 0, a.stream, p);
     return hipGetLastError();
 }

@@ -235,13 +235,19 @@ PKV_EXPORT int pkv_paged_attention_decode_shared_prefix(
     return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+PKV_EXPORT size_t pkv_prefill_workspace_bytes(int32_t head_dim) {
+    if (head_dim != 64 && head_dim != 128) return 0;
+    return pkv::round256((size_t)pkv::kPrefixSlots * pkv::prefix_slot_floats(head_dim) * sizeof(float));
+}
+
 PKV_EXPORT int pkv_paged_attention_prefill(const void* q, int32_t q_dtype, int32_t num_seqs,
                                            int32_t num_tokens, int32_t num_q_heads,
                                            const int32_t* query_start, const void* k_cache,
                                            const void* v_cache, const pkv_cache_desc* cache,
                                            const int32_t* block_tables,
                                            int32_t max_blocks_per_seq,
-                                           const int32_t* context_lens, float scale, void* out,
+                                           const int32_t* context_lens, float scale,
+                                           void* workspace, size_t workspace_bytes, void* out,
                                            hipStream_t stream) {
     if (num_tokens < 0 || query_start == nullptr) return PKV_ERR_INVALID_ARG;
     if (num_tokens == 0) {  // nothing to compute: q and out may be NULL
@@ -255,8 +261,13 @@ PKV_EXPORT int pkv_paged_attention_prefill(const void* q, int32_t q_dtype, int32
                                block_tables, max_blocks_per_seq, context_lens, scale, 0,
                                false, nullptr, out, stream);
     if (rc != PKV_OK) return rc;
-    if (pkv::prefill_task_bound(num_seqs, num_tokens, d.group, cache->num_kv_heads) > INT32_MAX)
+    if (pkv::prefill_task_bound(num_seqs, num_tokens, d.group, cache->num_kv_heads) +
+            pkv::kPrefixTargetWorkgroups > INT32_MAX ||
+        (int64_t)cache->num_kv_heads * (((int64_t)num_tokens * d.group) / 16 + num_seqs) > INT32_MAX)
         return PKV_ERR_UNSUPPORTED;
+    if (workspace != nullptr && (((uintptr_t)workspace & 255u) != 0 ||
+                                 workspace_bytes < pkv_prefill_workspace_bytes(cache->head_dim)))
+        return PKV_ERR_WORKSPACE;
     pkv::PrefillArgs a{};
     a.q = q;
     a.q_dtype = q_dtype;
@@ -277,6 +288,7 @@ PKV_EXPORT int pkv_paged_attention_prefill(const void* q, int32_t q_dtype, int32
     a.scale = scale;
     a.k_scale = cache->k_scale;
     a.v_scale = cache->v_scale;
+    a.slots = static_cast<float*>(workspace);
     a.out = out;
     a.stream = stream;
     hipError_t err = pkv::launch_paged_prefill(a);

@@ -147,6 +147,7 @@ struct PrefillArgs {
     float scale;
     float k_scale;
     float v_scale;
+    float* slots = nullptr;  // kPrefixSlots partial slots: few-row sequences split their keys
     void* out;
     hipStream_t stream;
 };

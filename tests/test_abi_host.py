@@ -185,6 +185,41 @@ def test_shared_prefix_rejects_before_any_hip_call(kw, status):
     assert _shared(**kw) == status
 
 
+def test_prefill_workspace_bytes_formula():
+    for d in (64, 128):
+        assert B.pkv_prefill_workspace_bytes(d) == r256(4096 * (16 * d + 32) * 4)
+    assert B.pkv_prefill_workspace_bytes(96) == 0
+
+
+def _prefill(**kw):
+    a = dict(q=FAKE, q_dtype=B.PKV_F16, S=2, T=10, Hq=8, qs=FAKE, k=FAKE, v=FAKE,
+             desc=B.cache_desc(16, 2, 128, "f16"), bt=FAKE, mb=64, cl=FAKE, scale=0.1,
+             ws=None, ws_bytes=0, out=FAKE)
+    a.update(kw)
+    return B.lib().pkv_paged_attention_prefill(
+        a["q"], a["q_dtype"], a["S"], a["T"], a["Hq"], a["qs"], a["k"], a["v"],
+        ctypes.byref(a["desc"]), a["bt"], a["mb"], a["cl"], a["scale"], a["ws"], a["ws_bytes"],
+        a["out"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), B.PKV_ERR_INVALID_ARG),
+    (dict(qs=None), B.PKV_ERR_INVALID_ARG),
+    (dict(T=0, q=None, out=None), B.PKV_OK),                  # nothing to compute
+    (dict(q=None), B.PKV_ERR_INVALID_ARG),
+    (dict(out=FAKE + 4), B.PKV_ERR_INVALID_ARG),              # misaligned
+    (dict(Hq=7), B.PKV_ERR_INVALID_ARG),
+    (dict(Hq=18), B.PKV_ERR_UNSUPPORTED),                     # G = 9
+    (dict(q_dtype=B.PKV_BF16), B.PKV_ERR_UNSUPPORTED),        # bf16 q over an f16 cache
+    (dict(desc=B.cache_desc(16, 2, 96, "f16")), B.PKV_ERR_UNSUPPORTED),
+    (dict(scale=float("nan")), B.PKV_ERR_INVALID_ARG),
+    (dict(ws=FAKE, ws_bytes=1 << 20), B.PKV_ERR_WORKSPACE),   # too small for the slots
+    (dict(ws=FAKE + 16, ws_bytes=1 << 30), B.PKV_ERR_WORKSPACE),  # not 256-byte aligned
+])
+def test_prefill_rejects_before_any_hip_call(kw, status):
+    assert _prefill(**kw) == status
+
+
 def test_copy_blocks_rejects_bad_args():
     L = B.lib()
     d = B.cache_desc(16, 2, 128, "f16")

@@ -30,12 +30,13 @@ def make(case, ctx, q_lens, kv, qd, Hq, H, d, gpu, canary=True):
     return b, q, qs
 
 
-def gpu_prefill(b, q, qs, ctx=None, out=None):
+def gpu_prefill(b, q, qs, ctx=None, out=None, workspace=None):
     if out is None:
         out = torch.empty_like(q)
     kc, vc = device_caches(b)
     B.pkv_paged_attention_prefill(q, kc, vc, desc(b), b.block_tables,
-                                  b.context_lens if ctx is None else ctx, qs, b.scale, out)
+                                  b.context_lens if ctx is None else ctx, qs, b.scale, out,
+                                  workspace=workspace)
     return out
 
 
@@ -139,3 +140,70 @@ def test_no_tokens_is_a_no_op(gpu):
     qs = torch.zeros(b.num_seqs + 1, dtype=torch.int32, device=gpu)
     gpu_prefill(b, q, qs)
     torch.cuda.synchronize()
+
+
+# ---- few query rows over long contexts: the keys split over workgroups ----
+
+@pytest.mark.parametrize("kv,qd,Hq,H,d", [
+    ("bf16", "bf16", 32, 8, 128),   # G = 4
+    ("f16", "f16", 12, 2, 128),     # G = 6
+    ("fp8", "bf16", 64, 8, 128),    # G = 8
+    ("fp8", "f16", 8, 8, 64),       # G = 1
+    ("f32", "f32", 4, 1, 64),       # MQA
+])
+def test_split_keys_match_oracle(gpu, kv, qd, Hq, H, d):
+    """Chunks of 1..16 tokens over contexts up to 3000: with a workspace each
+    row tile's keys are split into chunks of their own (up to 22 here) and
+    merged; every row against the oracle, and against the unsplit result."""
+    ctx = [3000, 1999, 700, 45]
+    q_lens = [4, 16, 1, 9]
+    b, q, qs = make(67, ctx, q_lens, kv, qd, Hq, H, d, gpu)
+    ws = B.prefill_workspace(d, gpu)
+    split = out_to_f64(gpu_prefill(b, q, qs, workspace=ws))
+    whole = out_to_f64(gpu_prefill(b, q, qs))
+    assert_close(split, oracle_rows(b, q, qs), kv, f"split prefill {kv} G={Hq // H} d={d}")
+    assert_close(split, whole, kv, "split vs unsplit")
+
+
+def test_split_chunks_starting_past_rows(gpu):
+    """A 64-token chunk over a 64-token context with G = 4: its first row tile
+    (tokens 0..31) has two key tiles, so the keys split in two, and the rows of
+    tokens 0..15 see no key of the second chunk (their partial is empty). Two
+    more sequences with long contexts keep the batch small enough to split."""
+    ctx = [64, 2500, 1200]
+    q_lens = [64, 8, 3]
+    b, q, qs = make(68, ctx, q_lens, "bf16", "bf16", 16, 4, 128, gpu)
+    got = out_to_f64(gpu_prefill(b, q, qs, workspace=B.prefill_workspace(128, gpu)))
+    assert_close(got, oracle_rows(b, q, qs), "bf16", "chunks starting past rows")
+
+
+def test_split_workspace_reused_and_invalid_blocks(gpu):
+    """One workspace for two calls of different shapes (no zeroing between);
+    a block outside the pool still gives NaN rows through the merge."""
+    ws = B.prefill_workspace(64, gpu)
+    b, q, qs = make(69, [900, 40], [2, 7], "bf16", "bf16", 8, 2, 64, gpu)
+    assert_close(out_to_f64(gpu_prefill(b, q, qs, workspace=ws)), oracle_rows(b, q, qs), "bf16",
+                 "first call")
+    b2, q2, qs2 = make(70, [1500, 600, 30], [5, 1, 30], "bf16", "bf16", 8, 2, 64, gpu)
+    bt = b2.block_tables.clone()
+    bt[1, 20] = b2.num_blocks + 5  # a block outside the pool in sequence 1's range
+    out = torch.empty_like(q2)
+    kc, vc = device_caches(b2)
+    B.pkv_paged_attention_prefill(q2, kc, vc, desc(b2), bt, b2.context_lens, qs2, b2.scale, out,
+                                  workspace=ws)
+    torch.cuda.synchronize()
+    got = out_to_f64(out)
+    assert np.isnan(got[5:6]).all()
+    ref = oracle_rows(b2, q2, qs2)
+    keep = np.r_[0:5, 6:36]
+    assert_close(got[keep], ref[keep], "bf16", "second call, valid sequences")
+
+
+def test_split_not_used_for_many_rows(gpu):
+    """With many row tiles the chunk count is one: a workspace changes nothing
+    (bit for bit)."""
+    b, q, qs = make(71, [3000, 700], [1536, 700], "bf16", "bf16", 32, 8, 128, gpu, canary=False)
+    a = gpu_prefill(b, q, qs, workspace=B.prefill_workspace(128, gpu))
+    c = gpu_prefill(b, q, qs)
+    torch.cuda.synchronize()
+    assert torch.equal(a, c)
