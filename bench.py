@@ -56,6 +56,7 @@ PREFILL_CHUNK = 2048
 # and is bound by HBM.
 PREFILL_SMALL_CONTEXTS = [8192] * 8
 PREFILL_SMALL_CHUNK = 16
+PREFILL_MIN_WARMUP_S = 0.25  # untimed warm-up of the prefill workloads, at least
 
 
 def parse():
@@ -232,6 +233,14 @@ def bench_prefill(args):
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
+        # A launch lasts well under a millisecond, too short for the GPU's
+        # clock to settle within a few warm-up steps: keep warming up (untimed)
+        # for at least PREFILL_MIN_WARMUP_S.
+        t_end = time.perf_counter() + PREFILL_MIN_WARMUP_S
+        while time.perf_counter() < t_end:
+            for _ in range(20):
+                step()
+            torch.cuda.synchronize()
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)]
         for e0, e1 in evs:

@@ -24,8 +24,10 @@
 //     row's lanes; online softmax in log2 units with a lazily moved maximum.
 //     P^T . V contracts both tiles of a step in one 16x16x32 MFMA per 16
 //     output columns. Tiles wholly before a row block's first position need
-//     no mask; the diagonal tiles mask key k > p per row by select; tiles
-//     after its last position are skipped.
+//     no mask; the diagonal tiles mask key k > p per row by select; steps
+//     after the last position of all the wave's rows are skipped. Every step
+//     runs one straight-line body, so the compiler overlaps the next step's
+//     QK products with this step's softmax.
 //   * Workgroup index -> (sequence, row tile, KV head) with the KV head fastest,
 //     so the workgroups of one head land on one XCD (workgroups are dealt to
 //     the 8 XCDs round-robin) and share its L2; within a sequence the row
@@ -216,8 +218,14 @@ void paged_prefill_kernel(PrefillParams p) {
     typedef typename Compute16<QT>::V2 V2;
     typedef typename Compute16<QT>::V8 V8;
 
-    // kRing stages of two tiles' (K, V): tile A's K, A's V, B's K, B's V
+    // kRing stages of two tiles' (K, V). 16-bit tiles: A's K, B's K, then the
+    // V pieces of both alternating per 1 KiB (A's piece 0, B's piece 0, A's
+    // piece 1, ...), so that the two 8-byte halves of a P . V operand are the
+    // only pair of reads 1 KiB apart from one base and the compiler joins
+    // each pair into one read of the whole operand. Other tiles: A's K, A's
+    // V, B's K, B's V.
     __shared__ __attribute__((aligned(16))) uint8_t lds[kRing * kStepBytes];
+    constexpr uint32_t kKTileB = kDirectV ? kTileBytes : 2 * kTileBytes;  // B's K in a stage
 
     const int lane = lane_id();
     const int wv = wave_id();
@@ -356,6 +364,10 @@ void paged_prefill_kernel(PrefillParams p) {
 
     // ---- per lane: its query row (column t of the MFMA tiles) in each row block ----
     const int t = lane & 15;
+    // lane * 16 + 8 in a register whose value the compiler cannot see (the
+    // P . V operand reads address their second halves from it)
+    uint32_t v_half1 = (uint32_t)lane * 16 + 8;
+    asm volatile("" : "+v"(v_half1));
     const int g4 = lane >> 4;
     const int row_w = row_wg + wv * kWaveRows;
     typename TM::Q q[kRowBlocks];
@@ -388,6 +400,12 @@ void paged_prefill_kernel(PrefillParams p) {
         rb_last[rb] = r0 < nrows ? (PFX ? key_end : min(base_pos + r1 / G, key_end)) : -1;
         wave_last = max(wave_last, rb_last[rb]);
     }
+    // A step needs the causal select for row block rb once its last key
+    // passes sel_from[rb]; a block with no valid row always takes it, so its
+    // stand-in rows never score keys past their position.
+    int sel_from[kRowBlocks];
+#pragma unroll
+    for (int rb = 0; rb < kRowBlocks; ++rb) sel_from[rb] = rb_last[rb] >= 0 ? rb_first[rb] : -1;
 
     // ---- the tile stream: an LDS ring of two-tile steps, filled by direct loads ----
     // Step sp (tiles 2 sp and 2 sp + 1) goes to ring stage sp % kRing. It is
@@ -436,7 +454,11 @@ void paged_prefill_kernel(PrefillParams p) {
         const int pc = is_v ? cc - kPieces / 2 : cc;
         pc_src[i] = is_v ? v_piece_src(pc) : (uint32_t)pc * 1024 + (uint32_t)lane * 16;
         pc_v[i] = is_v;
-        pc_dst[i] = (uint32_t)th * 2 * kTileBytes + (is_v ? kTileBytes : 0) + (uint32_t)pc * 1024;
+        if constexpr (kDirectV)
+            pc_dst[i] = is_v ? 2 * kTileBytes + (uint32_t)(2 * pc + th) * 1024
+                             : (uint32_t)th * kTileBytes + (uint32_t)pc * 1024;
+        else
+            pc_dst[i] = (uint32_t)th * 2 * kTileBytes + (is_v ? kTileBytes : 0) + (uint32_t)pc * 1024;
         pc_b[i] = th == 1;
     }
     bool bad = false;
@@ -506,11 +528,14 @@ void paged_prefill_kernel(PrefillParams p) {
     // units, scaled), the lane's part of the weight sum, and O^T: o[rb][j]
     // holds elements 16 j + 4 g4 + r of row t (O^T = V^T P^T puts the query
     // row in the MFMA column, so every row statistic stays in its lanes).
-    float m_run[kRowBlocks], l_run[kRowBlocks];
+    // m_use is the maximum the weights subtract: m, or 0 while m is -inf (a
+    // row that has seen no key yet), so -inf - (-inf) never arises.
+    float m_run[kRowBlocks], m_use[kRowBlocks], l_run[kRowBlocks];
     f32x4_t o[kRowBlocks][NV];
 #pragma unroll
     for (int rb = 0; rb < kRowBlocks; ++rb) {
         m_run[rb] = -INFINITY;
+        m_use[rb] = 0.f;
         l_run[rb] = 0.f;
 #pragma unroll
         for (int j = 0; j < NV; ++j) o[rb][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -551,25 +576,28 @@ void paged_prefill_kernel(PrefillParams p) {
     auto scores = [&](uint32_t st, f32x4_t (&sc)[2][kRowBlocks]) {
         uint32_t kr[2][NK][KW];
         read_k(st, kr[0]);
-        read_k(st + 2 * kTileBytes, kr[1]);
+        read_k(st + kKTileB, kr[1]);
         qk_products(kr, sc);
     };
     // V of the step in stage st: for 16-bit caches the P . V operands
     // themselves (operand j = tile A's 4 tokens of element column 16 j + t,
-    // then tile B's: two 8-byte reads, 2 * kTileBytes apart), else the loads.
+    // then tile B's: two 8-byte reads 1 KiB apart), else the loads. The
+    // second halves of a lane's 16-byte chunks are addressed from their own
+    // base (lane * 16 + 8, hidden from the compiler), so that no read of a
+    // first half is joined with its neighbouring second half.
     auto read_vops = [&](uint32_t st, u32x4_t (&vop)[NV], uint32_t (&va)[NVL][VLW],
                          uint32_t (&vb)[NVL][VLW]) {
         if constexpr (kDirectV) {
-            const uint8_t* la = lds + st + kTileBytes + lane * 16;
 #pragma unroll
-            for (int i = 0; i < NVL; ++i)
+            for (int hh = 0; hh < 2; ++hh) {
+                const uint8_t* la = lds + st + 2 * kTileBytes + (hh ? v_half1 : lane * 16);
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const u32x2_t a2 = *reinterpret_cast<const u32x2_t*>(la + i * 1024 + hh * 8);
-                    const u32x2_t b2 =
-                        *reinterpret_cast<const u32x2_t*>(la + 2 * kTileBytes + i * 1024 + hh * 8);
+                for (int i = 0; i < NVL; ++i) {
+                    const u32x2_t a2 = *reinterpret_cast<const u32x2_t*>(la + 2 * i * 1024);
+                    const u32x2_t b2 = *reinterpret_cast<const u32x2_t*>(la + (2 * i + 1) * 1024);
                     vop[2 * i + hh] = __builtin_shufflevector(a2, b2, 0, 1, 2, 3);
                 }
+            }
         } else {
             read_v(st + kTileBytes, va);
             read_v(st + 3 * kTileBytes, vb);
@@ -610,6 +638,7 @@ void paged_prefill_kernel(PrefillParams p) {
 #pragma unroll
             for (int j = 0; j < NV; ++j) o[rb][j] *= cf;
             m_run[rb] = mn;
+            m_use[rb] = mn == -INFINITY ? 0.f : mn;
         }
     };
     // The weights of a row block's eight raw scores against the maximum m,
@@ -657,99 +686,116 @@ void paged_prefill_kernel(PrefillParams p) {
     if (kRing - 1 < steps) step_ids(kRing - 1, nia, nib);
     wait_steps(min(kRing - 2, steps - 1));
     workgroup_barrier();
-    f32x4_t s_cur[2][kRowBlocks];
+    // The scores of the step being computed and of the next one alternate
+    // between two register sets (the loop is unrolled by two), so the next
+    // step's products never have to be copied into the current step's set.
+    f32x4_t s_cur[2][kRowBlocks], s_alt[2][kRowBlocks];
     scores(0, s_cur);
-    const bool rows_full = rb_last[kRowBlocks - 1] >= 0;  // every row block of the wave has rows
 
-    for (int sp = 0; sp < steps; ++sp) {
-        const bool has_next = sp + 1 < steps;
-        if (has_next) {
-            // step sp + 1 in LDS for every wave; stage (sp - 1) % kRing free
-            wait_steps(min(kRing - 3, steps - 2 - sp));
-            workgroup_barrier();
-            if (sp + kRing - 1 < steps) issue(sp + kRing - 1, nia, nib);
-        }
-        const uint32_t st = (uint32_t)(sp % kRing) * kStepBytes;
-        const uint32_t st_next = (uint32_t)((sp + 1) % kRing) * kStepBytes;
-        const int key0 = 2 * sp * kBlock;  // first key of tile A; tile B starts at key0 + 16
-        const bool has_b = 2 * sp + 1 < tiles;
-        bool done = false;
-        if constexpr (!TM::kF32) {
-            if (has_next && rows_full && key0 + 2 * kBlock - 1 <= rb_first[0]) {
-                // A full step: every row of the wave sees all 32 keys (no
-                // causal mask, no key past n) and a next step exists. After
-                // the rare rescale, one straight-line block that the compiler
-                // schedules as a whole: the next step's QK products, this
-                // step's weights, the V reads and P . V.
-                uint32_t kr[2][NK][KW];
-                read_k(st_next, kr[0]);
-                read_k(st_next + 2 * kTileBytes, kr[1]);
-                float x[kRowBlocks][8], xm[kRowBlocks];
-                bool trig = false;
+    auto step = [&](int sp, f32x4_t (&s_now)[2][kRowBlocks], f32x4_t (&s_nxt)[2][kRowBlocks])
+                    __attribute__((always_inline)) {
+            const bool has_next = sp + 1 < steps;
+            if (has_next) {
+                // step sp + 1 in LDS for every wave; stage (sp - 1) % kRing free
+                wait_steps(min(kRing - 3, steps - 2 - sp));
+                workgroup_barrier();
+                if (sp + kRing - 1 < steps) issue(sp + kRing - 1, nia, nib);
+            }
+            const uint32_t st = (uint32_t)(sp % kRing) * kStepBytes;
+            const uint32_t st_next = (uint32_t)((sp + 1) % kRing) * kStepBytes;
+            const int key0 = 2 * sp * kBlock;  // first key of tile A; tile B starts at key0 + 16
+            const bool has_b = 2 * sp + 1 < tiles;
+            if constexpr (!TM::kF32) {
+                if (wave_last >= key0) {  // else every row of the wave is complete
+                    // One straight-line block per step, so the compiler can
+                    // interleave the next step's QK products with this step's
+                    // weights, and so the accumulators have one definition per
+                    // step: the next step's K reads and QK products, this step's
+                    // maximum (the rare rescale first), weights, V reads and
+                    // P . V. On the last step the next-step reads see a stage no
+                    // load targets and their products are never used.
+                    // Diagonal steps replace the scores of keys past a row's
+                    // position by -inf. Keys at or past n (the unused rows of the
+                    // last block) and a tile B past the workgroup's last tile
+                    // (which the causal limit, not n, can end) are seen by no row:
+                    // their V elements are zeroed too, so that whatever those rows
+                    // hold cannot reach P . V.
+                    uint32_t kr[2][NK][KW];
+                    read_k(st_next, kr[0]);
+                    read_k(st_next + kKTileB, kr[1]);
+                    float x[kRowBlocks][8], xm[kRowBlocks];
+                    bool trig = false;
 #pragma unroll
-                for (int rb = 0; rb < kRowBlocks; ++rb) {
+                    for (int rb = 0; rb < kRowBlocks; ++rb) {
+                        // raw scores: tile A keys key0 + 4 g4 + e, tile B keys key0 + 16 + 4 g4 + e
+                        // (selected in place, so that they keep their registers)
+                        if (key0 + 2 * kBlock - 1 > sel_from[rb]) {
+                            const int lim = pos[rb] - key0 - 4 * g4;  // visible: key offsets up to lim
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        x[rb][e] = s_cur[0][rb][e];
-                        x[rb][4 + e] = s_cur[1][rb][e];
+                            for (int e = 0; e < 4; ++e) {
+                                s_now[0][rb][e] = e <= lim ? s_now[0][rb][e] : -INFINITY;
+                                s_now[1][rb][e] = kBlock + e <= lim ? s_now[1][rb][e] : -INFINITY;
+                            }
+                        }
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            x[rb][e] = s_now[0][rb][e];
+                            x[rb][4 + e] = s_now[1][rb][e];
+                        }
+                        xm[rb] = max8(x[rb]);
+                        trig = trig || xm[rb] * c > m_run[rb] + kLazyRescale;
                     }
-                    xm[rb] = max8(x[rb]);
-                    trig = trig || xm[rb] * c > m_run[rb] + kLazyRescale;
-                }
-                if (__any(trig)) {
+                    if (__any(trig)) {
 #pragma unroll
-                    for (int rb = 0; rb < kRowBlocks; ++rb) rescale(rb, xm[rb]);
-                }
-                qk_products(kr, s_cur);
-                V8 pk[kRowBlocks];
+                        for (int rb = 0; rb < kRowBlocks; ++rb) rescale(rb, xm[rb]);
+                    }
+                    qk_products(kr, s_nxt);
+                    V8 pk[kRowBlocks];
 #pragma unroll
-                for (int rb = 0; rb < kRowBlocks; ++rb) pk[rb] = weights16(rb, x[rb], m_run[rb]);
-                // V is read once the K operands are consumed (their registers
-                // are reused)
+                    for (int rb = 0; rb < kRowBlocks; ++rb) pk[rb] = weights16(rb, x[rb], m_use[rb]);
+                    // V is read once the K operands are consumed (their registers
+                    // are reused)
+                    u32x4_t vop[NV];
+                    uint32_t va[NVL][VLW], vb[NVL][VLW];
+                    read_vops(st, vop, va, vb);
+                    if (key0 + 2 * kBlock > n || !has_b) {
+                        const int na = n - key0 - 4 * g4;        // live keys among this lane's four of tile A
+                        const int nb = has_b ? na - kBlock : 0;  // and of tile B (the null block: none)
+                        mask_vops(na, nb, vop, va, vb);
+                    }
+#pragma unroll
+                    for (int rb = 0; rb < kRowBlocks; ++rb) pv16(rb, pk[rb], vop, va, vb);
+                }
+            } else if (wave_last >= key0) {  // else every row of the wave is complete
+                // float32: this step's softmax and P . V, then the next step's
+                // scores. Keys at or past n and a tile B past the workgroup's last
+                // tile are seen by no row: their V elements are zeroed and their
+                // scores excluded by select.
                 u32x4_t vop[NV];
                 uint32_t va[NVL][VLW], vb[NVL][VLW];
                 read_vops(st, vop, va, vb);
+                const int na = n - key0 - 4 * g4;          // live keys among this lane's four of tile A
+                const int nb = has_b ? na - kBlock : 0;  // and of tile B (the null block: none)
+                if (key0 + 2 * kBlock > n || !has_b) mask_vops(na, nb, vop, va, vb);
 #pragma unroll
-                for (int rb = 0; rb < kRowBlocks; ++rb) pv16(rb, pk[rb], vop, va, vb);
-                done = true;
-            }
-        }
-        if (!done && wave_last >= key0) {  // else every row of the wave is complete
-            // A step on the causal diagonal, past n, or in the last position:
-            // this step's softmax and P . V, then the next step's scores
-            // (sequential: such steps are few).
-            // Keys at or past n (the unused rows of the last block), and a tile B
-            // past the workgroup's last tile (which the causal limit, not n, can
-            // end), are seen by no row: their V elements are zeroed, so that
-            // whatever those rows hold cannot reach P . V (their scores are
-            // excluded by select below).
-            u32x4_t vop[NV];
-            uint32_t va[NVL][VLW], vb[NVL][VLW];
-            read_vops(st, vop, va, vb);
-            const int na = n - key0 - 4 * g4;          // live keys among this lane's four of tile A
-            const int nb = has_b ? na - kBlock : 0;  // and of tile B (the null block: none)
-            if (key0 + 2 * kBlock > n || !has_b) mask_vops(na, nb, vop, va, vb);
-#pragma unroll
-            for (int rb = 0; rb < kRowBlocks; ++rb) {
-                if (rb_last[rb] < key0) continue;  // no row of the block sees this step
-                // raw scores: tile A keys key0 + 4 g4 + e, tile B keys key0 + 16 + 4 g4 + e
-                float x[8];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    x[e] = s_cur[0][rb][e];
-                    x[4 + e] = s_cur[1][rb][e];
-                }
-                if (key0 + 2 * kBlock - 1 > rb_first[rb]) {  // a diagonal step: causal select
+                for (int rb = 0; rb < kRowBlocks; ++rb) {
+                    if (rb_last[rb] < key0) continue;  // no row of the block sees this step
+                    // raw scores: tile A keys key0 + 4 g4 + e, tile B keys key0 + 16 + 4 g4 + e
+                    float x[8];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        x[e] = key0 + 4 * g4 + e <= pos[rb] ? x[e] : -INFINITY;
-                        x[4 + e] = key0 + kBlock + 4 * g4 + e <= pos[rb] ? x[4 + e] : -INFINITY;
+                        x[e] = s_now[0][rb][e];
+                        x[4 + e] = s_now[1][rb][e];
                     }
-                }
-                rescale(rb, max8(x));
-                // a row with no visible key so far has m = -inf and gets zero weights
-                const float m = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
-                if constexpr (TM::kF32) {
+                    if (key0 + 2 * kBlock - 1 > rb_first[rb]) {  // a diagonal step: causal select
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            x[e] = key0 + 4 * g4 + e <= pos[rb] ? x[e] : -INFINITY;
+                            x[4 + e] = key0 + kBlock + 4 * g4 + e <= pos[rb] ? x[4 + e] : -INFINITY;
+                        }
+                    }
+                    rescale(rb, max8(x));
+                    const float m = m_use[rb];
                     float pw[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) pw[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], c, -m));
@@ -766,13 +812,14 @@ void paged_prefill_kernel(PrefillParams p) {
                                 o[rb][j], 0, 0, 0);
                         }
                     l_run[rb] += ((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7]));
-                } else {
-                    pv16(rb, weights16(rb, x, m), vop, va, vb);
                 }
+                if (has_next && wave_last >= key0 + 2 * kBlock) scores(st_next, s_nxt);
             }
-            if (has_next && wave_last >= key0 + 2 * kBlock) scores(st_next, s_cur);
-        }
-        if (sp + kRing < steps) step_ids(sp + kRing, nia, nib);
+            if (sp + kRing < steps) step_ids(sp + kRing, nia, nib);
+    };
+    for (int sp = 0; sp < steps; sp += 2) {
+        step(sp, s_cur, s_alt);
+        if (sp + 1 < steps) step(sp + 1, s_alt, s_cur);
     }
 
     __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));  // no load into LDS outlives the workgroup
