@@ -348,9 +348,11 @@ void paged_decode_kernel(DecodeParams p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) head_lane[j] = (4 * g4 + j) << 2;
 
-    typename TM::Q q;
-    auto load_q = [&](int s, int g) {
-        TM::load_q(q, p.q + ((size_t)s * Hq + (size_t)g * G + t) * D * QB, t < G, g4);
+    // q: the query of the piece being computed; q_nx: that of the next
+    // piece, read as soon as the tile stream reaches it.
+    typename TM::Q q, q_nx;
+    auto load_q = [&](typename TM::Q& dst, int s, int g) {
+        TM::load_q(dst, p.q + ((size_t)s * Hq + (size_t)g * G + t) * D * QB, t < G, g4);
     };
 
     // Where ic's tile lives, and how many of its bytes to read: a whole tile,
@@ -390,7 +392,7 @@ void paged_decode_kernel(DecodeParams p) {
 
     // The query first: the oldest load in flight, so the first tile's wait
     // covers it and the loop never has to wait for everything.
-    load_q(cc.s, cc.g);
+    load_q(q, cc.s, cc.g);
 #pragma unroll
     for (int slot = 0; slot < kPrefetch; ++slot) {
         const TileRef tr = ic_tile(slot_bad[slot]);
@@ -429,6 +431,12 @@ void paged_decode_kernel(DecodeParams p) {
             piece_bad |= slot_bad[slot];
             bool next_bad;
             const TileRef nxt = ic_tile(next_bad);
+            // The tile about to be loaded opens the next piece (with one tile
+            // in flight, the current tile then ends this piece): its query is
+            // read first, so the in-order wait for that tile covers it too and
+            // the piece change waits for nothing else.
+            static_assert(kPrefetch == 1, "the next piece's query is read one tile ahead");
+            if (ic_valid && ic.seg != cc.seg) load_q(q_nx, ic.s, ic.g);
 
             // ---- scores; the next K goes out as soon as this K is consumed ----
             f32x4_t sc = TM::qk(kr[slot], q);
@@ -547,10 +555,7 @@ void paged_decode_kernel(DecodeParams p) {
             clo = 0;
             first_piece = false;
             piece_bad = false;
-            load_q(cc.s, cc.g);
-            // The query has landed before this path joins the streaming one,
-            // so the join does not make every tile wait for all loads.
-            __builtin_amdgcn_s_waitcnt(0);
+            q = q_nx;  // read with the piece's first tile, before it
             m_run = -INFINITY;
             l_run = 0.f;
 #pragma unroll
