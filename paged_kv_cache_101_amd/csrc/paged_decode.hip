@@ -113,8 +113,10 @@ __device__ __forceinline__ int worker_of(int64_t f, int64_t total, int nw) {
 // Merge the partials of one split segment, left by workers w0..w1 (worker w0
 // in its slot k0, the others in slot 0), into the output rows orow..orow+G-1:
 //   M = max_j m_j,  out = sum_j 2^(m_j - M) acc_j / sum_j 2^(m_j - M) l_j.
-// Lane j reads partial j's maxima and sums; the accumulators of 8 partials
-// are in flight at a time.
+// With at most 64 partials (the usual case), lane j reads partial j's maxima
+// and sums once and the accumulators of 16 partials are in flight at a time;
+// with more, the maxima and the sums are read in passes of 64 partials and 8
+// accumulators are in flight.
 template <int QT, int D, int GM>
 __device__ __forceinline__ void merge_segment(const DecodeParams& p, int w0, int w1,
                                                         int k0, int G, size_t orow, int lane,
@@ -127,43 +129,72 @@ __device__ __forceinline__ void merge_segment(const DecodeParams& p, int w0, int
         return p.slots + (size_t)(2 * (w0 + j) + (j == 0 ? k0 : 0)) * SLOT;
     };
     float mx[GM];
-#pragma unroll
-    for (int h = 0; h < GM; ++h) mx[h] = -INFINITY;
-    for (int j0 = 0; j0 < nparts; j0 += kWave) {
-        const int j = j0 + lane;
-#pragma unroll
-        for (int h = 0; h < GM; ++h) {
-            const float v = j < nparts ? coherent_load(slot_of(j) + GM * D + h) : -INFINITY;
-            mx[h] = fmaxf(mx[h], wave_max(v));
-        }
-    }
     float lsum[GM], o[PER_LANE];
 #pragma unroll
     for (int h = 0; h < GM; ++h) lsum[h] = 0.f;
 #pragma unroll
     for (int i = 0; i < PER_LANE; ++i) o[i] = 0.f;
-    for (int j0 = 0; j0 < nparts; j0 += kWave) {
-        const int j = j0 + lane;
+    if (nparts <= kWave) {
+        // At most one partial per lane: its maxima and sums are read once,
+        // and the accumulators of 16 partials are in flight at a time.
+        const int j = min(lane, nparts - 1);
+        const float* sl = slot_of(j);
         float c[GM];
 #pragma unroll
         for (int h = 0; h < GM; ++h) {
-            const float* sl = slot_of(min(j, nparts - 1));
-            c[h] = j < nparts ? __builtin_amdgcn_exp2f(coherent_load(sl + GM * D + h) - mx[h]) : 0.f;
-            lsum[h] += wave_sum(j < nparts ? coherent_load(sl + GM * D + GM + h) * c[h] : 0.f);
+            const float mj = lane < nparts ? coherent_load(sl + GM * D + h) : -INFINITY;
+            const float lj = lane < nparts ? coherent_load(sl + GM * D + GM + h) : 0.f;
+            mx[h] = wave_max(mj);
+            c[h] = lane < nparts ? __builtin_amdgcn_exp2f(mj - mx[h]) : 0.f;
+            lsum[h] = wave_sum(lj * c[h]);
         }
-        const int cnt = min(kWave, nparts - j0);
-#pragma unroll 8
-        for (int jj = 0; jj < cnt; ++jj) {
-            const float* sl = slot_of(j0 + jj);
+#pragma unroll 16
+        for (int jj = 0; jj < nparts; ++jj) {
+            const float* sj = slot_of(jj);
 #pragma unroll
             for (int i = 0; i < PER_LANE; ++i) {
-                const int idx = i * kWave + lane;       // h * D + e
+                const int idx = i * kWave + lane;  // h * D + e
                 if (idx < GM * D) {
-                    // D is a multiple of the wave width, so the head of
-                    // element idx is (i * kWave) / D: known at compile time
                     const int cj = __builtin_amdgcn_readlane(
                         __builtin_bit_cast(int, c[(i * kWave) / D]), jj);
-                    o[i] = fmaf(__builtin_bit_cast(float, cj), coherent_load(sl + idx), o[i]);
+                    o[i] = fmaf(__builtin_bit_cast(float, cj), coherent_load(sj + idx), o[i]);
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int h = 0; h < GM; ++h) mx[h] = -INFINITY;
+        for (int j0 = 0; j0 < nparts; j0 += kWave) {
+            const int j = j0 + lane;
+#pragma unroll
+            for (int h = 0; h < GM; ++h) {
+                const float v = j < nparts ? coherent_load(slot_of(j) + GM * D + h) : -INFINITY;
+                mx[h] = fmaxf(mx[h], wave_max(v));
+            }
+        }
+        for (int j0 = 0; j0 < nparts; j0 += kWave) {
+            const int j = j0 + lane;
+            float c[GM];
+#pragma unroll
+            for (int h = 0; h < GM; ++h) {
+                const float* sl = slot_of(min(j, nparts - 1));
+                c[h] = j < nparts ? __builtin_amdgcn_exp2f(coherent_load(sl + GM * D + h) - mx[h]) : 0.f;
+                lsum[h] += wave_sum(j < nparts ? coherent_load(sl + GM * D + GM + h) * c[h] : 0.f);
+            }
+            const int cnt = min(kWave, nparts - j0);
+#pragma unroll 8
+            for (int jj = 0; jj < cnt; ++jj) {
+                const float* sl = slot_of(j0 + jj);
+#pragma unroll
+                for (int i = 0; i < PER_LANE; ++i) {
+                    const int idx = i * kWave + lane;       // h * D + e
+                    if (idx < GM * D) {
+                        // D is a multiple of the wave width, so the head of
+                        // element idx is (i * kWave) / D: known at compile time
+                        const int cj = __builtin_amdgcn_readlane(
+                            __builtin_bit_cast(int, c[(i * kWave) / D]), jj);
+                        o[i] = fmaf(__builtin_bit_cast(float, cj), coherent_load(sl + idx), o[i]);
+                    }
                 }
             }
         }
