@@ -26,6 +26,14 @@ KV bytes (the shared prefix once, every suffix), and it also reports the
 logical bytes plain decode would read. --cold adds launches timed after a
 1 GiB write that evicts the caches (a small layer such as qwen's otherwise
 stays in the 256 MB MALL between iterations).
+
+--workload prefill times one chunked-prefill step (four 2048-token chunks at
+contexts 2048..8192, fp16, the 32/8-head d-128 shape) in TFLOP/s against the
+matrix-core peak; --workload prefill_small times eight 16-token chunks over
+8192-token contexts (keys split over workgroups through the workspace; HBM
+bound) and also reports the unsplit launch. Both warm up for at least
+PREFILL_MIN_WARMUP_S before timing, since a launch is too short for the clock
+to settle within a few warm-up steps.
 """
 import argparse
 import json
