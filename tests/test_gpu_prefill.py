@@ -207,3 +207,33 @@ def test_split_not_used_for_many_rows(gpu):
     c = gpu_prefill(b, q, qs)
     torch.cuda.synchronize()
     assert torch.equal(a, c)
+
+
+# ---- seeded random shapes: every cache type, head grouping and chunk mix ----
+_TYPES = [("bf16", "bf16"), ("f16", "f16"), ("fp8", "bf16"), ("fp8", "f16"), ("f32", "f32")]
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_shapes_match_oracle(gpu, seed):
+    """Random batches (seeded): 1..5 sequences with contexts 1..1200 and chunks
+    of 0 up to the whole context (short chunks favoured), G = 1..8, d 64/128,
+    every cache type, with and without the split workspace; every row is
+    compared with the oracle."""
+    rng = np.random.default_rng(9000 + seed)
+    kv, qd = _TYPES[seed % len(_TYPES)]
+    d = (64, 128)[int(rng.integers(0, 2))]
+    G = int(rng.integers(1, 9))
+    H = int(rng.integers(1, 4))
+    S = int(rng.integers(1, 6))
+    ctx = [int(rng.integers(1, 1201)) for _ in range(S)]
+    q_lens = [min(c, int(rng.integers(0, 41)) if rng.random() < 0.5 else int(rng.integers(0, c + 1)))
+              for c in ctx]
+    if sum(q_lens) == 0:
+        q_lens[0] = ctx[0]
+    b, q, qs = make(2000 + seed, ctx, q_lens, kv, qd, G * H, H, d, gpu)
+    ws = B.prefill_workspace(d, gpu) if rng.random() < 0.5 else None
+    what = f"seed {seed}: {kv}/{qd} d={d} G={G} H={H} ctx={ctx} q={q_lens} split={ws is not None}"
+    print(f"[case] {what}", flush=True)
+    got = out_to_f64(gpu_prefill(b, q, qs, workspace=ws))
+    e = assert_close(got, oracle_rows(b, q, qs), kv, what)
+    print(f"[parity] {what}: {e}", flush=True)
