@@ -39,10 +39,47 @@ __device__ __forceinline__ void copy1(uint8_t* dst, const uint8_t* src, int eb) 
 
 }  // namespace
 
+// One 8-element group of EB-byte elements as dwords (EB 1: 2, 2: 4, 4: 8).
+template <int EB>
+struct Group {
+    uint32_t w[2 * EB];
+    __device__ __forceinline__ void load(const uint8_t* src) {
+        if constexpr (EB == 1) {
+            const uint2 a = *reinterpret_cast<const uint2*>(src);
+            w[0] = a.x, w[1] = a.y;
+        } else {
+#pragma unroll
+            for (int i = 0; i < EB / 2; ++i) {
+                const uint4 a = reinterpret_cast<const uint4*>(src)[i];
+                w[4 * i] = a.x, w[4 * i + 1] = a.y, w[4 * i + 2] = a.z, w[4 * i + 3] = a.w;
+            }
+        }
+    }
+    __device__ __forceinline__ void store(uint8_t* dst) const {
+        if constexpr (EB == 1) {
+            *reinterpret_cast<uint2*>(dst) = uint2{w[0], w[1]};
+        } else {
+#pragma unroll
+            for (int i = 0; i < EB / 2; ++i)
+                reinterpret_cast<uint4*>(dst)[i] = uint4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+        }
+    }
+    // element e (0..7)
+    __device__ __forceinline__ void store_elem(uint8_t* dst, int e) const {
+        if constexpr (EB == 4)
+            *reinterpret_cast<uint32_t*>(dst) = w[e];
+        else if constexpr (EB == 2)
+            *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+        else
+            *dst = (uint8_t)(w[e >> 2] >> (8 * (e & 3)));
+    }
+};
+
+template <int EB>
 __global__ __launch_bounds__(256) void kv_append_kernel(
     const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
     const int64_t* __restrict__ slot_mapping, int num_tokens, uint8_t* __restrict__ k_cache,
-    uint8_t* __restrict__ v_cache, int num_blocks, int num_kv_heads, int head_dim, int eb) {
+    uint8_t* __restrict__ v_cache, int num_blocks, int num_kv_heads, int head_dim) {
     const int groups = head_dim / 8;
     const int64_t total = (int64_t)num_tokens * num_kv_heads * groups;
     for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
@@ -51,15 +88,19 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
         const int64_t row = idx / groups;  // token * H + g
         const int g = (int)(row % num_kv_heads);
         const int64_t tok = row / num_kv_heads;
+        // The source group's address does not depend on the slot, so its K
+        // and V are read together with the slot: one memory latency, not two.
+        const size_t src = ((size_t)row * head_dim + (size_t)c * 8) * EB;
+        Group<EB> kg, vg;
+        kg.load(k + src);
+        vg.load(v + src);
         const int64_t slot = slot_mapping[tok];
         if (slot < 0 || slot >= (int64_t)num_blocks * kBlock) continue;
         const int t = (int)(slot % kBlock);
         const size_t tile = tile_elem_offset(slot / kBlock, g, num_kv_heads, head_dim);
-        const size_t src = ((size_t)row * head_dim + (size_t)c * 8) * eb;
-        copy8(k_cache + (tile + k_elem_index(t, c * 8)) * eb, k + src, eb);
+        kg.store(k_cache + (tile + k_elem_index(t, c * 8)) * EB);
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            copy1(v_cache + (tile + v_elem_index(t, c * 8 + e)) * eb, v + src + (size_t)e * eb, eb);
+        for (int e = 0; e < 8; ++e) vg.store_elem(v_cache + (tile + v_elem_index(t, c * 8 + e)) * EB, e);
     }
 }
 
@@ -178,11 +219,18 @@ hipError_t launch_kv_append(const void* k, const void* v, int elem_bytes,
     const int64_t total = (int64_t)num_tokens * num_kv_heads * (head_dim / 8);
     int64_t blocks = (total + 255) / 256;
     if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       static_cast<const uint8_t*>(k), static_cast<const uint8_t*>(v),
-                       slot_mapping, num_tokens, static_cast<uint8_t*>(k_cache),
-                       static_cast<uint8_t*>(v_cache), num_blocks, num_kv_heads, head_dim,
-                       elem_bytes);
+    auto args = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           static_cast<const uint8_t*>(k), static_cast<const uint8_t*>(v),
+                           slot_mapping, num_tokens, static_cast<uint8_t*>(k_cache),
+                           static_cast<uint8_t*>(v_cache), num_blocks, num_kv_heads, head_dim);
+    };
+    if (elem_bytes == 4)
+        args(kv_append_kernel<4>);
+    else if (elem_bytes == 2)
+        args(kv_append_kernel<2>);
+    else
+        args(kv_append_kernel<1>);
     return hipGetLastError();
 }
 
