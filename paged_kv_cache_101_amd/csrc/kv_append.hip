@@ -166,14 +166,16 @@ __global__ __launch_bounds__(256) void kv_append_fp8_kernel(
         const int64_t row = idx / groups;  // token * H + g
         const int g = (int)(row % num_kv_heads);
         const int64_t tok = row / num_kv_heads;
-        const int64_t slot = slot_mapping[tok];
-        if (slot < 0 || slot >= (int64_t)num_blocks * kBlock) continue;
-        const int t = (int)(slot % kBlock);
-        const size_t tile = tile_elem_offset(slot / kBlock, g, num_kv_heads, head_dim);
+        // the source rows are read together with the slot (their addresses
+        // do not depend on it)
         const size_t src = ((size_t)row * head_dim + (size_t)c * 8) * SB;
         float kf[8], vf[8];
         load8_f32<SRC>(k + src, kf);
         load8_f32<SRC>(v + src, vf);
+        const int64_t slot = slot_mapping[tok];
+        if (slot < 0 || slot >= (int64_t)num_blocks * kBlock) continue;
+        const int t = (int)(slot % kBlock);
+        const size_t tile = tile_elem_offset(slot / kBlock, g, num_kv_heads, head_dim);
         uint32_t lo = 0, hi = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
