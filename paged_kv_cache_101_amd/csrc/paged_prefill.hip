@@ -963,6 +963,9 @@ __global__ __launch_bounds__(kMergeThreads) void chunk_merge_kernel(PrefillParam
     const float* slot0 = p.slots + (size_t)(t16 + (int64_t)rb16 * (H * C) + g * C) * SLOT;
     const float lse = PFX ? p.res_lse[orow] : -INFINITY;
     float M = lse;
+    // eight chunks' loads in flight at a time (a loop that is not unrolled
+    // waits for each load before issuing the next)
+#pragma unroll 8
     for (int cc = 0; cc < C; ++cc) M = fmaxf(M, slot0[(size_t)cc * SLOT + 16 * D + r]);
     const float ws = PFX ? __builtin_amdgcn_exp2f(lse - M) : 0.f;
     float L = ws;
@@ -974,7 +977,7 @@ __global__ __launch_bounds__(kMergeThreads) void chunk_merge_kernel(PrefillParam
 #pragma unroll
         for (int x = 0; x < 4; ++x) acc[i + x] = ws * so[x];
     }
-#pragma unroll 4
+#pragma unroll 8
     for (int cc = 0; cc < C; ++cc) {
         const float* sl = slot0 + (size_t)cc * SLOT;
         // a chunk where the row saw no key holds m = -inf, l = 0 and zeros
