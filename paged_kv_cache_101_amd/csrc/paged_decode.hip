@@ -114,9 +114,11 @@ __device__ __forceinline__ int worker_of(int64_t f, int64_t total, int nw) {
 // in its slot k0, the others in slot 0), into the output rows orow..orow+G-1:
 //   M = max_j m_j,  out = sum_j 2^(m_j - M) acc_j / sum_j 2^(m_j - M) l_j.
 // With at most 64 partials (the usual case), lane j reads partial j's maxima
-// and sums once and the accumulators of 16 partials are in flight at a time;
-// with more, the maxima and the sums are read in passes of 64 partials and 8
-// accumulators are in flight.
+// and sums once; with more, they are read in passes of 64 partials. The
+// accumulator loops hold cross-lane reads, so the compiler does not unroll
+// them: one partial's loads are in flight at a time. (Fixed batches of 16 that
+// do unroll, with clamped indices past the last partial, were twice as slow
+// on short streams.)
 template <int QT, int D, int GM>
 __device__ __forceinline__ void merge_segment(const DecodeParams& p, int w0, int w1,
                                                         int k0, int G, size_t orow, int lane,
@@ -148,7 +150,6 @@ __device__ __forceinline__ void merge_segment(const DecodeParams& p, int w0, int
             c[h] = lane < nparts ? __builtin_amdgcn_exp2f(mj - mx[h]) : 0.f;
             lsum[h] = wave_sum(lj * c[h]);
         }
-#pragma unroll 16
         for (int jj = 0; jj < nparts; ++jj) {
             const float* sj = slot_of(jj);
 #pragma unroll
@@ -182,7 +183,6 @@ __device__ __forceinline__ void merge_segment(const DecodeParams& p, int w0, int
                 lsum[h] += wave_sum(j < nparts ? coherent_load(sl + GM * D + GM + h) * c[h] : 0.f);
             }
             const int cnt = min(kWave, nparts - j0);
-#pragma unroll 8
             for (int jj = 0; jj < cnt; ++jj) {
                 const float* sl = slot_of(j0 + jj);
 #pragma unroll

@@ -191,7 +191,7 @@ PKV_EXPORT size_t pkv_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t nu
     if (pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, num_workers) == 0 ||
         num_groups < 0 || num_groups > num_seqs)
         return 0;
-    return pkv::shared_prefix_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, num_groups,
+    return pkv::shared_prefix_layout(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                      num_workers == 0 ? pkv::kMaxWorkers : num_workers)
         .total;
 }
@@ -216,7 +216,7 @@ PKV_EXPORT int pkv_paged_attention_decode_shared_prefix(
         return PKV_ERR_WORKSPACE;
     const pkv::SharedPrefixLayout l =
         pkv::shared_prefix_layout(num_seqs, num_q_heads, cache->num_kv_heads, cache->head_dim,
-                                  num_groups, num_workers == 0 ? pkv::kMaxWorkers : num_workers);
+                                  num_workers == 0 ? pkv::kMaxWorkers : num_workers);
     char* ws = static_cast<char*>(workspace);
     const size_t dctr = pkv::tail_offset(workspace_bytes, l.decode_counter_bytes);
     a.counters = reinterpret_cast<int*>(ws + dctr);

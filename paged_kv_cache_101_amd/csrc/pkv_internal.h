@@ -77,7 +77,7 @@ struct SharedPrefixLayout {
     size_t total;
 };
 inline SharedPrefixLayout shared_prefix_layout(int num_seqs, int num_q_heads, int num_kv_heads,
-                                               int head_dim, int num_groups, int workers) {
+                                               int head_dim, int workers) {
     SharedPrefixLayout l;
     size_t off = decode_slot_bytes(num_q_heads, num_kv_heads, head_dim, workers);
     l.res_o = off;
