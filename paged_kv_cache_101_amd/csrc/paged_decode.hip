@@ -114,11 +114,9 @@ __device__ __forceinline__ int worker_of(int64_t f, int64_t total, int nw) {
 // in its slot k0, the others in slot 0), into the output rows orow..orow+G-1:
 //   M = max_j m_j,  out = sum_j 2^(m_j - M) acc_j / sum_j 2^(m_j - M) l_j.
 // With at most 64 partials (the usual case), lane j reads partial j's maxima
-// and sums once; with more, they are read in passes of 64 partials. The
-// accumulator loops hold cross-lane reads, so the compiler does not unroll
-// them: one partial's loads are in flight at a time. (Fixed batches of 16 that
-// do unroll, with clamped indices past the last partial, were twice as slow
-// on short streams.)
+// and sums once, and the accumulators of several partials are in flight at a
+// time; with more, the maxima and sums are read in passes of 64 partials and
+// one partial's accumulators are in flight at a time.
 template <int QT, int D, int GM>
 __device__ __forceinline__ void merge_segment(const DecodeParams& p, int w0, int w1,
                                                         int k0, int G, size_t orow, int lane,
@@ -150,16 +148,22 @@ __device__ __forceinline__ void merge_segment(const DecodeParams& p, int w0, int
             c[h] = lane < nparts ? __builtin_amdgcn_exp2f(mj - mx[h]) : 0.f;
             lsum[h] = wave_sum(lj * c[h]);
         }
+        // Every lane forms partial jj's weights itself from its maxima (one
+        // address for the whole wave), so the loop holds no cross-lane read
+        // and unrolls: the loads of four partials (two with 16 accumulator
+        // elements per lane, where four measured 30% slower) are in flight
+        // at a time.
+        constexpr int kMergeUnroll = PER_LANE <= 12 ? 4 : 2;
+#pragma unroll kMergeUnroll
         for (int jj = 0; jj < nparts; ++jj) {
             const float* sj = slot_of(jj);
+            float wj[GM];
+#pragma unroll
+            for (int h = 0; h < GM; ++h) wj[h] = __builtin_amdgcn_exp2f(coherent_load(sj + GM * D + h) - mx[h]);
 #pragma unroll
             for (int i = 0; i < PER_LANE; ++i) {
                 const int idx = i * kWave + lane;  // h * D + e
-                if (idx < GM * D) {
-                    const int cj = __builtin_amdgcn_readlane(
-                        __builtin_bit_cast(int, c[(i * kWave) / D]), jj);
-                    o[i] = fmaf(__builtin_bit_cast(float, cj), coherent_load(sj + idx), o[i]);
-                }
+                if (idx < GM * D) o[i] = fmaf(wj[(i * kWave) / D], coherent_load(sj + idx), o[i]);
             }
         }
     } else {
