@@ -189,12 +189,19 @@ def cpu_baseline(layer, target_s: float):
         k = max(1, min(S, int(target_s / max(el, 1e-3))))
         if k > 1:
             el = run(k)
+    # a whole layer that still takes well under the target is timed over
+    # several passes (at most 10), and the mean pass is reported
+    passes = 1
+    if k == S and el < target_s / 2:
+        passes = min(10, max(2, int(target_s / max(el, 1e-3))))
+        el = sum(run(k) for _ in range(passes)) / passes
     tokens = int(h["ctx"][:k].clip(min=0).sum())
     return {
         "value": round(tokens * bpt / el / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
         "kind": "oracle",
         "sample": f"layer 0, sequences 0..{k - 1} of {S} (all {layer.num_q_heads} query heads), "
-                  f"{tokens} tokens, {tokens * bpt} KV bytes, {el:.2f} s",
+                  f"{tokens} tokens, {tokens * bpt} KV bytes, {el:.2f} s per pass, "
+                  f"mean of {passes} pass{'es' if passes > 1 else ''}",
         "seqs_per_s": round(k / el, 4),
     }
 
