@@ -1,0 +1,87 @@
+"""GPU: the library's calls captured in a HIP graph (torch.cuda.graph) and
+replayed. The calls allocate nothing, never synchronise and leave their
+workspace counters at zero, so a captured step must give the eager result on
+every replay. Each graph is replayed several times with eager work (the
+outputs overwritten with NaN) and synchronisations between replays, and every
+replay is compared bit for bit with the eager run, which is itself checked
+against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_cache_101_amd import binding as B
+from paged_kv_cache_101_amd import workloads as W
+from tests.helpers import assert_close, desc, device_caches, host_copy, oracle_decode, out_to_f64
+
+pytestmark = pytest.mark.gpu
+REPLAYS = 4
+
+
+def _capture_and_replay(step, outs):
+    step()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for r in range(REPLAYS):
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (o, e) in enumerate(zip(outs, eager)):
+            assert torch.equal(o, e), f"replay {r}, output {i} differs from the eager run"
+    return eager
+
+
+def test_append_and_decode_step_replayed(gpu):
+    """Two layers of the GQA shape (6 sequences of 2048 tokens): per layer the
+    new token's rows are appended, then decoded, as in the benchmark's step."""
+    layers = [W.gqa40_layer(device=gpu, layer=l, num_seqs=6, ctx=2048, append_last=True,
+                            canary=True) for l in range(2)]
+    hosts = [host_copy(b) for b in layers]
+    caches = [device_caches(b) for b in layers]
+    descs = [desc(b) for b in layers]
+    ws = B.decode_workspace(6, 32, 8, 128, 0, gpu)
+    outs = [torch.empty_like(b.q) for b in layers]
+
+    def step():
+        for i, b in enumerate(layers):
+            B.pkv_kv_append(b.new_k, b.new_v, b.slot_mapping, *caches[i], descs[i])
+            B.pkv_paged_attention_decode(b.q, *caches[i], descs[i], b.block_tables,
+                                         b.context_lens, b.scale, outs[i], workspace=ws)
+
+    eager = _capture_and_replay(step, outs)
+    for i, (b, h) in enumerate(zip(layers, hosts)):
+        oracle.kv_append(W.to_numpy(b.new_k), W.to_numpy(b.new_v), b.slot_mapping.cpu().numpy(),
+                         h["k_cache"], h["v_cache"])
+        ref = oracle.paged_decode(h["q"], h["k_cache"], h["v_cache"], h["bt"], h["ctx"], b.scale)
+        assert_close(out_to_f64(eager[i]), ref, "f16", f"graph step, layer {i}")
+
+
+def test_shared_prefix_call_replayed(gpu):
+    """The shared-prefix decode (three launches: suffix pass, prefix pass and
+    the chunk merge) of 24 sequences sharing a 256-token prefix."""
+    ctx = W.prefix_shared_lengths(24, 256)
+    b = W.make_batch("prefix-graph", 55, ctx, 32, 8, 128, "bf16", "bf16", device=gpu,
+                     shared_prefix_blocks=16, canary=True)
+    kc, vc = device_caches(b)
+    ws = B.shared_prefix_workspace(b.num_seqs, 32, 8, 128, int(b.group_prefix.numel()), 0, gpu)
+    out = torch.empty_like(b.q)
+
+    def step():
+        B.pkv_paged_attention_decode_shared_prefix(b.q, kc, vc, desc(b), b.block_tables,
+                                                   b.context_lens, b.group_starts, b.group_prefix,
+                                                   b.scale, out, workspace=ws)
+
+    eager = _capture_and_replay(step, [out])
+    assert_close(out_to_f64(eager[0]), oracle_decode(b), "bf16", "graph shared-prefix call")
