@@ -1,5 +1,5 @@
-"""GPU: the library's calls captured in a HIP graph (torch.cuda.graph) and
-replayed. The calls allocate nothing, never synchronise and leave their
+"""GPU: the library's calls (append + decode, the shared-prefix decode, the
+split-key prefill) captured in a HIP graph (torch.cuda.graph) and replayed. The calls allocate nothing, never synchronise and leave their
 workspace counters at zero, so a captured step must give the eager result on
 every replay. Each graph is replayed several times with eager work (the
 outputs overwritten with NaN) and synchronisations between replays, and every
@@ -85,3 +85,29 @@ def test_shared_prefix_call_replayed(gpu):
 
     eager = _capture_and_replay(step, [out])
     assert_close(out_to_f64(eager[0]), oracle_decode(b), "bf16", "graph shared-prefix call")
+
+
+def test_split_prefill_replayed(gpu):
+    """Chunked prefill with the split-key workspace (the attention launch and
+    the chunk merge): short chunks over long contexts."""
+    ctx, q_lens = [3000, 1200, 2047], [16, 5, 40]
+    b = W.make_batch("prefill-graph", 56, ctx, 32, 8, 128, "f16", "f16", device=gpu,
+                     pool_factor=1.2, canary=True)
+    kc, vc = device_caches(b)
+    g = torch.Generator(device=gpu)
+    g.manual_seed(56)
+    T = sum(q_lens)
+    q = torch.randn((T, 32, 128), generator=g, device=gpu).to(torch.float16)
+    qs = torch.tensor(np.concatenate([[0], np.cumsum(q_lens)]), dtype=torch.int32, device=gpu)
+    out = torch.empty_like(q)
+    ws = B.prefill_workspace(128, gpu)
+
+    def step():
+        B.pkv_paged_attention_prefill(q, kc, vc, desc(b), b.block_tables, b.context_lens, qs,
+                                      b.scale, out, workspace=ws)
+
+    eager = _capture_and_replay(step, [out])
+    ref = oracle.paged_prefill(W.to_numpy(q), W.to_numpy(b.k_cache), W.to_numpy(b.v_cache),
+                               b.block_tables.cpu().numpy(), b.context_lens.cpu().numpy(),
+                               qs.cpu().numpy(), b.scale)
+    assert_close(out_to_f64(eager[0]), ref, "f16", "graph split prefill")
