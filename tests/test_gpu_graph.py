@@ -1,10 +1,11 @@
 """GPU: the library's calls (append + decode, the shared-prefix decode, the
-split-key prefill) captured in a HIP graph (torch.cuda.graph) and replayed. The calls allocate nothing, never synchronise and leave their
-workspace counters at zero, so a captured step must give the eager result on
-every replay. Each graph is replayed several times with eager work (the
-outputs overwritten with NaN) and synchronisations between replays, and every
-replay is compared bit for bit with the eager run, which is itself checked
-against the oracle."""
+split-key prefill) captured in a HIP graph (torch.cuda.graph) and replayed.
+The calls allocate nothing, never synchronise and leave their workspace
+counters at zero, so a captured step must give the eager result on every
+replay. Each graph is replayed several times with eager work (the outputs
+overwritten with NaN) and synchronisations between replays, and every replay
+is compared bit for bit with the eager run, which is itself checked against
+the oracle."""
 import numpy as np
 import pytest
 import torch
