@@ -77,6 +77,9 @@ def parse():
                              "prefill", "prefill_small"])
     ap.add_argument("--workers", type=int, default=0, help="worker waves (0 = fill the device)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured in a HIP graph and replayed (reported as "
+                         "a 'graph' object; value and roofline stay the eager, event-timed run)")
     ap.add_argument("--cold", action="store_true",
                     help="also time decode launches that each follow a 1 GiB device write, "
                          "which evicts the L2 caches and the 256 MB MALL (the timed launch then "
@@ -434,6 +437,34 @@ def main():
         "launch_p10_us": round(sorted(decode_ms)[len(decode_ms) // 10] * 1e3, 2),
         "launch_p90_us": round(sorted(decode_ms)[(9 * len(decode_ms)) // 10] * 1e3, 2),
     }
+    graph = None
+    if args.graph:
+        # the whole step (every append and decode launch) captured once and
+        # replayed: the launches are the same, only the host submission and
+        # the dispatch gaps between dependent kernels change
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        gms = g0.elapsed_time(g1) / args.steps
+        graph = {"ms_per_step": round(gms, 4), "value": round(kv_bytes_step / (gms * 1e-3) / 1e9, 1),
+                 "unit": "GB/s", "steps": args.steps}
+        del g
     cold = None
     if args.cold:
         # a 1 GiB write before every decode launch, outside its events
@@ -473,6 +504,8 @@ def main():
     }
     if cold is not None:
         line["cold"] = cold
+    if graph is not None:
+        line["graph"] = graph
     if shared:
         line["logical_kv_bytes_per_launch"] = logical_launch
         line["logical_kv_gbps"] = round(logical_launch / (decode_avg_ms * 1e-3) / 1e9, 1)
