@@ -111,13 +111,19 @@ def _check(fn: str, rc: int):
 
 
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # a plain int: the argtypes (c_void_p) convert it without a wrapper object
+    return None if t is None else t.data_ptr()
 
 
-def _stream(stream) -> ctypes.c_void_p:
+def _stream(stream) -> int:
+    """The stream handle: the given torch stream's, or the current stream of
+    the current device, read directly rather than through a Stream object.
+    With plain int pointers this took a decode call's host cost from 10.5 to
+    7.4 us (the bare C call: 3.9 us), which matters when a step is dozens of
+    short launches."""
     if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
+        return torch._C._cuda_getCurrentRawStream(torch.cuda.current_device())
+    return stream.cuda_stream
 
 
 def _need(cond: bool, msg: str):
