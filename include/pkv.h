@@ -24,7 +24,10 @@
  *    state between calls and is safe to call from several host threads.
  *  - Work is enqueued on the given HIP stream (NULL = the null stream) and
  *    never synchronised: results are visible after the stream reaches the
- *    point of the call.
+ *    point of the call. No call issues a memset, a copy or a host
+ *    synchronisation, and workspaces keep their counters at zero from call
+ *    to call, so a sequence of calls may be captured in a HIP graph and
+ *    replayed (with the same buffers, which replays reuse).
  *  - Argument errors that the host can see (null pointers, sizes, dtypes)
  *    return before any HIP call; launch failures return PKV_ERR_HIP.
  *  - Values in device memory (block ids, slots, lengths) are not read by the
