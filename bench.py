@@ -76,6 +76,8 @@ def parse():
                     choices=["gqa40", "gqa40_tp8", "qwen", "prefix", "prefix_shared", "fp8", "tiny",
                              "prefill", "prefill_small"])
     ap.add_argument("--workers", type=int, default=0, help="worker waves (0 = fill the device)")
+    ap.add_argument("--partition-size", type=int, default=0,
+                    help="decode split: 0 = balanced split, else tokens per fixed partition")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured in a HIP graph and replayed (reported as "
@@ -367,7 +369,7 @@ def main():
                                        ng, args.workers, dev)
     else:
         ws = B.decode_workspace(b0.num_seqs, b0.num_q_heads, b0.num_kv_heads, b0.head_dim,
-                                args.workers, dev)
+                                args.workers, dev, b0.max_blocks_per_seq, args.partition_size)
     do_append = args.workload in ("gqa40", "gqa40_tp8")
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
@@ -381,7 +383,8 @@ def main():
         else:
             B.pkv_paged_attention_decode(b.q, *caches[i], descs[i], b.block_tables,
                                          b.context_lens, b.scale, outs[i],
-                                         num_workers=args.workers, workspace=ws)
+                                         num_workers=args.workers, workspace=ws,
+                                         partition_size=args.partition_size)
 
     def step(evs=None):
         for i, b in enumerate(layers):

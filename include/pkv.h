@@ -20,8 +20,10 @@
  *  - Every function returns an int status: PKV_OK or a negative PKV_ERR_*.
  *    pkv_status_string() names it.
  *  - All buffers are caller-owned, contiguous, row-major device memory
- *    unless a parameter says "host". The library allocates nothing, keeps no
- *    state between calls and is safe to call from several host threads.
+ *    unless a parameter says "host". The library allocates nothing and keeps
+ *    no state between calls beyond constants of the device it reads once (the
+ *    compute-unit count per device, each decode kernel's occupancy), and is
+ *    safe to call from several host threads.
  *  - Work is enqueued on the given HIP stream (NULL = the null stream) and
  *    never synchronised: results are visible after the stream reaches the
  *    point of the call. No call issues a memset, a copy or a host
@@ -153,25 +155,33 @@ int pkv_kv_append(const void *k, const void *v, int32_t kv_dtype, const int64_t 
 /* Largest number of worker waves one decode launch uses. */
 #define PKV_MAX_WORKERS 4096
 
-/* Workspace bytes pkv_paged_attention_decode needs for this batch shape and
- * worker count (num_workers 0 = the device default, sized for
- * PKV_MAX_WORKERS): 2 * workers float partial slots of Gp * head_dim +
- * pad(2 * Gp) floats each at the front, Gp being G = num_q_heads /
- * num_kv_heads rounded up to 1, 2, 4, 6 or 8 and pad() rounding up to a
- * multiple of 4; int32 counters [num_seqs][num_kv_heads] in the last bytes;
- * each part rounded up to 256 bytes. Returns 0 for invalid arguments
- * (non-positive sizes, G not a whole number or above 8, num_workers < 0 or
- * > PKV_MAX_WORKERS).
+/* Workspace bytes pkv_paged_attention_decode needs for this batch shape,
+ * partition size and worker count. Gp is G = num_q_heads / num_kv_heads
+ * rounded up to 1, 2, 4, 6 or 8, and one partial slot holds Gp * head_dim +
+ * pad(2 * Gp) floats (an accumulator row, a maximum and a sum per head;
+ * pad() rounds up to a multiple of 4). Front, float partial slots:
+ *   partition_size == 0 (balanced split): 2 * workers slots, workers =
+ *     num_workers or PKV_MAX_WORKERS for num_workers 0;
+ *   partition_size  > 0 (fixed partitions): one slot per (sequence, KV head,
+ *     partition), num_seqs * num_kv_heads * Pn slots with
+ *     Pn = ceil(max_blocks_per_seq * 16 / partition_size); for G = 2, 4, 6
+ *     or 8 that is num_seqs * num_q_heads * Pn * (head_dim + 2) floats.
+ * End: int32 counters [num_seqs][num_kv_heads]. Each part is rounded up to
+ * 256 bytes. Returns 0 for invalid arguments (non-positive sizes, G not a
+ * whole number or above 8, a partition size that is negative or not a
+ * multiple of 16, num_workers < 0 or > PKV_MAX_WORKERS).
  *
  * Workspace rule (both decode entry points): the counters sit in the last
  * bytes of the workspace as passed (workspace_bytes rounded down to 256) and
  * must be zero when a call starts; every call leaves them zero. Float
  * scratch sits at the front. So a workspace sized for the largest shape a
- * caller runs (num_seqs, num_groups, num_workers; same heads and head_dim)
- * and zeroed once serves any call of that shape or smaller, passed with the
- * same workspace_bytes, without being cleared again. */
+ * caller runs (num_seqs, max_blocks_per_seq, num_groups, num_workers; same
+ * heads, head_dim and partition size) and zeroed once serves any call of
+ * that shape or smaller, passed with the same workspace_bytes, without being
+ * cleared again. */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                                  int32_t head_dim, int32_t num_workers);
+                                  int32_t head_dim, int32_t max_blocks_per_seq,
+                                  int32_t partition_size, int32_t num_workers);
 
 /* Paged decode attention: one new query token per sequence attends over its
  * own cached tokens, read through its block table.
@@ -188,12 +198,20 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  * row. Arithmetic is float32; the result is rounded to nearest-even into
  * q_dtype.
  *
- * Split-KV: the (sequence, KV head, 16-token block) tiles of the whole batch
- * are split evenly over num_workers waves, so a long (sequence, KV head) may
- * be shared by several waves; each leaves a partial (max, sum, accumulator)
- * and the last one to finish merges them by the log-sum-exp rule. Results
- * depend on num_workers only through float32 rounding, and are bit-for-bit
- * repeatable for a fixed num_workers and device.
+ * Split-KV, two ways (results depend on the split only through float32
+ * rounding, and are bit-for-bit repeatable for a fixed split and device):
+ *  - partition_size == 0, the balanced split: the (sequence, KV head,
+ *    16-token block) tiles of the whole batch are split evenly over
+ *    num_workers waves, so a long (sequence, KV head) may be shared by
+ *    several waves; each leaves a partial (max, sum, accumulator) and the
+ *    last one to finish merges them by the log-sum-exp rule.
+ *  - partition_size = P > 0, fixed partitions: the tokens of each (sequence,
+ *    KV head) are cut into partitions [j * P, min((j + 1) * P, n)); the
+ *    partitions of the batch are split evenly over num_workers waves (whole
+ *    partitions each); every partition of a sequence with more than one
+ *    leaves its partial (max, sum, accumulator) in its own workspace slot,
+ *    and a second launch on the stream reduces them by the log-sum-exp rule
+ *    (one wave per sequence and query head).
  *
  *  q             [num_seqs][num_q_heads][head_dim] in q_dtype (device)
  *  q_dtype       (q, cache) pairs: (F32, F32), (F16, F16), (BF16, BF16),
@@ -204,8 +222,12 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *                first ceil(n / 16) entries of a row are read
  *  context_lens  int32 [num_seqs] (device)
  *  scale         softmax scale applied to q . k (typically 1/sqrt(head_dim))
- *  num_workers   waves sharing the work: 0 = enough to fill the device,
- *                otherwise 1..PKV_MAX_WORKERS
+ *  partition_size  0 (balanced split) or tokens per fixed partition, a
+ *                positive multiple of 16
+ *  num_workers   waves sharing the work: 0 = enough to fill the device (with
+ *                fixed partitions: the waves that give every wave about the
+ *                same whole number of partitions of a batch of full-length
+ *                sequences), otherwise 1..PKV_MAX_WORKERS
  *  workspace, workspace_bytes  at least pkv_decode_workspace_bytes(...) of
  *                device memory, 256-byte aligned, zeroed before its first
  *                use (see the workspace rule above). Two calls must not use
@@ -214,13 +236,15 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *                not alias any input or the workspace
  * A sequence whose length exceeds max_blocks_per_seq * 16, or whose needed
  * block ids fall outside [0, num_blocks), gets a NaN row (no out-of-range
- * read happens). Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP. */
+ * read happens). Errors: INVALID_ARG (also a partition size that is negative
+ * or not a multiple of 16), UNSUPPORTED, WORKSPACE, HIP. */
 int pkv_paged_attention_decode(const void *q, int32_t q_dtype, int32_t num_seqs,
                                int32_t num_q_heads, const void *k_cache, const void *v_cache,
                                const pkv_cache_desc *cache, const int32_t *block_tables,
                                int32_t max_blocks_per_seq, const int32_t *context_lens,
-                               float scale, int32_t num_workers, void *workspace,
-                               size_t workspace_bytes, void *out, hipStream_t stream);
+                               float scale, int32_t partition_size, int32_t num_workers,
+                               void *workspace, size_t workspace_bytes, void *out,
+                               hipStream_t stream);
 
 /* Workspace bytes pkv_paged_attention_decode_shared_prefix needs. Front:
  * the decode slots for the worker count, float32 suffix results

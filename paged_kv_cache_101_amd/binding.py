@@ -78,10 +78,10 @@ def lib():
         L.pkv_cache_tensor_bytes.restype = sz
         L.pkv_kv_append.argtypes = [vp, vp, i32, vp, i32, vp, vp, descp, vp]
         L.pkv_kv_append.restype = ctypes.c_int
-        L.pkv_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+        L.pkv_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
         L.pkv_decode_workspace_bytes.restype = sz
         L.pkv_paged_attention_decode.argtypes = [vp, i32, i32, i32, vp, vp, descp, vp, i32, vp,
-                                                 f32, i32, vp, sz, vp, vp]
+                                                 f32, i32, i32, vp, sz, vp, vp]
         L.pkv_paged_attention_decode.restype = ctypes.c_int
         L.pkv_shared_prefix_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
         L.pkv_shared_prefix_workspace_bytes.restype = sz
@@ -149,7 +149,57 @@ def _dtype_of(t: torch.Tensor, declared: Optional[str] = None) -> int:
         return PKV_FP8_E4M3
     if t.dtype == torch.float8_e4m3fn:
         return PKV_FP8_E4M3
+    _need(t.dtype in _TORCH_CODES, f"unsupported tensor dtype {t.dtype}")
     return _TORCH_CODES[t.dtype]
+
+
+# bytes per element of each dtype code (pkv_dtype)
+_ELEM_BYTES = {PKV_F32: 4, PKV_F16: 2, PKV_BF16: 2, PKV_FP8_E4M3: 1}
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
+def _check_desc_caches(desc: pkv_cache_desc, k_cache: torch.Tensor, v_cache: torch.Tensor):
+    """The caches must hold the pool the descriptor describes (the C side
+    cannot see tensor sizes, so a descriptor larger than the tensors would
+    make the kernels read or write past their ends)."""
+    eb = _ELEM_BYTES.get(desc.dtype)
+    _need(eb is not None, f"descriptor dtype {desc.dtype} unknown")
+    need = desc.num_blocks * desc.num_kv_heads * PKV_BLOCK_SIZE * desc.head_dim * eb
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _need(_nbytes(t) >= need,
+              f"{name} holds {_nbytes(t)} bytes, the descriptor's pool needs {need}")
+        _need(_dtype_of(t, "fp8" if desc.dtype == PKV_FP8_E4M3 else None) == desc.dtype
+              or (desc.dtype == PKV_FP8_E4M3 and t.dtype == torch.uint8),
+              f"{name} dtype {t.dtype} does not match the descriptor")
+
+
+def _check_rows(name: str, t: torch.Tensor, desc: pkv_cache_desc, heads: Optional[int] = None):
+    """t: [rows][heads][desc.head_dim]; heads a multiple of desc.num_kv_heads
+    (query heads, at most 8 per KV head) unless given exactly."""
+    _need(t.dim() == 3, f"{name} must be [rows][heads][head_dim]")
+    _need(t.shape[2] == desc.head_dim,
+          f"{name} head_dim {t.shape[2]} != descriptor head_dim {desc.head_dim}")
+    if heads is not None:
+        _need(t.shape[1] == heads, f"{name} has {t.shape[1]} heads, expected {heads}")
+    else:
+        _need(t.shape[1] % desc.num_kv_heads == 0,
+              f"{name} heads {t.shape[1]} not a multiple of num_kv_heads {desc.num_kv_heads}")
+
+
+def _check_device(*ts):
+    for t in ts:
+        _need(t.is_contiguous() and t.is_cuda, "all tensors must be contiguous device tensors")
+
+
+def _no_capture(what: str):
+    """Allocating a workspace from torch inside a graph capture would record a
+    memset into the graph: the caller must pass one made beforehand."""
+    if torch.cuda.is_available() and torch.cuda.is_current_stream_capturing():
+        raise RuntimeError(f"{what}: pass a workspace made before the graph capture "
+                           "(allocating one here would capture a memset)")
 
 
 # ---- entry points (same names as the C ABI) --------------------------------
@@ -164,16 +214,19 @@ def pkv_cache_tensor_bytes(desc: pkv_cache_desc) -> int:
 
 
 def pkv_decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int,
-                               head_dim: int, num_workers: int = 0) -> int:
+                               head_dim: int, max_blocks_per_seq: int = 1,
+                               partition_size: int = 0, num_workers: int = 0) -> int:
     return int(lib().pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                                num_workers))
+                                                max_blocks_per_seq, partition_size, num_workers))
 
 
 def decode_workspace(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
-                     num_workers: int = 0, device=None) -> torch.Tensor:
+                     num_workers: int = 0, device=None, max_blocks_per_seq: int = 1,
+                     partition_size: int = 0) -> torch.Tensor:
     """A zero-filled decode workspace (its counters must start at zero; every
     decode call leaves them zero, so it can be reused call after call)."""
-    n = pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, num_workers)
+    n = pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                   max_blocks_per_seq, partition_size, num_workers)
     _need(n > 0, "invalid decode shape")
     return torch.zeros(n, dtype=torch.uint8, device=device)
 
@@ -186,44 +239,54 @@ def pkv_kv_append(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
     slot_mapping: int64 [T]."""
     T = k.shape[0]
     _need(k.shape == v.shape and k.dim() == 3, "k and v must be [T][H_kv][d]")
+    _check_rows("k", k, desc, heads=desc.num_kv_heads)
     _need(slot_mapping.dtype == torch.int64 and slot_mapping.numel() == T,
           "slot_mapping must be int64 [T]")
-    for t in (k, v, slot_mapping, k_cache, v_cache):
-        _need(t.is_contiguous() and t.is_cuda, "all tensors must be contiguous device tensors")
     _need(k.dtype == v.dtype and k_cache.dtype == v_cache.dtype, "k/v or cache dtypes differ")
     _need(k.dtype == k_cache.dtype
           or (_dtype_of(k_cache, "fp8") == PKV_FP8_E4M3 and _dtype_of(k) != PKV_FP8_E4M3),
           "k/v must be in the cache dtype, or 16/32-bit floats into an fp8 cache")
+    _check_desc_caches(desc, k_cache, v_cache)
+    _check_device(k, v, slot_mapping, k_cache, v_cache)
     rc = lib().pkv_kv_append(_ptr(k), _ptr(v), _dtype_of(k), _ptr(slot_mapping), T,
                              _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc), _stream(stream))
     _check("pkv_kv_append", rc)
+
+
+def _check_decode_args(q, k_cache, v_cache, desc, block_tables, context_lens, out):
+    S, Hq, d = q.shape
+    _check_rows("q", q, desc)
+    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+          and block_tables.shape[0] == S, "block_tables must be int32 [S][max_blocks]")
+    _need(context_lens.dtype == torch.int32 and context_lens.numel() == S,
+          "context_lens must be int32 [S]")
+    _check_desc_caches(desc, k_cache, v_cache)
+    _check_device(q, k_cache, v_cache, block_tables, context_lens, out)
 
 
 def pkv_paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                                desc: pkv_cache_desc, block_tables: torch.Tensor,
                                context_lens: torch.Tensor, scale: float, out: torch.Tensor,
                                num_workers: int = 0,
-                               workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+                               workspace: Optional[torch.Tensor] = None, stream=None,
+                               partition_size: int = 0) -> None:
     """q, out: [S][H_q][d]; block_tables: int32 [S][max_blocks]; context_lens: int32 [S].
+    partition_size: 0 (balanced split) or tokens per fixed partition.
     A zero-filled workspace (decode_workspace) is allocated from torch when
-    none is given."""
+    none is given (not allowed while a graph is being captured)."""
+    _check_decode_args(q, k_cache, v_cache, desc, block_tables, context_lens, out)
     S, Hq, d = q.shape
-    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
-    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
-          and block_tables.shape[0] == S, "block_tables must be int32 [S][max_blocks]")
-    _need(context_lens.dtype == torch.int32 and context_lens.numel() == S,
-          "context_lens must be int32 [S]")
-    for t in (q, k_cache, v_cache, block_tables, context_lens, out):
-        _need(t.is_contiguous() and t.is_cuda, "all tensors must be contiguous device tensors")
     mb = block_tables.shape[1]
     if workspace is None:
-        workspace = decode_workspace(S, Hq, desc.num_kv_heads, d, num_workers, q.device)
+        _no_capture("pkv_paged_attention_decode")
+        workspace = decode_workspace(S, Hq, desc.num_kv_heads, d, num_workers, q.device, mb,
+                                     partition_size)
     _need(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a device tensor")
-    ws_bytes = workspace.numel() * workspace.element_size()
     rc = lib().pkv_paged_attention_decode(
         _ptr(q), _dtype_of(q), S, Hq, _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
-        _ptr(block_tables), mb, _ptr(context_lens), float(scale), num_workers,
-        _ptr(workspace), ws_bytes, _ptr(out), _stream(stream))
+        _ptr(block_tables), mb, _ptr(context_lens), float(scale), partition_size, num_workers,
+        _ptr(workspace), _nbytes(workspace), _ptr(out), _stream(stream))
     _check("pkv_paged_attention_decode", rc)
 
 
@@ -251,28 +314,22 @@ def pkv_paged_attention_decode_shared_prefix(
     [G + 1] and group_prefix_blocks int32 [G] (device); group j is sequences
     [group_starts[j], group_starts[j + 1]) sharing their first
     group_prefix_blocks[j] blocks."""
+    _check_decode_args(q, k_cache, v_cache, desc, block_tables, context_lens, out)
     S, Hq, d = q.shape
-    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
-    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
-          and block_tables.shape[0] == S, "block_tables must be int32 [S][max_blocks]")
-    _need(context_lens.dtype == torch.int32 and context_lens.numel() == S,
-          "context_lens must be int32 [S]")
     ng = group_prefix_blocks.numel()
     _need(group_starts.dtype == torch.int32 and group_prefix_blocks.dtype == torch.int32
           and group_starts.numel() == ng + 1, "group arrays must be int32 [G + 1] and [G]")
-    for t in (q, k_cache, v_cache, block_tables, context_lens, out, group_starts,
-              group_prefix_blocks):
-        _need(t.is_contiguous() and t.is_cuda, "all tensors must be contiguous device tensors")
+    _check_device(group_starts, group_prefix_blocks)
     mb = block_tables.shape[1]
     if workspace is None:
+        _no_capture("pkv_paged_attention_decode_shared_prefix")
         workspace = shared_prefix_workspace(S, Hq, desc.num_kv_heads, d, ng, num_workers,
                                             q.device)
     _need(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a device tensor")
-    ws_bytes = workspace.numel() * workspace.element_size()
     rc = lib().pkv_paged_attention_decode_shared_prefix(
         _ptr(q), _dtype_of(q), S, Hq, _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
         _ptr(block_tables), mb, _ptr(context_lens), ng, _ptr(group_starts),
-        _ptr(group_prefix_blocks), float(scale), num_workers, _ptr(workspace), ws_bytes,
+        _ptr(group_prefix_blocks), float(scale), num_workers, _ptr(workspace), _nbytes(workspace),
         _ptr(out), _stream(stream))
     _check("pkv_paged_attention_decode_shared_prefix", rc)
 
@@ -299,18 +356,19 @@ def pkv_paged_attention_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache:
     workspace: None, or prefill_workspace(d) to let few-row batches split their keys."""
     T, Hq, d = q.shape
     S = context_lens.numel()
+    _check_rows("q", q, desc)
     _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
     _need(query_start.dtype == torch.int32 and query_start.numel() == S + 1,
           "query_start must be int32 [S + 1]")
     _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
           and block_tables.shape[0] == S, "block_tables must be int32 [S][max_blocks]")
     _need(context_lens.dtype == torch.int32, "context_lens must be int32 [S]")
-    for t in (q, k_cache, v_cache, block_tables, context_lens, query_start, out):
-        _need(t.is_contiguous() and t.is_cuda, "all tensors must be contiguous device tensors")
+    _check_desc_caches(desc, k_cache, v_cache)
+    _check_device(q, k_cache, v_cache, block_tables, context_lens, query_start, out)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         _need(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a device tensor")
-        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+        ws_ptr, ws_bytes = _ptr(workspace), _nbytes(workspace)
     rc = lib().pkv_paged_attention_prefill(
         _ptr(q), _dtype_of(q), S, T, Hq, _ptr(query_start), _ptr(k_cache), _ptr(v_cache),
         ctypes.byref(desc), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
@@ -323,8 +381,8 @@ def pkv_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, desc: pkv_cach
     """pairs: int32 [n][2] (device) of (source block, destination block)."""
     _need(pairs.dtype == torch.int32 and pairs.dim() == 2 and pairs.shape[1] == 2,
           "pairs must be int32 [n][2]")
-    for t in (k_cache, v_cache, pairs):
-        _need(t.is_contiguous() and t.is_cuda, "all tensors must be contiguous device tensors")
+    _check_desc_caches(desc, k_cache, v_cache)
+    _check_device(k_cache, v_cache, pairs)
     rc = lib().pkv_copy_blocks(_ptr(k_cache), _ptr(v_cache), ctypes.byref(desc), _ptr(pairs),
                                pairs.shape[0], _stream(stream))
     _check("pkv_copy_blocks", rc)
@@ -335,8 +393,15 @@ def pkv_debug_gather(k_cache: torch.Tensor, v_cache: torch.Tensor, desc: pkv_cac
                      k_out: torch.Tensor, v_out: torch.Tensor, stream=None) -> None:
     """k_out, v_out: [S][H_kv][max_ctx][d] in the cache dtype."""
     S = context_lens.numel()
-    for t in (k_cache, v_cache, block_tables, context_lens, k_out, v_out):
-        _need(t.is_contiguous() and t.is_cuda, "all tensors must be contiguous device tensors")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+          and block_tables.shape[0] == S, "block_tables must be int32 [S][max_blocks]")
+    _need(context_lens.dtype == torch.int32, "context_lens must be int32 [S]")
+    _check_desc_caches(desc, k_cache, v_cache)
+    need = S * desc.num_kv_heads * max_ctx * desc.head_dim * _ELEM_BYTES[desc.dtype]
+    for name, t in (("k_out", k_out), ("v_out", v_out)):
+        _need(_nbytes(t) >= need, f"{name} holds {_nbytes(t)} bytes, [S][H_kv][max_ctx][d] "
+                                  f"needs {need}")
+    _check_device(k_cache, v_cache, block_tables, context_lens, k_out, v_out)
     rc = lib().pkv_debug_gather(_ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
                                 _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
                                 S, max_ctx, _ptr(k_out), _ptr(v_out), _stream(stream))

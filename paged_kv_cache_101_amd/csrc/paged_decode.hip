@@ -21,6 +21,12 @@
 //     m, sum l, unnormalised accumulator) per wave in the workspace; the last
 //     wave to finish the segment, found with a device-scope counter, merges
 //     them with the log-sum-exp rule and writes the output.
+//   * Fixed partitions (PART, the caller's partition_size): the unit of the
+//     split is a partition of partition_size / 16 tiles instead of a tile,
+//     each wave takes whole partitions, every piece ends at a partition end,
+//     and each partition of a multi-partition segment leaves its partial in
+//     its own workspace slot; partition_merge_kernel, launched next on the
+//     stream, reduces them by the log-sum-exp rule.
 //
 // Per tile, both contractions run on the matrix cores, in the operand layouts
 // of the 16x16 MFMA shapes (lane l: column/row l % 16, k-group l / 16):
@@ -68,10 +74,14 @@ struct DecodeParams {
     int num_blocks;
     int max_blocks_per_seq;
     int num_workers;      // waves sharing the tile stream
+    // fixed partitions (PART): partition_size / 16 tiles per partition, and
+    // partition slots per (sequence, KV head) segment in the workspace
+    int part_tiles;
+    int part_stride;
     float qk_scale_log2;  // scale * k_scale * log2(e)
     float v_scale;
     int* counters;        // [S][H_kv], zero on entry and on exit
-    float* slots;         // [2 * num_workers][GM * (D + 2)]
+    float* slots;         // balanced: [2 * num_workers][SLOT]; PART: [S][H_kv][part_stride][SLOT]
     void* out;
     // suffix pass only (PFX): the prefix-group description and the float32
     // results of grouped sequences
@@ -110,24 +120,18 @@ __device__ __forceinline__ int worker_of(int64_t f, int64_t total, int nw) {
     return (int)(((f + 1) * nw - 1) / total);
 }
 
-// Merge the partials of one split segment, left by workers w0..w1 (worker w0
-// in its slot k0, the others in slot 0), into the output rows orow..orow+G-1:
+// Merge the nparts partials of one split segment (partial j at slot_of(j))
+// into the output rows orow..orow+G-1:
 //   M = max_j m_j,  out = sum_j 2^(m_j - M) acc_j / sum_j 2^(m_j - M) l_j.
 // With at most 64 partials (the usual case), lane j reads partial j's maxima
 // and sums once, and the accumulators of several partials are in flight at a
 // time; with more, the maxima and sums are read in passes of 64 partials and
 // one partial's accumulators are in flight at a time.
-template <int QT, int D, int GM>
-__device__ __forceinline__ void merge_segment(const DecodeParams& p, int w0, int w1,
-                                                        int k0, int G, size_t orow, int lane,
-                                                        bool to_result) {
-    constexpr int SLOT = decode_slot_floats(GM, D);
+template <int QT, int D, int GM, typename SlotOf>
+__device__ __forceinline__ void merge_segment(const DecodeParams& p, int nparts, SlotOf slot_of,
+                                              int G, size_t orow, int lane, bool to_result) {
     static_assert(D % kWave == 0, "head size must be a multiple of the wave width");
     constexpr int PER_LANE = GM * D / kWave;  // accumulator elements per lane
-    const int nparts = w1 - w0 + 1;
-    auto slot_of = [&](int j) {
-        return p.slots + (size_t)(2 * (w0 + j) + (j == 0 ? k0 : 0)) * SLOT;
-    };
     float mx[GM];
     float lsum[GM], o[PER_LANE];
 #pragma unroll
@@ -224,7 +228,7 @@ __device__ __forceinline__ void merge_segment(const DecodeParams& p, int w0, int
     }
 }
 
-template <int KT, int QT, int D, int GM, bool PFX>
+template <int KT, int QT, int D, int GM, bool PFX, bool PART>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void paged_decode_kernel(DecodeParams p) {
     using TM = TileMath<KT, QT, D>;
@@ -233,6 +237,7 @@ void paged_decode_kernel(DecodeParams p) {
     constexpr int QB = Elem<QT>::bytes;
     constexpr uint32_t kTileBytes = (uint32_t)kBlock * D * KB;
     constexpr int SLOT = decode_slot_floats(GM, D);
+    static_assert(!(PFX && PART), "the suffix pass uses the balanced split");
 
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kWavesPerGroup) + wave_id());
@@ -241,6 +246,7 @@ void paged_decode_kernel(DecodeParams p) {
     const int S = p.num_seqs, H = p.num_kv_heads, G = p.group, Hq = p.num_q_heads;
     const int mb = p.max_blocks_per_seq;
     const int max_ctx = mb * kBlock;
+    const int pt = PART ? p.part_tiles : 1;  // tiles per partition (PART)
     const float nan = __builtin_nanf("");
     // prefix groups (suffix pass only; an unusable description counts as none)
     const int ng = PFX ? usable_groups(p.group_starts, p.group_prefix, p.num_groups, S, mb, lane) : 0;
@@ -251,6 +257,12 @@ void paged_decode_kernel(DecodeParams p) {
     auto pre_lane = [&](int s) -> int {
         if constexpr (PFX) return prefix_blocks_of<false>(p.group_starts, p.group_prefix, ng, s);
         else return 0;
+    };
+    // Units of work a segment of nb tiles holds: its tiles (balanced split),
+    // or its partitions of pt tiles (PART).
+    auto units_of = [&](int nb) -> int {
+        if constexpr (PART) return (nb + pt - 1) / pt;
+        else return nb;
     };
 
     // Sequences with no tiles: a zero row (n <= 0) or a NaN row (n longer than
@@ -270,11 +282,12 @@ void paged_decode_kernel(DecodeParams p) {
             store_f32_as<QT>(p.out, (size_t)s * Hq * D + idx, fill);
     }
 
-    // Total tiles T and this wave's slice.
+    // Total units T and this wave's slice [a, b) of them. Units are numbered
+    // like the tiles: sequence-major, then KV head, then position.
     int64_t total = 0;
     for (int base = 0; base < S; base += kWave) {
         const int s = base + lane;
-        total += wave_sum_int(s < S ? tiles_of(p.context_lens[s], pre_lane(s), max_ctx) : 0);
+        total += wave_sum_int(s < S ? units_of(tiles_of(p.context_lens[s], pre_lane(s), max_ctx)) : 0);
     }
     total *= H;
     if (total == 0) return;
@@ -283,14 +296,14 @@ void paged_decode_kernel(DecodeParams p) {
     const int64_t a = (int64_t)w * total / nw;
     const int64_t b = (int64_t)(w + 1) * total / nw;
 
-    // The sequence holding tile a, and the number of tiles before it.
+    // The sequence holding unit a, and the number of units before it.
     int cs = 0;
     int64_t seq_base = 0;
     {
         int64_t before = 0;
         for (int base = 0; base < S; base += kWave) {
             const int s = base + lane;
-            const int t = s < S ? tiles_of(p.context_lens[s], pre_lane(s), max_ctx) * H : 0;
+            const int t = s < S ? units_of(tiles_of(p.context_lens[s], pre_lane(s), max_ctx)) * H : 0;
             const int incl = wave_inclusive_scan(t, lane);
             const int64_t lo = before + incl - t;
             const unsigned long long hit = __ballot(t > 0 && lo <= a && a < before + incl);
@@ -304,19 +317,29 @@ void paged_decode_kernel(DecodeParams p) {
         }
     }
 
-    // A position in the tile stream: segment (s, g) of nb tiles whose first
-    // tile has index seg; block bi counted from the sequence's first streamed
-    // block pre (0 unless it is in a prefix group), n the length counted from
-    // there; the wave's slice of the segment ends at block hi. All fields are
-    // wave-uniform.
+    // A position in the tile stream: segment (s, g) of nb tiles (np units)
+    // whose first unit has index seg; block bi counted from the sequence's
+    // first streamed block pre (0 unless it is in a prefix group), n the
+    // length counted from there; the current piece of the segment ends at
+    // block hi (the slice's end, the segment's end, or with PART the
+    // partition's end). All fields are wave-uniform.
     struct Cursor {
-        int s, g, n, pre, nb, bi, hi;
+        int s, g, n, pre, nb, np, bi, hi;
         int64_t seg;
     };
-    // Move c to the first block of the next segment (order s, then g) inside
-    // the slice; false when the slice has no more tiles.
-    auto next_segment = [&](Cursor& c) -> bool {
-        const int64_t seg = c.seg + c.nb;
+    // Move c, which has just reached the end of its piece (bi == hi), to the
+    // first block of the next piece inside the slice: the next partition of
+    // the segment (PART), else the first block of the next segment (order s,
+    // then g). false when the slice has no more tiles.
+    auto next_piece = [&](Cursor& c) -> bool {
+        if constexpr (PART) {
+            if (c.bi < c.nb) {
+                if (c.seg + c.bi / pt >= b) return false;
+                c.hi = min(c.nb, c.bi + pt);
+                return true;
+            }
+        }
+        const int64_t seg = c.seg + c.np;
         if (seg >= b) return false;
         if (c.g + 1 < H) {
             ++c.g;
@@ -334,10 +357,11 @@ void paged_decode_kernel(DecodeParams p) {
             c.n = n - pre * kBlock;
             c.pre = pre;
             c.nb = nb;
+            c.np = units_of(nb);
         }
         c.seg = seg;
         c.bi = 0;
-        c.hi = (int)min((int64_t)c.nb, b - seg);
+        c.hi = PART ? min(c.nb, pt) : (int)min((int64_t)c.nb, b - seg);
         return true;
     };
 
@@ -347,13 +371,19 @@ void paged_decode_kernel(DecodeParams p) {
     cc.n = uniform_read(p.context_lens, cs);
     cc.nb = tiles_of(cc.n, cc.pre, max_ctx);
     cc.n -= cc.pre * kBlock;
-    if (cc.nb == 0) return;  // cannot happen: tile a lies in a non-empty sequence
-    cc.g = (int)((a - seq_base) / cc.nb);
-    cc.bi = (int)((a - seq_base) % cc.nb);
-    cc.seg = seq_base + (int64_t)cc.g * cc.nb;
-    cc.hi = (int)min((int64_t)cc.nb, cc.bi + (b - a));
+    if (cc.nb == 0) return;  // cannot happen: unit a lies in a non-empty sequence
+    cc.np = units_of(cc.nb);
+    cc.g = (int)((a - seq_base) / cc.np);
+    cc.seg = seq_base + (int64_t)cc.g * cc.np;
+    if constexpr (PART) {
+        cc.bi = (int)(a - cc.seg) * pt;
+        cc.hi = min(cc.nb, cc.bi + pt);
+    } else {
+        cc.bi = (int)(a - cc.seg);
+        cc.hi = (int)min((int64_t)cc.nb, cc.bi + (b - a));
+    }
     int clo = cc.bi;           // first block of the computed piece
-    bool first_piece = true;   // the piece holding tile a (partial slot 0)
+    bool first_piece = true;   // the piece holding unit a (partial slot 0)
     bool piece_bad = false;
 
     Cursor ic = cc;  // the next tile to load (kPrefetch tiles ahead of cc)
@@ -367,7 +397,7 @@ void paged_decode_kernel(DecodeParams p) {
     int ic_id = read_id(ic);
     auto ic_advance = [&]() {
         if (!ic_valid) return;
-        if (++ic.bi == ic.hi) ic_valid = next_segment(ic);
+        if (++ic.bi == ic.hi) ic_valid = next_piece(ic);
         if (ic_valid) ic_id = read_id(ic);
     };
 
@@ -384,7 +414,7 @@ void paged_decode_kernel(DecodeParams p) {
     for (int j = 0; j < 4; ++j) head_lane[j] = (4 * g4 + j) << 2;
 
     // q: the query of the piece being computed; q_nx: that of the next
-    // piece, read as soon as the tile stream reaches it.
+    // segment, read as soon as the tile stream reaches it.
     typename TM::Q q, q_nx;
     auto load_q = [&](typename TM::Q& dst, int s, int g) {
         TM::load_q(dst, p.q + ((size_t)s * Hq + (size_t)g * G + t) * D * QB, t < G, g4);
@@ -445,10 +475,11 @@ void paged_decode_kernel(DecodeParams p) {
     const float qk_scale = p.qk_scale_log2;
     bool active = true;  // cc holds a tile still to compute
 
-    // Split segments whose partials this wave was the last to deliver. Only
-    // the first and the last piece of a slice can be partial, so there are at
-    // most two; they are merged after the stream, which keeps the merge's
-    // loads and registers out of the streaming loop.
+    // Balanced split: split segments whose partials this wave was the last to
+    // deliver. Only the first and the last piece of a slice can be partial,
+    // so there are at most two; they are merged after the stream, which keeps
+    // the merge's loads and registers out of the streaming loop. (Fixed
+    // partitions are merged by a second launch.)
     struct Pending {
         int s, g, pre, nb;
         int64_t seg;
@@ -466,11 +497,11 @@ void paged_decode_kernel(DecodeParams p) {
             piece_bad |= slot_bad[slot];
             bool next_bad;
             const TileRef nxt = ic_tile(next_bad);
-            // The tile about to be loaded opens the next piece (with one tile
-            // in flight, the current tile then ends this piece): its query is
-            // read first, so the in-order wait for that tile covers it too and
-            // the piece change waits for nothing else.
-            static_assert(kPrefetch == 1, "the next piece's query is read one tile ahead");
+            // The tile about to be loaded opens the next segment (with one
+            // tile in flight, the current tile then ends this piece): its
+            // query is read first, so the in-order wait for that tile covers
+            // it too and the piece change waits for nothing else.
+            static_assert(kPrefetch == 1, "the next segment's query is read one tile ahead");
             if (ic_valid && ic.seg != cc.seg) load_q(q_nx, ic.s, ic.g);
 
             // ---- scores; the next K goes out as soon as this K is consumed ----
@@ -517,12 +548,9 @@ void paged_decode_kernel(DecodeParams p) {
             ic_advance();
 
             if (!active) continue;
-            if (cc.bi + 1 < cc.hi) {
-                ++cc.bi;
-                continue;
-            }
+            if (++cc.bi < cc.hi) continue;
 
-            // ---- the piece is done: write it out, or leave a partial ----
+            // ---- the piece [clo, hi) is done: write it out, or leave a partial ----
             float lt = l_run + lane_fetch(x16, l_run);
             lt += lane_fetch(x32, lt);  // weight sum of head t over the piece
             const size_t orow = (size_t)cc.s * Hq + (size_t)cc.g * G;  // first output row
@@ -552,6 +580,24 @@ void paged_decode_kernel(DecodeParams p) {
                                              piece_bad ? nan : o[j][r] * sc_r);
                     }
                 }
+            } else if constexpr (PART) {
+                // partition j of a split segment: unnormalised accumulator,
+                // max, sum to its own slot, plain stores; the merge launch
+                // that follows (the kernel boundary orders them) reduces them
+                float* slotp = p.slots +
+                               ((size_t)(cc.s * H + cc.g) * p.part_stride + clo / pt) * SLOT;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int hh = 4 * g4 + r;
+                    if (hh < GM) {
+#pragma unroll
+                        for (int j = 0; j < NV; ++j) slotp[hh * D + 16 * j + t] = o[j][r];
+                    }
+                }
+                if (lane < GM) {
+                    slotp[GM * D + lane] = piece_bad ? nan : m_run;
+                    slotp[GM * D + GM + lane] = piece_bad ? nan : lt;
+                }
             } else {
                 // partial of a split segment: unnormalised accumulator, max, sum
                 float* slotp = p.slots + (size_t)(2 * w + (first_piece ? 0 : 1)) * SLOT;
@@ -567,12 +613,18 @@ void paged_decode_kernel(DecodeParams p) {
                     coherent_store(slotp + GM * D + lane, piece_bad ? nan : m_run);
                     coherent_store(slotp + GM * D + GM + lane, piece_bad ? nan : lt);
                 }
-                __builtin_amdgcn_s_waitcnt(0);  // the partial has landed before it is announced
+                // The partial has landed before it is announced: wait for the
+                // write-through stores to complete, and keep the compiler from
+                // moving any memory access across the wait and the counter.
+                __builtin_amdgcn_s_waitcnt(0);
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
                 int* counter = p.counters + (size_t)cc.s * H + cc.g;
                 int old = 0;
                 if (lane == 0)
                     old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 old = __builtin_amdgcn_readfirstlane(old);
+                // No load of the partials may be hoisted above the counter read.
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
                 const int w0 = worker_of(cc.seg, total, nw);
                 const int w1 = worker_of(cc.seg + cc.nb - 1, total, nw);
                 if (old == w1 - w0) {  // every partial of the segment is in
@@ -583,14 +635,15 @@ void paged_decode_kernel(DecodeParams p) {
             }
 
             // ---- next piece (its first tiles are already in flight) ----
-            if (!next_segment(cc)) {
+            const bool same_segment = PART && cc.bi < cc.nb;
+            if (!next_piece(cc)) {
                 active = false;
                 continue;
             }
-            clo = 0;
+            clo = cc.bi;
             first_piece = false;
             piece_bad = false;
-            q = q_nx;  // read with the piece's first tile, before it
+            if (!same_segment) q = q_nx;  // read with the segment's first tile, before it
             m_run = -INFINITY;
             l_run = 0.f;
 #pragma unroll
@@ -605,19 +658,104 @@ void paged_decode_kernel(DecodeParams p) {
         const int w0 = worker_of(pd.seg, total, nw);
         const int w1 = worker_of(pd.seg + pd.nb - 1, total, nw);
         const int k0 = (int64_t)w0 * total / nw < pd.seg ? 1 : 0;
-        merge_segment<QT, D, GM>(p, w0, w1, k0, G, (size_t)pd.s * Hq + (size_t)pd.g * G, lane,
-                                 PFX && pd.pre > 0);
+        // worker w0's partial is in its slot k0, the others' in their slot 0
+        merge_segment<QT, D, GM>(
+            p, w1 - w0 + 1,
+            [&](int j) { return p.slots + (size_t)(2 * (w0 + j) + (j == 0 ? k0 : 0)) * SLOT; }, G,
+            (size_t)pd.s * Hq + (size_t)pd.g * G, lane, PFX && pd.pre > 0);
         if (lane == 0)
             __hip_atomic_store(p.counters + (size_t)pd.s * H + pd.g, 0, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
+// ---- fixed partitions: the cross-partition reduce --------------------------------
+//
+// After a fixed-partition decode launch, every (sequence, KV head) segment
+// with more than one partition has left partition j's unnormalised
+// accumulator acc_j, maximum m_j and sum l_j (log2 units) in slot j of its
+// workspace row. One wave per (sequence, query head) row reduces them by the
+// log-sum-exp rule,
+//   M = max_j m_j,  out = v_scale * sum_j 2^(m_j - M) acc_j / sum_j 2^(m_j - M) l_j,
+// reading them with plain loads (the kernel boundary orders them after the
+// decode launch). Rows of segments with one partition were written by the
+// decode launch itself and are skipped, as are rows of sequences without
+// tiles; a NaN partial (a block id outside the pool) makes the row NaN.
+struct PartitionMergeParams {
+    const int32_t* context_lens;
+    const float* slots;  // [S][H_kv][part_stride][SLOT]
+    void* out;
+    int num_seqs, num_q_heads, num_kv_heads, group, max_blocks_per_seq;
+    int part_tiles, part_stride;
+    float v_scale;
+};
+
+constexpr int kMergeWaves = 4;  // rows per workgroup of the reduce
+
+template <int QT, int D, int GM>
+__global__ __launch_bounds__(kMergeWaves * kWave) void partition_merge_kernel(PartitionMergeParams p) {
+    constexpr int SLOT = decode_slot_floats(GM, D);
+    constexpr int EPL = D / kWave;  // output elements per lane
+    static_assert(D % kWave == 0, "head size must be a multiple of the wave width");
+    const int lane = lane_id();
+    const int row = (int)blockIdx.x * kMergeWaves + wave_id();
+    if (row >= p.num_seqs * p.num_q_heads) return;
+    const int s = row / p.num_q_heads, h = row % p.num_q_heads;
+    const int g = h / p.group, hh = h % p.group;
+    const int nb = tiles_of(p.context_lens[s], 0, p.max_blocks_per_seq * kBlock);
+    const int np = (nb + p.part_tiles - 1) / p.part_tiles;
+    if (np <= 1) return;
+    const float* base = p.slots + (size_t)(s * p.num_kv_heads + g) * p.part_stride * SLOT;
+    float M = -INFINITY;
+    for (int j0 = 0; j0 < np; j0 += kWave) {
+        const int j = j0 + lane;
+        M = fmaxf(M, wave_max(j < np ? base[(size_t)j * SLOT + GM * D + hh] : -INFINITY));
+    }
+    float L = 0.f, acc[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+#pragma unroll 8
+    for (int j = 0; j < np; ++j) {
+        const float* sj = base + (size_t)j * SLOT;
+        const float wj = __builtin_amdgcn_exp2f(sj[GM * D + hh] - M);
+        L = fmaf(wj, sj[GM * D + GM + hh], L);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] = fmaf(wj, sj[hh * D + lane * EPL + e], acc[e]);
+    }
+    const float sc = p.v_scale / L;
+    const size_t orow = (size_t)s * p.num_q_heads + h;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) store_f32_as<QT>(p.out, orow * D + lane * EPL + e, acc[e] * sc);
+}
+
 // ---- dispatch ------------------------------------------------------------------
 
-template <int KT, int QT, int D, int GM, bool PFX>
+// Compute units of the current device, read once per device.
+static int device_cus() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cus_cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (dev < 0 || dev >= kMaxDevices) {
+        int cus = 0;
+        return hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess ? cus : 0;
+    }
+    int cus = cus_cache[dev].load(std::memory_order_relaxed);
+    if (cus == 0) {
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        cus_cache[dev].store(cus, std::memory_order_relaxed);
+    }
+    return cus;
+}
+
+template <int KT, int QT, int D, int GM, bool PFX, bool PART>
 static hipError_t launch_typed(const DecodeArgs& a) {
-    auto kernel = paged_decode_kernel<KT, QT, D, GM, PFX>;
+    auto kernel = paged_decode_kernel<KT, QT, D, GM, PFX, PART>;
+    const int pt = PART ? a.partition_size / kBlock : 1;
+    // units of work at most: tiles, or partitions of pt tiles (PART)
+    const int64_t unit_bound = (int64_t)a.num_seqs * a.num_kv_heads *
+                               ((a.max_blocks_per_seq + pt - 1) / pt);
     int nw = a.num_workers;
     if (nw == 0) {
         // worker waves per CU so that about 12 KiB of K tiles (and as much V)
@@ -625,6 +763,7 @@ static hipError_t launch_typed(const DecodeArgs& a) {
         // tiles, 6 for fp8 d 128, clamped to 2..8
         constexpr int kTileBytes = kBlock * D * Elem<KT>::bytes;
         constexpr int kTarget = 12288 / kTileBytes < 2 ? 2 : 12288 / kTileBytes > 8 ? 8 : 12288 / kTileBytes;
+        // occupancy of this kernel (the same on every device of this kind)
         static std::atomic<int> per_cu_cache{0};
         int per_cu = per_cu_cache.load(std::memory_order_relaxed);
         if (per_cu == 0) {
@@ -634,10 +773,8 @@ static hipError_t launch_typed(const DecodeArgs& a) {
                 per_cu = 1;
             per_cu_cache.store(per_cu, std::memory_order_relaxed);
         }
-        int dev = 0, cus = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            return hipErrorInvalidDevice;
+        const int cus = device_cus();
+        if (cus <= 0) return hipErrorInvalidDevice;
         // Measured on the 40 x 8192 fp16 GQA shape, 3 per CU is best (a sweep
         // over 2..16 per CU): more concurrent streams lower the bandwidth the
         // memory system delivers and widen the spread between waves. fp8
@@ -645,10 +782,17 @@ static hipError_t launch_typed(const DecodeArgs& a) {
         // faster at 6 per CU than at 3.
         nw = (per_cu < kTarget ? per_cu : kTarget) * cus * kWavesPerGroup;
         if (nw > kMaxWorkers) nw = kMaxWorkers;
+        if (PART) {
+            // whole partitions per wave: the nearest whole number k of them
+            // for the full batch, and as many waves as that needs
+            int64_t k = (unit_bound + nw / 2) / nw;
+            if (k < 1) k = 1;
+            const int64_t want = (unit_bound + k - 1) / k;
+            nw = (int)(want < kMaxWorkers ? want : kMaxWorkers);
+        }
     }
-    // never more workers than tiles could exist
-    const int64_t tile_bound = (int64_t)a.num_seqs * a.num_kv_heads * a.max_blocks_per_seq;
-    if (nw > tile_bound) nw = (int)tile_bound;
+    // never more workers than units could exist
+    if (nw > unit_bound) nw = (int)unit_bound;
     if (nw < 1) nw = 1;
 
     DecodeParams p;
@@ -664,6 +808,8 @@ static hipError_t launch_typed(const DecodeArgs& a) {
     p.num_blocks = a.num_blocks;
     p.max_blocks_per_seq = a.max_blocks_per_seq;
     p.num_workers = nw;
+    p.part_tiles = pt;
+    p.part_stride = PART ? (a.max_blocks_per_seq + pt - 1) / pt : 0;
     p.qk_scale_log2 = a.scale * (KT == PKV_FP8_E4M3 ? a.k_scale : 1.f) * kLog2e;
     p.v_scale = KT == PKV_FP8_E4M3 ? a.v_scale : 1.f;
     p.counters = a.counters;
@@ -676,26 +822,50 @@ static hipError_t launch_typed(const DecodeArgs& a) {
     p.res_lse = a.res_lse;
     const int grid = (nw + kWavesPerGroup - 1) / kWavesPerGroup;
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, a.stream, p);
+    if constexpr (PART) {
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        PartitionMergeParams mp;
+        mp.context_lens = a.context_lens;
+        mp.slots = a.slots;
+        mp.out = a.out;
+        mp.num_seqs = a.num_seqs;
+        mp.num_q_heads = a.num_q_heads;
+        mp.num_kv_heads = a.num_kv_heads;
+        mp.group = a.group;
+        mp.max_blocks_per_seq = a.max_blocks_per_seq;
+        mp.part_tiles = p.part_tiles;
+        mp.part_stride = p.part_stride;
+        mp.v_scale = p.v_scale;
+        const int64_t rows = (int64_t)a.num_seqs * a.num_q_heads;
+        hipLaunchKernelGGL((partition_merge_kernel<QT, D, GM>),
+                           dim3((unsigned)((rows + kMergeWaves - 1) / kMergeWaves)),
+                           dim3(kMergeWaves * kWave), 0, a.stream, mp);
+    }
     return hipGetLastError();
 }
 
-template <int KT, int QT, int D, bool PFX>
+template <int KT, int QT, int D, bool PFX, bool PART>
 static hipError_t launch_group(const DecodeArgs& a) {
     switch (padded_group(a.group)) {
-    case 1: return launch_typed<KT, QT, D, 1, PFX>(a);
-    case 2: return launch_typed<KT, QT, D, 2, PFX>(a);
-    case 4: return launch_typed<KT, QT, D, 4, PFX>(a);
-    case 6: return launch_typed<KT, QT, D, 6, PFX>(a);
-    default: return launch_typed<KT, QT, D, 8, PFX>(a);
+    case 1: return launch_typed<KT, QT, D, 1, PFX, PART>(a);
+    case 2: return launch_typed<KT, QT, D, 2, PFX, PART>(a);
+    case 4: return launch_typed<KT, QT, D, 4, PFX, PART>(a);
+    case 6: return launch_typed<KT, QT, D, 6, PFX, PART>(a);
+    default: return launch_typed<KT, QT, D, 8, PFX, PART>(a);
     }
+}
+
+template <int KT, int QT, int D>
+static hipError_t launch_mode(const DecodeArgs& a) {
+    if (a.res_o != nullptr) return launch_group<KT, QT, D, true, false>(a);  // suffix pass
+    if (a.partition_size > 0) return launch_group<KT, QT, D, false, true>(a);
+    return launch_group<KT, QT, D, false, false>(a);
 }
 
 template <int KT, int QT>
 static hipError_t launch_dim(const DecodeArgs& a) {
-    if (a.res_o != nullptr)
-        return a.head_dim == 64 ? launch_group<KT, QT, 64, true>(a)
-                                : launch_group<KT, QT, 128, true>(a);
-    return a.head_dim == 64 ? launch_group<KT, QT, 64, false>(a) : launch_group<KT, QT, 128, false>(a);
+    return a.head_dim == 64 ? launch_mode<KT, QT, 64>(a) : launch_mode<KT, QT, 128>(a);
 }
 
 hipError_t launch_paged_decode(const DecodeArgs& a) {

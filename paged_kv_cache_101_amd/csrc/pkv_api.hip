@@ -88,14 +88,31 @@ PKV_EXPORT int pkv_kv_append(const void* k, const void* v, int32_t kv_dtype,
     return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+namespace {
+
+// The decode shape checks of the workspace-size functions.
+bool decode_shape_ok(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, int32_t num_workers) {
+    return num_seqs > 0 && num_q_heads > 0 && num_kv_heads > 0 && head_dim > 0 &&
+           num_q_heads % num_kv_heads == 0 && num_q_heads / num_kv_heads <= 8 &&
+           num_workers >= 0 && num_workers <= pkv::kMaxWorkers;
+}
+
+bool partition_ok(int32_t partition_size) {
+    return partition_size >= 0 && partition_size % PKV_BLOCK_SIZE == 0;
+}
+
+}  // namespace
+
 PKV_EXPORT size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                              int32_t num_kv_heads, int32_t head_dim,
+                                             int32_t max_blocks_per_seq, int32_t partition_size,
                                              int32_t num_workers) {
-    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-        num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > 8 || num_workers < 0 ||
-        num_workers > pkv::kMaxWorkers)
+    if (!decode_shape_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, num_workers) ||
+        max_blocks_per_seq <= 0 || !partition_ok(partition_size))
         return 0;
     return pkv::decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                       max_blocks_per_seq, partition_size,
                                        num_workers == 0 ? pkv::kMaxWorkers : num_workers);
 }
 
@@ -167,16 +184,19 @@ PKV_EXPORT int pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_
                                           const int32_t* block_tables,
                                           int32_t max_blocks_per_seq,
                                           const int32_t* context_lens, float scale,
-                                          int32_t num_workers, void* workspace,
-                                          size_t workspace_bytes, void* out,
+                                          int32_t partition_size, int32_t num_workers,
+                                          void* workspace, size_t workspace_bytes, void* out,
                                           hipStream_t stream) {
     pkv::DecodeArgs a;
     const int rc = decode_args(a, q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, cache,
                                block_tables, max_blocks_per_seq, context_lens, scale, num_workers,
                                true, workspace, out, stream);
     if (rc != PKV_OK) return rc;
+    if (!partition_ok(partition_size)) return PKV_ERR_INVALID_ARG;
+    a.partition_size = partition_size;
     if (workspace_bytes < pkv_decode_workspace_bytes(num_seqs, num_q_heads, cache->num_kv_heads,
-                                                     cache->head_dim, num_workers))
+                                                     cache->head_dim, max_blocks_per_seq,
+                                                     partition_size, num_workers))
         return PKV_ERR_WORKSPACE;
     a.counters = reinterpret_cast<int*>(
         static_cast<char*>(workspace) +
@@ -188,7 +208,7 @@ PKV_EXPORT int pkv_paged_attention_decode(const void* q, int32_t q_dtype, int32_
 PKV_EXPORT size_t pkv_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                                     int32_t num_kv_heads, int32_t head_dim,
                                                     int32_t num_groups, int32_t num_workers) {
-    if (pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, num_workers) == 0 ||
+    if (!decode_shape_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, num_workers) ||
         num_groups < 0 || num_groups > num_seqs)
         return 0;
     return pkv::shared_prefix_layout(num_seqs, num_q_heads, num_kv_heads, head_dim,
@@ -328,3 +348,4 @@ PKV_EXPORT int pkv_debug_gather(const void* k_cache, const void* v_cache,
                                         max_ctx, k_out, v_out, stream);
     return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
+

@@ -27,8 +27,9 @@ inline size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 // call sized no larger, so one workspace, zeroed once and sized for the
 // largest shape, serves every smaller call without clearing it again.
 //
-// Decode: 2 * workers partial slots at the front, counters [S][H_kv] at the
-// end, each part a multiple of 256 bytes.
+// Decode: 2 * workers partial slots (balanced split) or one slot per
+// (sequence, KV head, partition) (fixed partitions) at the front, counters
+// [S][H_kv] at the end, each part a multiple of 256 bytes.
 inline size_t decode_slot_bytes(int num_q_heads, int num_kv_heads, int head_dim, int workers) {
     const int gm = padded_group(num_q_heads / num_kv_heads);
     return round256((size_t)2 * workers * decode_slot_floats(gm, head_dim) * sizeof(float));
@@ -36,10 +37,29 @@ inline size_t decode_slot_bytes(int num_q_heads, int num_kv_heads, int head_dim,
 inline size_t decode_counter_bytes(int num_seqs, int num_kv_heads) {
     return round256((size_t)num_seqs * num_kv_heads * sizeof(int32_t));
 }
+// Fixed partitions of partition_size tokens: one slot per (sequence, KV head,
+// partition), ceil(max_blocks_per_seq * 16 / partition_size) partitions.
+inline int decode_partitions(int max_blocks_per_seq, int partition_size) {
+    const int pt = partition_size / 16;
+    return (max_blocks_per_seq + pt - 1) / pt;
+}
+inline size_t decode_partition_slot_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
+                                          int head_dim, int max_blocks_per_seq,
+                                          int partition_size) {
+    const int gm = padded_group(num_q_heads / num_kv_heads);
+    return round256((size_t)num_seqs * num_kv_heads *
+                    decode_partitions(max_blocks_per_seq, partition_size) *
+                    decode_slot_floats(gm, head_dim) * sizeof(float));
+}
 inline size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
-                                     int head_dim, int workers) {
-    return decode_slot_bytes(num_q_heads, num_kv_heads, head_dim, workers) +
-           decode_counter_bytes(num_seqs, num_kv_heads);
+                                     int head_dim, int max_blocks_per_seq, int partition_size,
+                                     int workers) {
+    const size_t slots =
+        partition_size > 0
+            ? decode_partition_slot_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                          max_blocks_per_seq, partition_size)
+            : decode_slot_bytes(num_q_heads, num_kv_heads, head_dim, workers);
+    return slots + decode_counter_bytes(num_seqs, num_kv_heads);
 }
 // Start of the last `bytes` bytes of a workspace of ws_bytes (256-aligned).
 inline size_t tail_offset(size_t ws_bytes, size_t bytes) { return (ws_bytes & ~(size_t)255) - bytes; }
@@ -111,6 +131,7 @@ struct DecodeArgs {
     float k_scale;
     float v_scale;
     int num_workers;  // 0 = fill the device
+    int partition_size = 0;  // tokens per fixed partition (a multiple of 16); 0 = balanced split
     int* counters;    // [S][H_kv], zero on entry
     float* slots;     // partial slots
     void* out;

@@ -61,12 +61,14 @@ def gpu_append(b: W.DecodeBatch):
     B.pkv_kv_append(b.new_k, b.new_v, b.slot_mapping, kc, vc, desc(b))
 
 
-def gpu_decode(b: W.DecodeBatch, num_workers=0, out=None, workspace=None) -> torch.Tensor:
+def gpu_decode(b: W.DecodeBatch, num_workers=0, out=None, workspace=None,
+               partition_size=0) -> torch.Tensor:
     if out is None:
         out = torch.empty_like(b.q)
     kc, vc = device_caches(b)
     B.pkv_paged_attention_decode(b.q, kc, vc, desc(b), b.block_tables, b.context_lens, b.scale,
-                                 out, num_workers=num_workers, workspace=workspace)
+                                 out, num_workers=num_workers, workspace=workspace,
+                                 partition_size=partition_size)
     return out
 
 

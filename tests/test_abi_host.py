@@ -9,6 +9,7 @@ import re
 import subprocess
 
 import pytest
+import torch
 
 from paged_kv_cache_101_amd import binding as B
 
@@ -66,29 +67,54 @@ def r256(x):
 
 
 def test_workspace_bytes_formula():
-    # 2 slots per worker, then counters [S][H_kv] int32, each rounded up to 256 B
+    # balanced split: 2 slots per worker, then counters [S][H_kv] int32, each
+    # rounded up to 256 B (max_blocks_per_seq does not enter)
     ctr = r256(40 * 8 * 4)
-    assert B.pkv_decode_workspace_bytes(40, 32, 8, 128, 2048) == r256(2 * 2048 * _slot_floats(4, 128) * 4) + ctr
-    assert B.pkv_decode_workspace_bytes(40, 32, 8, 128, 0) == r256(2 * 4096 * _slot_floats(4, 128) * 4) + ctr
+    ws = B.pkv_decode_workspace_bytes
+    assert ws(40, 32, 8, 128, 512, 0, 2048) == r256(2 * 2048 * _slot_floats(4, 128) * 4) + ctr
+    assert ws(40, 32, 8, 128, 1, 0, 0) == r256(2 * 4096 * _slot_floats(4, 128) * 4) + ctr
     # G = 6 and G = 5 use 6-head slots, G = 3 uses 4, G = 7 uses 8
-    assert B.pkv_decode_workspace_bytes(64, 12, 2, 128, 10) == 512 + r256(20 * _slot_floats(6, 128) * 4)
-    assert B.pkv_decode_workspace_bytes(1, 5, 1, 64, 1) == 256 + r256(2 * _slot_floats(6, 64) * 4)
-    assert B.pkv_decode_workspace_bytes(1, 3, 1, 64, 1) == 256 + r256(2 * _slot_floats(4, 64) * 4)
-    assert B.pkv_decode_workspace_bytes(1, 7, 1, 64, 1) == 256 + r256(2 * _slot_floats(8, 64) * 4)
-    assert B.pkv_decode_workspace_bytes(4, 4, 3, 64, 1) == 0        # 4 % 3 != 0
-    assert B.pkv_decode_workspace_bytes(4, 18, 2, 64, 1) == 0       # G = 9
-    assert B.pkv_decode_workspace_bytes(4, 4, 1, 64, -1) == 0
-    assert B.pkv_decode_workspace_bytes(4, 4, 1, 64, B.PKV_MAX_WORKERS + 1) == 0
+    assert ws(64, 12, 2, 128, 256, 0, 10) == 512 + r256(20 * _slot_floats(6, 128) * 4)
+    assert ws(1, 5, 1, 64, 1, 0, 1) == 256 + r256(2 * _slot_floats(6, 64) * 4)
+    assert ws(1, 3, 1, 64, 1, 0, 1) == 256 + r256(2 * _slot_floats(4, 64) * 4)
+    assert ws(1, 7, 1, 64, 1, 0, 1) == 256 + r256(2 * _slot_floats(8, 64) * 4)
+    assert ws(4, 4, 3, 64, 1, 0, 1) == 0        # 4 % 3 != 0
+    assert ws(4, 18, 2, 64, 1, 0, 1) == 0       # G = 9
+    assert ws(4, 4, 1, 64, 1, 0, -1) == 0
+    assert ws(4, 4, 1, 64, 1, 0, B.PKV_MAX_WORKERS + 1) == 0
+    assert ws(4, 4, 1, 64, 0, 0, 1) == 0        # no block-table columns
+
+
+def test_partition_workspace_bytes_formula():
+    """Fixed partitions: one slot per (sequence, KV head, partition),
+    Pn = ceil(max_blocks * 16 / P); for G = 8 (the long-context fp8 shape:
+    16 x 32768, 64/8 heads, d 128, P = 512 -> Pn = 64) that is
+    S * H_q * Pn * (d + 2) floats, the split-KV partial layout of
+    (m_j, l_j, o_j) per (sequence, query head, partition)."""
+    ws = B.pkv_decode_workspace_bytes
+    S, Hq, H, d, mb = 16, 64, 8, 128, 2048
+    assert ws(S, Hq, H, d, mb, 512, 0) == r256(S * Hq * 64 * (d + 2) * 4) + r256(S * H * 4)
+    assert ws(S, Hq, H, d, mb, 512, 0) == 34078720 + 512
+    # the worker count does not enter; a partial last partition still has a slot
+    assert ws(S, Hq, H, d, mb, 512, 7) == ws(S, Hq, H, d, mb, 512, 0)
+    assert ws(3, 32, 8, 128, 33, 512, 0) == r256(3 * 8 * 2 * _slot_floats(4, 128) * 4) + 256
+    # P = 16: one partition per block; P past the longest context: one partition
+    assert ws(2, 4, 1, 64, 5, 16, 0) == r256(2 * 1 * 5 * _slot_floats(4, 64) * 4) + 256
+    assert ws(2, 4, 1, 64, 5, 4096, 0) == r256(2 * 1 * 1 * _slot_floats(4, 64) * 4) + 256
+    # G = 3 pads to 4-head slots
+    assert ws(2, 3, 1, 64, 4, 32, 0) == r256(2 * 1 * 2 * _slot_floats(4, 64) * 4) + 256
+    for bad in (-16, 8, 520):                   # negative or not a multiple of 16
+        assert ws(S, Hq, H, d, mb, bad, 0) == 0
 
 
 def _decode(**kw):
     a = dict(q=FAKE, q_dtype=B.PKV_F16, S=4, Hq=8, k=FAKE, v=FAKE,
-             desc=B.cache_desc(16, 2, 128, "f16"), bt=FAKE, mb=64, cl=FAKE, scale=0.1, P=0,
-             ws=None, ws_bytes=0, out=FAKE)
+             desc=B.cache_desc(16, 2, 128, "f16"), bt=FAKE, mb=64, cl=FAKE, scale=0.1, Psz=0,
+             W=0, ws=None, ws_bytes=0, out=FAKE)
     a.update(kw)
     return B.lib().pkv_paged_attention_decode(
         a["q"], a["q_dtype"], a["S"], a["Hq"], a["k"], a["v"], ctypes.byref(a["desc"]), a["bt"],
-        a["mb"], a["cl"], a["scale"], a["P"], a["ws"], a["ws_bytes"], a["out"], None)
+        a["mb"], a["cl"], a["scale"], a["Psz"], a["W"], a["ws"], a["ws_bytes"], a["out"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -106,8 +132,13 @@ def _decode(**kw):
     (dict(desc=B.cache_desc(16, 2, 128, "fp8", 0.0, 1.0), q_dtype=B.PKV_BF16),
      B.PKV_ERR_INVALID_ARG),                                  # fp8 needs positive scales
     (dict(q_dtype=7), B.PKV_ERR_UNSUPPORTED),
-    (dict(P=-1), B.PKV_ERR_INVALID_ARG),                      # negative worker count
-    (dict(P=B.PKV_MAX_WORKERS + 1), B.PKV_ERR_UNSUPPORTED),
+    (dict(W=-1), B.PKV_ERR_INVALID_ARG),                      # negative worker count
+    (dict(W=B.PKV_MAX_WORKERS + 1), B.PKV_ERR_UNSUPPORTED),
+    (dict(Psz=-16, ws=FAKE, ws_bytes=1 << 40), B.PKV_ERR_INVALID_ARG),  # negative partition
+    (dict(Psz=24, ws=FAKE, ws_bytes=1 << 40), B.PKV_ERR_INVALID_ARG),   # not a multiple of 16
+    # a balanced-split workspace is too small for 512-token partitions of this shape
+    (dict(Psz=512, S=256, mb=2048, ws=FAKE, ws_bytes=B.pkv_decode_workspace_bytes(
+        256, 8, 2, 128, 2048, 0, 0)), B.PKV_ERR_WORKSPACE),
     (dict(ws=None, ws_bytes=0), B.PKV_ERR_WORKSPACE),         # a workspace is always needed
     (dict(ws=FAKE, ws_bytes=100), B.PKV_ERR_WORKSPACE),
     (dict(ws=FAKE + 16, ws_bytes=1 << 30), B.PKV_ERR_WORKSPACE),  # not 256-byte aligned
@@ -147,12 +178,12 @@ def test_append_rejects_before_any_hip_call(kw, status):
 
 def test_shared_prefix_workspace_bytes_formula():
     S, Hq, H, d, ng, W = 256, 32, 8, 128, 3, 768
-    base = B.pkv_decode_workspace_bytes(S, Hq, H, d, W)  # decode slots + decode counters
+    base = B.pkv_decode_workspace_bytes(S, Hq, H, d, 1, 0, W)  # decode slots + counters
     res = r256(S * Hq * d * 4) + r256(S * Hq * 4)
     slots = r256(4096 * (16 * d + 32) * 4)
     assert B.pkv_shared_prefix_workspace_bytes(S, Hq, H, d, ng, W) == base + res + slots
     assert B.pkv_shared_prefix_workspace_bytes(S, Hq, H, d, ng, 0) == \
-        B.pkv_decode_workspace_bytes(S, Hq, H, d, 0) + res + slots
+        B.pkv_decode_workspace_bytes(S, Hq, H, d, 1, 0, 0) + res + slots
     assert B.pkv_shared_prefix_workspace_bytes(S, Hq, H, d, -1, W) == 0
     assert B.pkv_shared_prefix_workspace_bytes(S, Hq, H, d, S + 1, W) == 0
     assert B.pkv_shared_prefix_workspace_bytes(4, 18, 2, 64, 1, 1) == 0  # G = 9
@@ -244,3 +275,82 @@ def test_gather_rejects_bad_args():
 def test_status_strings():
     for s in (0, -1, -2, -3, -4, 99):
         assert B.status_string(s)
+
+
+# ---- the Python binding checks tensors against the descriptor -----------------
+# (the C side sees pointers only; these checks run before any library call,
+# so CPU tensors show them)
+
+def _decode_tensors(S=4, Hq=8, H=2, d=128, nb=16, mb=4, dt=torch.float16):
+    q = torch.zeros((S, Hq, d), dtype=dt)
+    kc = torch.zeros((nb, H, 16, d), dtype=dt)
+    return dict(q=q, k_cache=kc, v_cache=kc.clone(), block_tables=torch.zeros((S, mb), dtype=torch.int32),
+                context_lens=torch.ones(S, dtype=torch.int32), out=torch.empty_like(q))
+
+
+@pytest.mark.parametrize("change,msg", [
+    (dict(desc=B.cache_desc(16, 2, 64, "f16")), "head_dim"),          # q's d != desc's
+    (dict(desc=B.cache_desc(16, 3, 128, "f16")), "multiple of num_kv_heads"),
+    (dict(desc=B.cache_desc(17, 2, 128, "f16")), "pool needs"),       # caches too small
+    (dict(desc=B.cache_desc(16, 2, 128, "bf16")), "does not match"),  # cache dtype
+    (dict(out=torch.zeros((4, 8, 64), dtype=torch.float16)), "out must match q"),
+    (dict(block_tables=torch.zeros((3, 4), dtype=torch.int32)), "block_tables"),
+    (dict(context_lens=torch.ones(4, dtype=torch.int64)), "context_lens"),
+])
+def test_binding_decode_rejects_mismatch(change, msg):
+    t = _decode_tensors()
+    desc = change.pop("desc", B.cache_desc(16, 2, 128, "f16"))
+    t.update(change)
+    with pytest.raises(ValueError, match=msg):
+        B.pkv_paged_attention_decode(t["q"], t["k_cache"], t["v_cache"], desc, t["block_tables"],
+                                     t["context_lens"], 0.1, t["out"])
+    with pytest.raises(ValueError, match=msg):
+        B.pkv_paged_attention_decode_shared_prefix(
+            t["q"], t["k_cache"], t["v_cache"], desc, t["block_tables"], t["context_lens"],
+            torch.tensor([0, 4], dtype=torch.int32), torch.tensor([1], dtype=torch.int32), 0.1,
+            t["out"])
+
+
+def test_binding_decode_checks_device_last():
+    """Matching CPU tensors pass every shape check and stop at the device check."""
+    t = _decode_tensors()
+    with pytest.raises(ValueError, match="device tensors"):
+        B.pkv_paged_attention_decode(t["q"], t["k_cache"], t["v_cache"],
+                                     B.cache_desc(16, 2, 128, "f16"), t["block_tables"],
+                                     t["context_lens"], 0.1, t["out"])
+
+
+def test_binding_prefill_rejects_mismatch():
+    t = _decode_tensors()
+    qs = torch.tensor([0, 1, 2, 3, 4], dtype=torch.int32)
+    for desc, msg in ((B.cache_desc(16, 2, 64, "f16"), "head_dim"),
+                      (B.cache_desc(32, 2, 128, "f16"), "pool needs")):
+        with pytest.raises(ValueError, match=msg):
+            B.pkv_paged_attention_prefill(t["q"], t["k_cache"], t["v_cache"], desc,
+                                          t["block_tables"], t["context_lens"], qs, 0.1, t["out"])
+
+
+def test_binding_append_rejects_mismatch():
+    kc = torch.zeros((16, 2, 16, 128), dtype=torch.float16)
+    k = torch.zeros((3, 2, 128), dtype=torch.float16)
+    slots = torch.zeros(3, dtype=torch.int64)
+    for desc, kk, msg in ((B.cache_desc(16, 4, 128, "f16"), k, "heads"),
+                          (B.cache_desc(16, 2, 64, "f16"), k, "head_dim"),
+                          (B.cache_desc(20, 2, 128, "f16"), k, "pool needs"),
+                          (B.cache_desc(16, 2, 128, "f16"), torch.zeros((3, 2, 64), dtype=torch.float16),
+                           "head_dim")):
+        with pytest.raises(ValueError, match=msg):
+            B.pkv_kv_append(kk, kk.clone(), slots, kc, kc.clone(), desc)
+
+
+def test_binding_gather_and_copy_reject_mismatch():
+    kc = torch.zeros((16, 2, 16, 64), dtype=torch.float32)
+    desc = B.cache_desc(16, 2, 64, "f32")
+    bt = torch.zeros((2, 3), dtype=torch.int32)
+    cl = torch.ones(2, dtype=torch.int32)
+    small = torch.zeros((2, 2, 40, 64), dtype=torch.float32)   # max_ctx 48 needs 48 rows
+    with pytest.raises(ValueError, match="k_out"):
+        B.pkv_debug_gather(kc, kc.clone(), desc, bt, cl, 48, small, small.clone())
+    with pytest.raises(ValueError, match="pool needs"):
+        B.pkv_copy_blocks(kc, kc.clone(), B.cache_desc(32, 2, 64, "f32"),
+                          torch.zeros((1, 2), dtype=torch.int32))

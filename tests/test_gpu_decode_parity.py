@@ -20,8 +20,8 @@ from tests.helpers import (assert_close, gpu_append, gpu_decode, host_copy, orac
 pytestmark = pytest.mark.gpu
 
 
-def _check(b, num_workers=0, seqs=None, what=""):
-    out = gpu_decode(b, num_workers)
+def _check(b, num_workers=0, seqs=None, what="", partition_size=0):
+    out = gpu_decode(b, num_workers, partition_size=partition_size)
     torch.cuda.synchronize()
     got = out_to_f64(out)
     ref = oracle_decode(b, seqs=seqs)
@@ -71,7 +71,8 @@ def test_gqa40_full_layer_sampled(gpu):
     """One layer of the 40-layer workload at full size (40 x 8192, 32/8 heads,
     fp16, 20,481-block pool), device-default workers; the oracle recomputes
     sequences 0, 17 and 39."""
-    _check(W.gqa40_layer(device=gpu, layer=3), seqs=[0, 17, 39], what="gqa40 full (sampled)")
+    _check(W.gqa40_layer(device=gpu, layer=3), seqs=[0, 11, 17, 28, 39],
+           what="gqa40 full (sampled)")
 
 
 def test_gqa40_tp8_share_sampled(gpu):
@@ -103,9 +104,42 @@ def test_fp8_f16_query(gpu):
 
 
 def test_fp8_full_sampled(gpu):
-    """The long-context fp8 workload at full size (16 x 32768, 64/8 heads);
-    the oracle recomputes sequence 9."""
-    _check(W.fp8_long(device=gpu), seqs=[9], what="fp8 full (sampled)")
+    """The long-context fp8 workload at full size (16 x 32768, 64/8 heads),
+    balanced split; the oracle recomputes sequences 0, 9 and 15."""
+    _check(W.fp8_long(device=gpu), seqs=[0, 9, 15], what="fp8 full (sampled)")
+
+
+def test_fp8_full_partition_512_sampled(gpu):
+    """The long-context fp8 workload at full size split into 512-token
+    partitions (64 per sequence, merged by log-sum-exp), the device-default
+    worker count for that split; the oracle recomputes sequences 0, 6, 9 and
+    15. The balanced split of the same batch agrees to float32 rounding."""
+    b = W.fp8_long(device=gpu)
+    got, ref = _check(b, seqs=[0, 6, 9, 15], partition_size=512, what="fp8 full P=512 (sampled)")
+    bal = out_to_f64(gpu_decode(b))[np.asarray([0, 6, 9, 15])]
+    assert np.abs(bal - got).max() <= 2e-2
+
+
+@pytest.mark.parametrize("P", [16, 48, 512, 8192, 16384])
+def test_fixed_partitions_ragged(gpu, P):
+    """Fixed partitions of P tokens over ragged lengths (one partition, a
+    partial last partition, up to 512 partitions per segment), several
+    worker counts (each wave holding whole partitions)."""
+    ctx = [1, 15, 16, 17, 511, 512, 513, 1000, 4097, 8192]
+    b = W.make_batch("gqa40-ragged", 31, ctx, 32, 8, 128, "f16", "f16", device=gpu, canary=True)
+    for nw in (0, 1, 7, 333, 4096):
+        _check(b, num_workers=nw, partition_size=P, what=f"ragged P={P} workers={nw}")
+
+
+@pytest.mark.parametrize("Hq,H,d,kv", [(4, 1, 64, "f32"), (6, 2, 64, "bf16"), (7, 1, 128, "f16"),
+                                       (16, 2, 64, "fp8"), (8, 1, 128, "bf16")])
+def test_fixed_partitions_head_shapes(gpu, Hq, H, d, kv):
+    q_dtype = "bf16" if kv == "fp8" else kv
+    b = W.make_batch("shapes-part", 161 + Hq + H, [1, 5, 16, 47, 300, 1100, 2049], Hq, H, d, kv,
+                     q_dtype, device=gpu, canary=True)
+    for P, nw in ((32, 0), (64, 3), (256, 50)):
+        _check(b, num_workers=nw, partition_size=P,
+               what=f"Hq={Hq} H={H} d={d} {kv} P={P} workers={nw}")
 
 
 @pytest.mark.parametrize("Hq,H,d,kv", [(4, 1, 64, "f32"), (8, 8, 64, "f16"), (6, 2, 64, "bf16"),

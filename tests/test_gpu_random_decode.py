@@ -4,7 +4,8 @@ the oracle.
 Each case draws its own shape: the cache type (and the query type that goes
 with it), d 64 or 128, G = 1..8, 1..4 KV heads, and ragged context lengths
 from one token to a few thousand (short, medium and long ones mixed), with the
-device's default worker count or a random one. The shared-prefix cases also
+device's default worker count or a random one, and the balanced split or
+fixed partitions of a random size. The shared-prefix cases also
 draw contiguous prefix groups (0..20 shared blocks, members holding their
 prefix plus 0..100 tokens) with ungrouped sequences between them."""
 import numpy as np
@@ -43,11 +44,13 @@ def test_random_decode(gpu, seed):
     S = int(rng.integers(1, 49))
     ctx = [_length(rng) for _ in range(S)]
     workers = 0 if rng.random() < 0.5 else int(rng.integers(1, 301))
-    what = f"seed {seed}: {kv}/{qd} d={d} Hq={Hq} H={H} S={S} workers={workers}"
+    # the balanced split, or fixed partitions of 16..1024 tokens
+    part = 0 if rng.random() < 0.5 else 16 * int(rng.integers(1, 65))
+    what = f"seed {seed}: {kv}/{qd} d={d} Hq={Hq} H={H} S={S} workers={workers} partition={part}"
     print(f"[case] {what} ctx={ctx}", flush=True)
     b = W.make_batch("random-decode", 3000 + seed, ctx, Hq, H, d, kv, qd, device=gpu,
                      pool_factor=1.3, canary=True)
-    got = out_to_f64(gpu_decode(b, num_workers=workers))
+    got = out_to_f64(gpu_decode(b, num_workers=workers, partition_size=part))
     e = assert_close(got, oracle_decode(b), kv, what)
     print(f"[parity] {what}: {e}", flush=True)
 
