@@ -75,6 +75,7 @@ typedef struct ihipStream_t *hipStream_t;
 #define PKV_ERR_UNSUPPORTED (-2) /* valid but not built: dtype pair, head_dim, group */
 #define PKV_ERR_WORKSPACE (-3)   /* workspace missing or smaller than required */
 #define PKV_ERR_HIP (-4)         /* a HIP launch reported an error */
+#define PKV_ERR_TOO_LARGE (-5)   /* beyond the allocation-free entry point's static scratch */
 
 /* Element types. PKV_FP8_E4M3 is OCP E4M3FN: 1 sign, 4 exponent bits
  * (bias 7), 3 mantissa bits, no infinities, NaN = 0x7F / 0xFF, largest
@@ -245,6 +246,36 @@ int pkv_paged_attention_decode(const void *q, int32_t q_dtype, int32_t num_seqs,
                                float scale, int32_t partition_size, int32_t num_workers,
                                void *workspace, size_t workspace_bytes, void *out,
                                hipStream_t stream);
+
+/* Bytes of the static device scratch array behind
+ * pkv_paged_attention_decode_noalloc (one per GPU the library runs on, held
+ * until the process ends). */
+#define PKV_NOALLOC_SCRATCH_BYTES (48u << 20)
+
+/* pkv_paged_attention_decode without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. The call allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine): its workspace is a
+ * static device array of PKV_NOALLOC_SCRATCH_BYTES, one per GPU, whose
+ * device address is taken on the first call on that GPU (make that first
+ * call outside a graph capture). Each call first zeroes the counters it uses
+ * (a small kernel on the stream, no memset), then runs the same decode
+ * kernel as pkv_paged_attention_decode, so for the same arguments the output
+ * is bit-for-bit the same.
+ * All arguments, results and errors as for pkv_paged_attention_decode, plus
+ * PKV_ERR_TOO_LARGE (before any HIP call) when
+ * pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+ * max_blocks_per_seq, partition_size, num_workers) exceeds
+ * PKV_NOALLOC_SCRATCH_BYTES. Every call on a GPU shares that GPU's array:
+ * calls that overlap on one GPU (other streams, other host threads) race and
+ * must be serialised by the caller. */
+int pkv_paged_attention_decode_noalloc(const void *q, int32_t q_dtype, int32_t num_seqs,
+                                       int32_t num_q_heads, const void *k_cache,
+                                       const void *v_cache, const pkv_cache_desc *cache,
+                                       const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t *context_lens, float scale,
+                                       int32_t partition_size, int32_t num_workers, void *out,
+                                       hipStream_t stream);
 
 /* Workspace bytes pkv_paged_attention_decode_shared_prefix needs. Front:
  * the decode slots for the worker count, float32 suffix results

@@ -23,10 +23,12 @@ PKV_ERR_INVALID_ARG = -1
 PKV_ERR_UNSUPPORTED = -2
 PKV_ERR_WORKSPACE = -3
 PKV_ERR_HIP = -4
+PKV_ERR_TOO_LARGE = -5
 
 PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2, 3
 PKV_BLOCK_SIZE = 16
 PKV_MAX_WORKERS = 4096
+PKV_NOALLOC_SCRATCH_BYTES = 48 << 20
 
 DTYPE_CODES = {"f32": PKV_F32, "f16": PKV_F16, "bf16": PKV_BF16, "fp8": PKV_FP8_E4M3}
 _TORCH_CODES = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
@@ -35,7 +37,7 @@ EXPORTS = ("pkv_status_string", "pkv_kv_bytes_per_token", "pkv_cache_tensor_byte
            "pkv_kv_append", "pkv_decode_workspace_bytes", "pkv_paged_attention_decode",
            "pkv_shared_prefix_workspace_bytes", "pkv_paged_attention_decode_shared_prefix",
            "pkv_paged_attention_prefill", "pkv_prefill_workspace_bytes", "pkv_copy_blocks",
-           "pkv_debug_gather",
+           "pkv_debug_gather", "pkv_paged_attention_decode_noalloc",
            # host block manager (pkv_blocks.h; bound in blocks.py)
            "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_num_free_blocks", "pkv_bm_add_request",
            "pkv_bm_can_append", "pkv_bm_append", "pkv_bm_fork", "pkv_bm_free_request",
@@ -83,6 +85,9 @@ def lib():
         L.pkv_paged_attention_decode.argtypes = [vp, i32, i32, i32, vp, vp, descp, vp, i32, vp,
                                                  f32, i32, i32, vp, sz, vp, vp]
         L.pkv_paged_attention_decode.restype = ctypes.c_int
+        L.pkv_paged_attention_decode_noalloc.argtypes = [vp, i32, i32, i32, vp, vp, descp, vp,
+                                                         i32, vp, f32, i32, i32, vp, vp]
+        L.pkv_paged_attention_decode_noalloc.restype = ctypes.c_int
         L.pkv_shared_prefix_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
         L.pkv_shared_prefix_workspace_bytes.restype = sz
         L.pkv_paged_attention_decode_shared_prefix.argtypes = [
@@ -288,6 +293,24 @@ def pkv_paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: 
         _ptr(block_tables), mb, _ptr(context_lens), float(scale), partition_size, num_workers,
         _ptr(workspace), _nbytes(workspace), _ptr(out), _stream(stream))
     _check("pkv_paged_attention_decode", rc)
+
+
+def pkv_paged_attention_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor,
+                                       v_cache: torch.Tensor, desc: pkv_cache_desc,
+                                       block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                       scale: float, out: torch.Tensor, num_workers: int = 0,
+                                       stream=None, partition_size: int = 0) -> None:
+    """pkv_paged_attention_decode with the library's static scratch as its
+    workspace: nothing is allocated, here or in the library (for graph
+    capture and loops that must not allocate). Calls that overlap on one GPU
+    share that scratch and race."""
+    _check_decode_args(q, k_cache, v_cache, desc, block_tables, context_lens, out)
+    S, Hq, d = q.shape
+    rc = lib().pkv_paged_attention_decode_noalloc(
+        _ptr(q), _dtype_of(q), S, Hq, _ptr(k_cache), _ptr(v_cache), ctypes.byref(desc),
+        _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), float(scale),
+        partition_size, num_workers, _ptr(out), _stream(stream))
+    _check("pkv_paged_attention_decode_noalloc", rc)
 
 
 def pkv_shared_prefix_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int,

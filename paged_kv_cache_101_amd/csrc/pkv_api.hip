@@ -4,6 +4,9 @@
 // validated arguments.
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "pkv.h"
 #include "pkv_internal.h"
 
@@ -44,6 +47,8 @@ PKV_EXPORT const char* pkv_status_string(int status) {
     case PKV_ERR_UNSUPPORTED: return "unsupported configuration";
     case PKV_ERR_WORKSPACE: return "workspace missing or too small";
     case PKV_ERR_HIP: return "HIP launch error";
+    case PKV_ERR_TOO_LARGE:
+        return "batch needs more scratch than the allocation-free entry point's static buffer";
     default: return "unknown status";
     }
 }
@@ -349,3 +354,87 @@ PKV_EXPORT int pkv_debug_gather(const void* k_cache, const void* v_cache,
     return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+// ---- allocation-free decode ------------------------------------------------
+//
+// For callers that cannot allocate (code under HIP graph capture, tight
+// serving loops, harnesses that forbid hipMalloc): the decode workspace is a
+// static device array, one copy per GPU, held from the library's load on that
+// GPU until the process ends. In host code `scratch` names a host-side
+// stand-in, not device memory: only its device address, taken once per
+// device with hipGetSymbolAddress, is ever passed on.
+
+static __device__ __align__(256) uint8_t scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch array (taken on the first
+// call on that device).
+int current_scratch(void** ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return PKV_ERR_HIP;
+    if (dev < 0 || dev >= kMaxScratchDevices) return PKV_ERR_UNSUPPORTED;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+                return PKV_ERR_HIP;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return PKV_OK;
+}
+
+// Zero n int32 counters (a kernel rather than a memset, so the call can be
+// captured in a HIP graph).
+__global__ void clear_counters_kernel(int32_t* c, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+        c[i] = 0;
+}
+
+}  // namespace
+
+PKV_EXPORT int pkv_paged_attention_decode_noalloc(const void* q, int32_t q_dtype,
+                                                  int32_t num_seqs, int32_t num_q_heads,
+                                                  const void* k_cache, const void* v_cache,
+                                                  const pkv_cache_desc* cache,
+                                                  const int32_t* block_tables,
+                                                  int32_t max_blocks_per_seq,
+                                                  const int32_t* context_lens, float scale,
+                                                  int32_t partition_size, int32_t num_workers,
+                                                  void* out, hipStream_t stream) {
+    pkv::DecodeArgs a;
+    // the same checks as pkv_paged_attention_decode (the workspace is ours)
+    const int rc = decode_args(a, q, q_dtype, num_seqs, num_q_heads, k_cache, v_cache, cache,
+                               block_tables, max_blocks_per_seq, context_lens, scale, num_workers,
+                               false, nullptr, out, stream);
+    if (rc != PKV_OK) return rc;
+    if (!partition_ok(partition_size)) return PKV_ERR_INVALID_ARG;
+    const size_t need = pkv_decode_workspace_bytes(num_seqs, num_q_heads, cache->num_kv_heads,
+                                                   cache->head_dim, max_blocks_per_seq,
+                                                   partition_size, num_workers);
+    if (need == 0) return PKV_ERR_INVALID_ARG;
+    if (need > PKV_NOALLOC_SCRATCH_BYTES) return PKV_ERR_TOO_LARGE;
+    void* ws = nullptr;
+    const int src = current_scratch(&ws);
+    if (src != PKV_OK) return src;
+    // the counters: the last bytes of the array, cleared for this call
+    const size_t ctr_bytes = pkv::decode_counter_bytes(num_seqs, cache->num_kv_heads);
+    int32_t* counters = reinterpret_cast<int32_t*>(
+        static_cast<char*>(ws) + pkv::tail_offset(PKV_NOALLOC_SCRATCH_BYTES, ctr_bytes));
+    const int n = (int)(ctr_bytes / sizeof(int32_t));
+    hipLaunchKernelGGL(clear_counters_kernel, dim3((n + 255) / 256 < 64 ? (n + 255) / 256 : 64),
+                       dim3(256), 0, stream, counters, n);
+    if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
+    a.partition_size = partition_size;
+    a.slots = static_cast<float*>(ws);
+    a.counters = counters;
+    hipError_t err = pkv::launch_paged_decode(a);
+    return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}

@@ -272,8 +272,31 @@ def test_gather_rejects_bad_args():
                               None) == B.PKV_ERR_INVALID_ARG
 
 
+def test_noalloc_rejects_before_any_hip_call():
+    """The allocation-free decode checks its arguments like decode, and a
+    batch whose workspace would exceed the static scratch is refused before
+    any HIP call."""
+    L = B.lib()
+
+    def call(S=4, Hq=8, mb=64, P=0, W=0, q=FAKE):
+        return L.pkv_paged_attention_decode_noalloc(
+            q, B.PKV_F16, S, Hq, FAKE, FAKE, ctypes.byref(B.cache_desc(16, 2, 128, "f16")), FAKE,
+            mb, FAKE, 0.1, P, W, FAKE, None)
+    assert call(q=None) == B.PKV_ERR_INVALID_ARG
+    assert call(Hq=18) == B.PKV_ERR_UNSUPPORTED
+    assert call(P=24) == B.PKV_ERR_INVALID_ARG
+    assert call(W=-1) == B.PKV_ERR_INVALID_ARG
+    # 256 sequences x 2 KV heads x 2048 blocks in 16-token partitions: far past the scratch
+    assert B.pkv_decode_workspace_bytes(256, 8, 2, 128, 2048, 16, 0) > B.PKV_NOALLOC_SCRATCH_BYTES
+    assert call(S=256, mb=2048, P=16) == B.PKV_ERR_TOO_LARGE
+    # the long-context fp8 shape at 512-token partitions fits
+    assert B.pkv_decode_workspace_bytes(16, 64, 8, 128, 2048, 512, 0) <= B.PKV_NOALLOC_SCRATCH_BYTES
+    # so does the default worker count at the largest group and head size
+    assert B.pkv_decode_workspace_bytes(1024, 64, 8, 128, 1, 0, 0) <= B.PKV_NOALLOC_SCRATCH_BYTES
+
+
 def test_status_strings():
-    for s in (0, -1, -2, -3, -4, 99):
+    for s in (0, -1, -2, -3, -4, -5, 99):
         assert B.status_string(s)
 
 
