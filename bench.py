@@ -27,6 +27,17 @@ logical bytes plain decode would read. --cold adds launches timed after a
 1 GiB write that evicts the caches (a small layer such as qwen's otherwise
 stays in the 256 MB MALL between iterations).
 
+Beside the peak, the line reports `achievable_read`: the bandwidth of a plain
+streaming read (pkv_stream_read, 16-byte nontemporal loads) over as many bytes
+as one decode launch reads, and roofline.frac_of_achievable. The default
+gqa40 line also carries `workloads`: the Qwen2.5-1.5B-shaped layer (append +
+decode, warm and after a cache-evicting write) and the long-context fp8 batch
+(quantising append + decode, balanced split and 512-token partitions), each
+timed after the headline's timed region (--no-summaries skips them).
+Every workload with new token rows appends them before decode in its step;
+the append calls are timed by their own events in extra steps outside the
+timed region.
+
 --workload prefill times one chunked-prefill step (four 2048-token chunks at
 contexts 2048..8192, fp16, the 32/8-head d-128 shape) in TFLOP/s against the
 matrix-core peak; --workload prefill_small times eight 16-token chunks over
@@ -79,6 +90,8 @@ def parse():
     ap.add_argument("--partition-size", type=int, default=0,
                     help="decode split: 0 = balanced split, else tokens per fixed partition")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-summaries", action="store_true",
+                    help="skip the Qwen-shaped and fp8 summaries of the default gqa40 line")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured in a HIP graph and replayed (reported as "
                          "a 'graph' object; value and roofline stay the eager, event-timed run)")
@@ -144,7 +157,7 @@ def build_layers(workload: str, device):
     elif workload in ("prefix", "prefix_shared"):
         layers = [W.prefix_shared(device=device)]
     elif workload == "fp8":
-        layers = [W.fp8_long(device=device)]
+        layers = [W.fp8_long(device=device, append_last=True)]
     else:
         layers = [W.tiny(device=device)]
     return layers
@@ -326,6 +339,232 @@ def bench_prefill(args):
     print(json.dumps(line), flush=True)
 
 
+def cpu_model() -> str:
+    """The host CPU's model name, as lscpu reports it (else /proc/cpuinfo)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.strip().lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def achievable_read_bandwidth(nbytes: int, steps: int, dev) -> dict:
+    """The read bandwidth a plain streaming kernel gets on this device
+    (pkv_stream_read over a buffer of nbytes, the decode launch's KV bytes),
+    timed with HIP events on the launch stream."""
+    import torch
+    from paged_kv_cache_101_amd import binding as B
+    nbytes = max(16, nbytes // 16 * 16)
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        B.pkv_stream_read(buf, sink)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        B.pkv_stream_read(buf, sink)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = statistics.fmean(a.elapsed_time(b) for a, b in evs)
+    del buf
+    return {"gbps": round(nbytes / (ms * 1e-3) / 1e9, 1), "bytes": nbytes,
+            "launch_avg_us": round(ms * 1e3, 2),
+            "kernel": "stream_read_kernel (pkv_stream_read: 16-byte nontemporal loads, "
+                      "one workgroup of 256 threads per CU, 8 loads in flight per thread)"}
+
+
+class DecodeRun:
+    """The layers of one decode workload, their library caches and the
+    calls of one step: optionally the append of each layer's new token rows
+    (a quantising append for fp8 caches), then the decode call."""
+
+    def __init__(self, workload: str, dev, workers: int, partition_size: int, append: bool):
+        import torch
+        from paged_kv_cache_101_amd import binding as B
+        from paged_kv_cache_101_amd import workloads as W
+        self.B, self.W, self.torch = B, W, torch
+        self.workload, self.workers, self.partition_size = workload, workers, partition_size
+        self.layers = build_layers(workload, dev)
+        self.descs = [B.desc_for(b.k_cache, b.kv_dtype, b.k_scale, b.v_scale) for b in self.layers]
+        # The library's caches, filled from each layer's token rows with
+        # pkv_kv_append (the row-order copies are dropped after, except layer
+        # 0's, which the CPU baseline reads).
+        self.caches = []
+        for i, b in enumerate(self.layers):
+            self.caches.append(B.fill_cache(b.k_cache, b.v_cache, self.descs[i]))
+            if i > 0:
+                b.k_cache = b.v_cache = None
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        self.outs = [torch.empty_like(b.q) for b in self.layers]
+        b0 = self.layers[0]
+        self.shared = workload == "prefix_shared"
+        if self.shared:
+            ng = int(b0.group_prefix.numel())
+            self.ws = B.shared_prefix_workspace(b0.num_seqs, b0.num_q_heads, b0.num_kv_heads,
+                                                b0.head_dim, ng, workers, dev)
+        else:
+            self.ws = B.decode_workspace(b0.num_seqs, b0.num_q_heads, b0.num_kv_heads,
+                                         b0.head_dim, workers, dev, b0.max_blocks_per_seq,
+                                         partition_size)
+        self.append = append and b0.slot_mapping is not None
+        self.stream = torch.cuda.current_stream()
+        torch.cuda.synchronize()
+
+    def decode(self, i):
+        b, B = self.layers[i], self.B
+        if self.shared:
+            B.pkv_paged_attention_decode_shared_prefix(
+                b.q, *self.caches[i], self.descs[i], b.block_tables, b.context_lens,
+                b.group_starts, b.group_prefix, b.scale, self.outs[i], num_workers=self.workers,
+                workspace=self.ws)
+        else:
+            B.pkv_paged_attention_decode(b.q, *self.caches[i], self.descs[i], b.block_tables,
+                                         b.context_lens, b.scale, self.outs[i],
+                                         num_workers=self.workers, workspace=self.ws,
+                                         partition_size=self.partition_size)
+
+    def append_rows(self, i):
+        b = self.layers[i]
+        k, v = (b.new_k, b.new_v) if b.new_k_rows is None else (b.new_k_rows, b.new_v_rows)
+        self.B.pkv_kv_append(k, v, b.slot_mapping, *self.caches[i], self.descs[i])
+
+    def step(self, evs=None, aevs=None):
+        """One step; evs / aevs: per-layer (start, end) event pairs recorded
+        around each decode / append call."""
+        for i in range(len(self.layers)):
+            if self.append:
+                if aevs is not None:
+                    aevs[i][0].record(self.stream)
+                self.append_rows(i)
+                if aevs is not None:
+                    aevs[i][1].record(self.stream)
+            if evs is not None:
+                evs[i][0].record(self.stream)
+            self.decode(i)
+            if evs is not None:
+                evs[i][1].record(self.stream)
+
+    def kv_bytes_per_launch(self) -> int:
+        """Algorithmic KV bytes of one decode call (unique bytes for the
+        shared-prefix path: every physical row some sequence reads, once)."""
+        b0, W = self.layers[0], self.W
+        if self.shared:
+            used = W.used_rows_per_block(b0.block_tables.cpu().numpy(),
+                                         b0.context_lens.cpu().numpy(), b0.num_blocks)
+            return int(used.sum()) * 2 * b0.num_kv_heads * b0.head_dim * W.STORAGE[b0.kv_dtype][1]
+        return b0.kv_bytes()
+
+    def _events(self):
+        torch = self.torch
+        return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in self.layers]
+
+    def timed(self, steps: int, warmup: int) -> dict:
+        """Warm-up steps, then `steps` timed ones: the whole region between
+        two events, and every decode call by its own events. The append calls
+        are then timed alone by their own events in `steps` more steps
+        (outside the timed region, whose events would otherwise add gaps)."""
+        torch = self.torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        evs = [self._events() for _ in range(steps)]
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(self.stream)
+        for s in range(steps):
+            self.step(evs[s])
+        t1.record(self.stream)
+        torch.cuda.synchronize()
+        dec = sorted(a.elapsed_time(b) for st in evs for (a, b) in st)
+        r = {"ms_per_step": t0.elapsed_time(t1) / steps, "decode_ms": dec,
+             "decode_avg_ms": statistics.fmean(dec)}
+        if self.append:
+            aevs = [self._events() for _ in range(steps)]
+            for s in range(steps):
+                self.step(None, aevs[s])
+            torch.cuda.synchronize()
+            r["append_avg_ms"] = statistics.fmean(a.elapsed_time(b) for st in aevs
+                                                  for (a, b) in st)
+        return r
+
+    def cold(self, steps: int) -> dict:
+        """Decode calls each timed after a 1 GiB device write that evicts the
+        L2 caches and the 256 MB MALL (the call then reads its KV from HBM)."""
+        torch = self.torch
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=self.outs[0].device)
+        pairs = []
+        for s in range(steps):
+            for i in range(len(self.layers)):
+                scratch.fill_(s & 0xFF)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(self.stream)
+                self.decode(i)
+                e1.record(self.stream)
+                pairs.append((e0, e1))
+        torch.cuda.synchronize()
+        cms = sorted(a.elapsed_time(b) for a, b in pairs)
+        del scratch
+        cavg = statistics.fmean(cms)
+        nb = self.kv_bytes_per_launch()
+        return {"launch_avg_us": round(cavg * 1e3, 2),
+                "launch_p10_us": round(cms[len(cms) // 10] * 1e3, 2),
+                "launch_p90_us": round(cms[(9 * len(cms)) // 10] * 1e3, 2),
+                "achieved_gbps": round(nb / (cavg * 1e-3) / 1e9, 1),
+                "frac": round(nb / (cavg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+    def free(self):
+        self.layers = self.caches = self.outs = self.ws = None
+        self.torch.cuda.synchronize()
+        self.torch.cuda.empty_cache()
+
+
+def summary(workload: str, dev, steps: int, warmup: int, partition_sizes=(0,),
+            cold: bool = False) -> dict:
+    """A compact record of another workload's step (append + decode), for
+    the headline line: per partition size, the decode call's average time
+    and roofline fraction, the append's time, and the step's."""
+    res = {}
+    run = None
+    for P in partition_sizes:
+        run = DecodeRun(workload, dev, 0, P, append=True)
+        t = run.timed(steps, warmup)
+        nb = run.kv_bytes_per_launch()
+        b0 = run.layers[0]
+        rec = {"decode_avg_us": round(t["decode_avg_ms"] * 1e3, 2),
+               "decode_p10_us": round(t["decode_ms"][len(t["decode_ms"]) // 10] * 1e3, 2),
+               "decode_p90_us": round(t["decode_ms"][(9 * len(t["decode_ms"])) // 10] * 1e3, 2),
+               "achieved_gbps": round(nb / (t["decode_avg_ms"] * 1e-3) / 1e9, 1),
+               "frac": round(nb / (t["decode_avg_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+               "step_us": round(t["ms_per_step"] * 1e3, 2),
+               "decode_seqs_per_s": round(b0.num_seqs / (t["ms_per_step"] * 1e-3), 1),
+               "kv_bytes_per_launch": nb}
+        if "append_avg_ms" in t:
+            rec["append_avg_us"] = round(t["append_avg_ms"] * 1e3, 2)
+        if cold:
+            rec["cold"] = run.cold(max(5, steps // 2))
+        res["balanced" if P == 0 else f"partition_{P}"] = rec
+        run.free()
+    return res
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -337,7 +576,6 @@ def main():
 
     import torch
     from paged_kv_cache_101_amd import binding as B
-    from paged_kv_cache_101_amd import workloads as W
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
@@ -348,112 +586,52 @@ def main():
         return
     B.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
-    layers = build_layers(args.workload, dev)
-    descs = [B.desc_for(b.k_cache, b.kv_dtype, b.k_scale, b.v_scale) for b in layers]
-    # The library's caches, filled from each layer's token rows with
-    # pkv_kv_append (the row-order copies are dropped after, except layer 0's,
-    # which the CPU baseline reads).
-    caches = []
-    for i, b in enumerate(layers):
-        caches.append(B.fill_cache(b.k_cache, b.v_cache, descs[i]))
-        if i > 0:
-            b.k_cache = b.v_cache = None
-    torch.cuda.synchronize()
-    torch.cuda.empty_cache()
-    outs = [torch.empty_like(b.q) for b in layers]
-    b0 = layers[0]
-    shared = args.workload == "prefix_shared"
-    if shared:
-        ng = int(b0.group_prefix.numel())
-        ws = B.shared_prefix_workspace(b0.num_seqs, b0.num_q_heads, b0.num_kv_heads, b0.head_dim,
-                                       ng, args.workers, dev)
-    else:
-        ws = B.decode_workspace(b0.num_seqs, b0.num_q_heads, b0.num_kv_heads, b0.head_dim,
-                                args.workers, dev, b0.max_blocks_per_seq, args.partition_size)
-    do_append = args.workload in ("gqa40", "gqa40_tp8")
-    stream = torch.cuda.current_stream()
-    torch.cuda.synchronize()
+    # every workload's step appends its new token rows (where it has them:
+    # the 40-layer steps, the Qwen-shaped layer, the fp8 batch) before decode
+    run = DecodeRun(args.workload, dev, args.workers, args.partition_size, append=True)
+    t = run.timed(args.steps, args.warmup)
+    layers, b0 = run.layers, run.layers[0]
+    shared = run.shared
 
-    def decode(i):
-        b = layers[i]
-        if shared:
-            B.pkv_paged_attention_decode_shared_prefix(
-                b.q, *caches[i], descs[i], b.block_tables, b.context_lens, b.group_starts,
-                b.group_prefix, b.scale, outs[i], num_workers=args.workers, workspace=ws)
-        else:
-            B.pkv_paged_attention_decode(b.q, *caches[i], descs[i], b.block_tables,
-                                         b.context_lens, b.scale, outs[i],
-                                         num_workers=args.workers, workspace=ws,
-                                         partition_size=args.partition_size)
-
-    def step(evs=None):
-        for i, b in enumerate(layers):
-            if do_append:
-                B.pkv_kv_append(b.new_k, b.new_v, b.slot_mapping, *caches[i], descs[i])
-            if evs is not None:
-                evs[i][0].record(stream)
-            decode(i)
-            if evs is not None:
-                evs[i][1].record(stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in layers] for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for s in range(args.steps):
-        step(evs[s])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-
-    ms_total = t_start.elapsed_time(t_end)
-    ms_step = ms_total / args.steps
-    decode_ms = [a.elapsed_time(b) for st in evs for (a, b) in st]
-    decode_avg_ms = statistics.fmean(decode_ms)
-    kv_bytes_step = sum(b.kv_bytes() for b in layers)
-    kv_bytes_launch = b0.kv_bytes()
-    logical_launch = kv_bytes_launch
-    if shared:
-        # bytes a call must read: every physical row some sequence attends to, once
-        used = W.used_rows_per_block(b0.block_tables.cpu().numpy(), b0.context_lens.cpu().numpy(),
-                                     b0.num_blocks)
-        kv_bytes_launch = int(used.sum()) * 2 * b0.num_kv_heads * b0.head_dim * \
-            W.STORAGE[b0.kv_dtype][1]
-        kv_bytes_step = kv_bytes_launch * len(layers)
+    ms_step = t["ms_per_step"]
+    decode_ms = t["decode_ms"]
+    decode_avg_ms = t["decode_avg_ms"]
+    kv_bytes_launch = run.kv_bytes_per_launch()
+    logical_launch = b0.kv_bytes()
+    kv_bytes_step = kv_bytes_launch * len(layers)
     seqs = b0.num_seqs
     value = kv_bytes_step / (ms_step * 1e-3) / 1e9
     achieved = kv_bytes_launch / (decode_avg_ms * 1e-3) / 1e9
-    traffic = load_traffic(args.workload)
+    traffic = load_traffic(args.workload if args.partition_size == 0 else
+                           f"{args.workload}_p{args.partition_size}")
+    kernel = ("paged_decode_kernel suffix pass + paged_prefill_kernel prefix mode + chunk_merge_kernel "
+              "(pkv_paged_attention_decode_shared_prefix)" if shared else
+              "paged_decode_kernel + partition_merge_kernel (pkv_paged_attention_decode, fixed "
+              f"{args.partition_size}-token partitions)" if args.partition_size else
+              "paged_decode_kernel (one launch per pkv_paged_attention_decode call)")
     roofline = {
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-        "kernel": ("paged_decode_kernel suffix pass + paged_prefill_kernel prefix mode (two launches per "
-                   "pkv_paged_attention_decode_shared_prefix call)" if shared else
-                   "paged_decode_kernel (one launch per pkv_paged_attention_decode call)"),
+        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
         "algorithmic_bytes_per_launch": kv_bytes_launch,
         "launch_avg_us": round(decode_avg_ms * 1e3, 2),
-        "launch_p10_us": round(sorted(decode_ms)[len(decode_ms) // 10] * 1e3, 2),
-        "launch_p90_us": round(sorted(decode_ms)[(9 * len(decode_ms)) // 10] * 1e3, 2),
+        "launch_p10_us": round(decode_ms[len(decode_ms) // 10] * 1e3, 2),
+        "launch_p90_us": round(decode_ms[(9 * len(decode_ms)) // 10] * 1e3, 2),
     }
     graph = None
     if args.graph:
         # the whole step (every append and decode launch) captured once and
         # replayed: the launches are the same, only the host submission and
         # the dispatch gaps between dependent kernels change
+        stream = run.stream
         side = torch.cuda.Stream()
         side.wait_stream(stream)
         with torch.cuda.stream(side):
-            step()
+            run.step()
         stream.wait_stream(side)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            step()
+            run.step()
         for _ in range(args.warmup):
             g.replay()
         torch.cuda.synchronize()
@@ -468,32 +646,11 @@ def main():
         graph = {"ms_per_step": round(gms, 4), "value": round(kv_bytes_step / (gms * 1e-3) / 1e9, 1),
                  "unit": "GB/s", "steps": args.steps}
         del g
-    cold = None
-    if args.cold:
-        # a 1 GiB write before every decode launch, outside its events
-        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        cold_ms = []
-        for s in range(args.steps):
-            for i in range(len(layers)):
-                scratch.fill_(s & 0xFF)
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                decode(i)
-                e1.record(stream)
-                cold_ms.append((e0, e1))
-        torch.cuda.synchronize()
-        cms = sorted(a.elapsed_time(b) for a, b in cold_ms)
-        cavg = statistics.fmean(cms)
-        del scratch
-        cold = {"launch_avg_us": round(cavg * 1e3, 2),
-                "launch_p10_us": round(cms[len(cms) // 10] * 1e3, 2),
-                "launch_p90_us": round(cms[(9 * len(cms)) // 10] * 1e3, 2),
-                "achieved_gbps": round(kv_bytes_launch / (cavg * 1e-3) / 1e9, 1),
-                "frac": round(kv_bytes_launch / (cavg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    cold = run.cold(args.steps) if args.cold else None
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(b0, args.cpu_seconds)
+        cpu["cpu_model"] = cpu_model()
     line = {
         "metric": "paged decode attention: achieved HBM GB/s (% of peak) + decode seqs/sec",
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -505,6 +662,10 @@ def main():
         "kv_bytes_per_step": kv_bytes_step,
         "roofline": roofline, "cpu_baseline": cpu,
     }
+    if args.partition_size:
+        line["config"]["partition_size"] = args.partition_size
+    if "append_avg_ms" in t:
+        line["append_avg_us"] = round(t["append_avg_ms"] * 1e3, 2)
     if cold is not None:
         line["cold"] = cold
     if graph is not None:
@@ -512,6 +673,19 @@ def main():
     if shared:
         line["logical_kv_bytes_per_launch"] = logical_launch
         line["logical_kv_gbps"] = round(logical_launch / (decode_avg_ms * 1e-3) / 1e9, 1)
+    run.free()
+    # the read bandwidth a plain streaming kernel gets here, over as many
+    # bytes as one decode launch reads
+    ach = achievable_read_bandwidth(kv_bytes_launch, max(10, args.steps), dev)
+    line["achievable_read"] = ach
+    line["roofline"]["frac_of_achievable"] = round(achieved / ach["gbps"], 4)
+    if args.workload == "gqa40" and not args.no_summaries:
+        # the other single-GPU configurations, each one step of append +
+        # decode, outside the headline's timed region
+        line["workloads"] = {
+            "qwen2.5_1.5b_layer": summary("qwen", dev, 20, 3, cold=True),
+            "fp8_long_32k": summary("fp8", dev, 10, 3, partition_sizes=(0, 512)),
+        }
     print(json.dumps(line), flush=True)
 
 

@@ -410,6 +410,21 @@ int pkv_debug_gather(const void *k_cache, const void *v_cache, const pkv_cache_d
                      const int32_t *context_lens, int32_t num_seqs, int32_t max_ctx, void *k_out,
                      void *v_out, hipStream_t stream);
 
+/* Measurement helper, not part of the attention path: read `bytes` of
+ * device memory at `src` once as a plain stream of 16-byte nontemporal
+ * loads (the decode kernel's load width and cache policy), spread over
+ * num_workgroups workgroups of 256 threads (0 = one per compute unit), and XOR
+ * every 32-bit word into *sink (device; one atomic per wave) so that no read
+ * can be dropped. Timed by the caller, it gives the read bandwidth this
+ * device delivers to a streaming kernel: the yardstick beside the published
+ * HBM peak ([ttlab] section 1 judges decode by the fraction of the rated
+ * bandwidth it reaches).
+ *  src   device, 16-byte aligned; bytes a multiple of 16 (0: nothing to do)
+ *  sink  device uint32, 4-byte aligned; XORed into, never cleared
+ * Errors: INVALID_ARG (null pointer, misalignment, negative count), HIP. */
+int pkv_stream_read(const void *src, size_t bytes, uint32_t *sink, int32_t num_workgroups,
+                    hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

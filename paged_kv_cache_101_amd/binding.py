@@ -37,7 +37,7 @@ EXPORTS = ("pkv_status_string", "pkv_kv_bytes_per_token", "pkv_cache_tensor_byte
            "pkv_kv_append", "pkv_decode_workspace_bytes", "pkv_paged_attention_decode",
            "pkv_shared_prefix_workspace_bytes", "pkv_paged_attention_decode_shared_prefix",
            "pkv_paged_attention_prefill", "pkv_prefill_workspace_bytes", "pkv_copy_blocks",
-           "pkv_debug_gather", "pkv_paged_attention_decode_noalloc",
+           "pkv_debug_gather", "pkv_paged_attention_decode_noalloc", "pkv_stream_read",
            # host block manager (pkv_blocks.h; bound in blocks.py)
            "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_num_free_blocks", "pkv_bm_add_request",
            "pkv_bm_can_append", "pkv_bm_append", "pkv_bm_fork", "pkv_bm_free_request",
@@ -85,6 +85,8 @@ def lib():
         L.pkv_paged_attention_decode.argtypes = [vp, i32, i32, i32, vp, vp, descp, vp, i32, vp,
                                                  f32, i32, i32, vp, sz, vp, vp]
         L.pkv_paged_attention_decode.restype = ctypes.c_int
+        L.pkv_stream_read.argtypes = [vp, sz, vp, i32, vp]
+        L.pkv_stream_read.restype = ctypes.c_int
         L.pkv_paged_attention_decode_noalloc.argtypes = [vp, i32, i32, i32, vp, vp, descp, vp,
                                                          i32, vp, f32, i32, i32, vp, vp]
         L.pkv_paged_attention_decode_noalloc.restype = ctypes.c_int
@@ -429,6 +431,17 @@ def pkv_debug_gather(k_cache: torch.Tensor, v_cache: torch.Tensor, desc: pkv_cac
                                 _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
                                 S, max_ctx, _ptr(k_out), _ptr(v_out), _stream(stream))
     _check("pkv_debug_gather", rc)
+
+
+def pkv_stream_read(buf: torch.Tensor, sink: torch.Tensor, num_workgroups: int = 0,
+                    stream=None) -> None:
+    """Read every byte of buf once (a streaming-read yardstick); sink: one
+    int32 device word the reads are XORed into."""
+    _need(sink.dtype == torch.int32 and sink.numel() >= 1, "sink must be an int32 device tensor")
+    _check_device(buf, sink)
+    rc = lib().pkv_stream_read(_ptr(buf), _nbytes(buf), _ptr(sink), num_workgroups,
+                               _stream(stream))
+    _check("pkv_stream_read", rc)
 
 
 def fill_cache(k_blocks: torch.Tensor, v_blocks: torch.Tensor, desc: pkv_cache_desc,

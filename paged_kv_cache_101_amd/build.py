@@ -19,7 +19,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["pkv_api.hip", "kv_append.hip", "paged_decode.hip",
-           "paged_prefill.hip"]
+           "paged_prefill.hip", "stream_read.hip"]
 HOST_SOURCES = ["block_manager.cpp"]  # plain host C++ (g++)
 CXX = os.environ.get("CXX", "g++")
 HOST_CFLAGS = ["-O2", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", f"-I{INCLUDE}"]

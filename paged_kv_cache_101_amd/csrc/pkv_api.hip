@@ -354,6 +354,15 @@ PKV_EXPORT int pkv_debug_gather(const void* k_cache, const void* v_cache,
     return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+PKV_EXPORT int pkv_stream_read(const void* src, size_t bytes, uint32_t* sink,
+                               int32_t num_workgroups, hipStream_t stream) {
+    if (src == nullptr || sink == nullptr || num_workgroups < 0) return PKV_ERR_INVALID_ARG;
+    if (!aligned16(src) || bytes % 16 != 0 || ((uintptr_t)sink & 3u) != 0) return PKV_ERR_INVALID_ARG;
+    if (bytes == 0) return PKV_OK;
+    hipError_t err = pkv::launch_stream_read(src, bytes, sink, num_workgroups, stream);
+    return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 // ---- allocation-free decode ------------------------------------------------
 //
 // For callers that cannot allocate (code under HIP graph capture, tight

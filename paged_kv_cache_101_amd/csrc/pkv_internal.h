@@ -188,6 +188,10 @@ hipError_t launch_kv_append_fp8(const void* k, const void* v, int src_dtype,
 
 hipError_t launch_paged_decode(const DecodeArgs& a);
 
+// The streaming-read yardstick (stream_read.hip).
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int num_workgroups,
+                              hipStream_t stream);
+
 // The shared-prefix decode: the suffix pass (launch_paged_decode with res_o
 // set), then the prefix pass that merges and writes out.
 hipError_t launch_shared_prefix(const DecodeArgs& a);

@@ -99,6 +99,10 @@ class DecodeBatch:
     new_k: Optional[torch.Tensor] = None   # [T][H_kv][d]
     new_v: Optional[torch.Tensor] = None
     slot_mapping: Optional[torch.Tensor] = None  # int64 [T]
+    # fp8 caches only: the new rows before quantisation, in the query's
+    # 16-bit type, for a quantising append (new_k / new_v hold their codes)
+    new_k_rows: Optional[torch.Tensor] = None
+    new_v_rows: Optional[torch.Tensor] = None
     # prefix groups: sequences [starts[j], starts[j+1]) share their first
     # prefix[j] blocks (None: no description)
     group_starts: Optional[torch.Tensor] = None  # int32 [G + 1]
@@ -278,9 +282,13 @@ def make_batch(name: str, case_id: int, context_lens: Sequence[int], num_q_heads
         nan = FP8_NAN if kv_dtype == "fp8" else float("nan")
         k_cache.masked_fill_(poison.expand_as(k_cache), nan)
         v_cache.masked_fill_(poison.expand_as(v_cache), nan)
+    new_k_rows = new_v_rows = None
     if append_last:
         new_k = to_storage(nk, kv_dtype, k_scale)
         new_v = to_storage(nv, kv_dtype, v_scale)
+        if kv_dtype == "fp8":
+            new_k_rows = nk.to(STORAGE[q_dtype][0])
+            new_v_rows = nv.to(STORAGE[q_dtype][0])
 
     q = qx.to(STORAGE[q_dtype][0])
     starts, prefix = group_arrays(prefix_groups)
@@ -291,7 +299,8 @@ def make_batch(name: str, case_id: int, context_lens: Sequence[int], num_q_heads
         block_tables=torch.from_numpy(bt).to(device), q=q, k_cache=k_cache, v_cache=v_cache,
         scale=scale if scale is not None else 1.0 / math.sqrt(head_dim),
         k_scale=k_scale, v_scale=v_scale,
-        new_k=new_k, new_v=new_v, slot_mapping=slot_mapping,
+        new_k=new_k, new_v=new_v, slot_mapping=slot_mapping, new_k_rows=new_k_rows,
+        new_v_rows=new_v_rows,
         group_starts=(torch.tensor(starts, dtype=torch.int32, device=device)
                       if prefix_groups else None),
         group_prefix=(torch.tensor(prefix, dtype=torch.int32, device=device)
@@ -361,8 +370,10 @@ def prefix_shared(device="cpu", canary=False, num_seqs=256, prefix=2048) -> Deco
                       max_blocks=(prefix + 512 + BLOCK - 1) // BLOCK)
 
 
-def fp8_long(device="cpu", canary=False, num_seqs=16, ctx=32768) -> DecodeBatch:
+def fp8_long(device="cpu", canary=False, num_seqs=16, ctx=32768,
+             append_last=False) -> DecodeBatch:
     """16 sequences of 32768 tokens, 64 query / 8 KV heads, d 128, fp8 E4M3FN
-    KV with one scale per tensor, bf16 q/out."""
+    KV with one scale per tensor, bf16 q/out. ``append_last`` holds back each
+    sequence's last row for a quantising append of bf16 rows."""
     return make_batch("fp8-long", 5, [ctx] * num_seqs, 64, 8, 128, "fp8", "bf16", device=device,
-                      canary=canary)
+                      canary=canary, append_last=append_last)

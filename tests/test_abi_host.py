@@ -295,6 +295,16 @@ def test_noalloc_rejects_before_any_hip_call():
     assert B.pkv_decode_workspace_bytes(1024, 64, 8, 128, 1, 0, 0) <= B.PKV_NOALLOC_SCRATCH_BYTES
 
 
+def test_stream_read_rejects_bad_args():
+    L = B.lib()
+    assert L.pkv_stream_read(None, 16, FAKE, 0, None) == B.PKV_ERR_INVALID_ARG
+    assert L.pkv_stream_read(FAKE, 16, None, 0, None) == B.PKV_ERR_INVALID_ARG
+    assert L.pkv_stream_read(FAKE + 8, 16, FAKE, 0, None) == B.PKV_ERR_INVALID_ARG
+    assert L.pkv_stream_read(FAKE, 20, FAKE, 0, None) == B.PKV_ERR_INVALID_ARG
+    assert L.pkv_stream_read(FAKE, 16, FAKE, -1, None) == B.PKV_ERR_INVALID_ARG
+    assert L.pkv_stream_read(FAKE, 0, FAKE, 0, None) == B.PKV_OK
+
+
 def test_status_strings():
     for s in (0, -1, -2, -3, -4, -5, 99):
         assert B.status_string(s)
