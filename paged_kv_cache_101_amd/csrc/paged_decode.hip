@@ -124,14 +124,21 @@ __device__ __forceinline__ int worker_of(int64_t f, int64_t total, int nw) {
 // into the output rows orow..orow+G-1:
 //   M = max_j m_j,  out = sum_j 2^(m_j - M) acc_j / sum_j 2^(m_j - M) l_j.
 // With at most 64 partials (the usual case), lane j reads partial j's maxima
-// and sums once, and the accumulators of several partials are in flight at a
-// time; with more, the maxima and sums are read in passes of 64 partials and
-// one partial's accumulators are in flight at a time.
+// and sums, and in the same memory round every lane reads its accumulator
+// elements of the first KPRE partials, so a merge of up to KPRE partials
+// waits for one round trip (it runs on the launch's tail, where each round
+// trip to memory shows); later partials follow, several in flight at a time.
+// With more than 64 partials, the maxima and sums are read in passes of 64
+// partials and one partial's accumulators are in flight at a time.
 template <int QT, int D, int GM, typename SlotOf>
 __device__ __forceinline__ void merge_segment(const DecodeParams& p, int nparts, SlotOf slot_of,
                                               int G, size_t orow, int lane, bool to_result) {
     static_assert(D % kWave == 0, "head size must be a multiple of the wave width");
     constexpr int PER_LANE = GM * D / kWave;  // accumulator elements per lane
+    // partials read with the maxima: up to 16, about 128 registers of
+    // accumulators (a default launch keeps at most two waves per SIMD, so
+    // registers are not what limits it)
+    constexpr int KPRE = 128 / PER_LANE > 16 ? 16 : 128 / PER_LANE;
     float mx[GM];
     float lsum[GM], o[PER_LANE];
 #pragma unroll
@@ -140,26 +147,54 @@ __device__ __forceinline__ void merge_segment(const DecodeParams& p, int nparts,
     for (int i = 0; i < PER_LANE; ++i) o[i] = 0.f;
     if (nparts <= kWave) {
         // At most one partial per lane: its maxima and sums are read once,
-        // and the accumulators of 16 partials are in flight at a time.
+        // together with the accumulators of the first KPRE partials.
         const int j = min(lane, nparts - 1);
         const float* sl = slot_of(j);
+        float mj[GM], lj[GM];
+#pragma unroll
+        for (int h = 0; h < GM; ++h) {
+            mj[h] = lane < nparts ? coherent_load(sl + GM * D + h) : -INFINITY;
+            lj[h] = lane < nparts ? coherent_load(sl + GM * D + GM + h) : 0.f;
+        }
+        float pre[KPRE][PER_LANE];
+#pragma unroll
+        for (int k = 0; k < KPRE; ++k) {
+            if (k < nparts) {  // wave-uniform
+                const float* sk = slot_of(k);
+#pragma unroll
+                for (int i = 0; i < PER_LANE; ++i) {
+                    const int idx = i * kWave + lane;  // h * D + e
+                    pre[k][i] = idx < GM * D ? coherent_load(sk + idx) : 0.f;
+                }
+            }
+        }
         float c[GM];
 #pragma unroll
         for (int h = 0; h < GM; ++h) {
-            const float mj = lane < nparts ? coherent_load(sl + GM * D + h) : -INFINITY;
-            const float lj = lane < nparts ? coherent_load(sl + GM * D + GM + h) : 0.f;
-            mx[h] = wave_max(mj);
-            c[h] = lane < nparts ? __builtin_amdgcn_exp2f(mj - mx[h]) : 0.f;
-            lsum[h] = wave_sum(lj * c[h]);
+            mx[h] = wave_max(mj[h]);
+            c[h] = lane < nparts ? __builtin_amdgcn_exp2f(mj[h] - mx[h]) : 0.f;
+            lsum[h] = wave_sum(lj[h] * c[h]);
         }
-        // Every lane forms partial jj's weights itself from its maxima (one
-        // address for the whole wave), so the loop holds no cross-lane read
-        // and unrolls: the loads of four partials (two with 16 accumulator
-        // elements per lane, where four measured 30% slower) are in flight
-        // at a time.
+        // partial k's weights sit in lane k
+#pragma unroll
+        for (int k = 0; k < KPRE; ++k) {
+            if (k < nparts) {
+#pragma unroll
+                for (int i = 0; i < PER_LANE; ++i) {
+                    const float wk = __builtin_bit_cast(
+                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, c[(i * kWave) / D]), k));
+                    o[i] = fmaf(wk, pre[k][i], o[i]);
+                }
+            }
+        }
+        // Later partials: every lane forms partial jj's weights itself from
+        // its maxima (one address for the whole wave), so the loop holds no
+        // cross-lane read and unrolls: the loads of four partials (two with
+        // 16 accumulator elements per lane, where four measured 30% slower)
+        // are in flight at a time.
         constexpr int kMergeUnroll = PER_LANE <= 12 ? 4 : 2;
 #pragma unroll kMergeUnroll
-        for (int jj = 0; jj < nparts; ++jj) {
+        for (int jj = KPRE; jj < nparts; ++jj) {
             const float* sj = slot_of(jj);
             float wj[GM];
 #pragma unroll
@@ -283,33 +318,57 @@ void paged_decode_kernel(DecodeParams p) {
     }
 
     // Total units T and this wave's slice [a, b) of them. Units are numbered
-    // like the tiles: sequence-major, then KV head, then position.
-    int64_t total = 0;
-    for (int base = 0; base < S; base += kWave) {
-        const int s = base + lane;
-        total += wave_sum_int(s < S ? units_of(tiles_of(p.context_lens[s], pre_lane(s), max_ctx)) : 0);
+    // like the tiles: sequence-major, then KV head, then position. The
+    // lengths of the first kScanChunks * 64 sequences are read once, in one
+    // memory round, and kept in registers for the second pass.
+    constexpr int kScanChunks = 4;
+    int n_c[kScanChunks], u_c[kScanChunks];  // length and units of sequence c * 64 + lane
+#pragma unroll
+    for (int c = 0; c < kScanChunks; ++c) {
+        const int s = c * kWave + lane;
+        n_c[c] = s < S ? p.context_lens[s] : 0;
     }
-    total *= H;
+    int64_t total = 0;
+#pragma unroll
+    for (int c = 0; c < kScanChunks; ++c) {
+        const int s = c * kWave + lane;
+        u_c[c] = s < S ? units_of(tiles_of(n_c[c], pre_lane(s), max_ctx)) * H : 0;
+        if (c * kWave < S) total += wave_sum_int(u_c[c]);
+    }
+    for (int base = kScanChunks * kWave; base < S; base += kWave) {
+        const int s = base + lane;
+        total += wave_sum_int(s < S ? units_of(tiles_of(p.context_lens[s], pre_lane(s), max_ctx)) * H : 0);
+    }
     if (total == 0) return;
     const int nw = (int)min((int64_t)nw_launch, total);  // every slice non-empty
     if (w >= nw) return;
     const int64_t a = (int64_t)w * total / nw;
     const int64_t b = (int64_t)(w + 1) * total / nw;
 
-    // The sequence holding unit a, and the number of units before it.
-    int cs = 0;
+    // The sequence holding unit a, its length, and the number of units before it.
+    int cs = 0, cs_n = 0;
     int64_t seq_base = 0;
     {
         int64_t before = 0;
         for (int base = 0; base < S; base += kWave) {
             const int s = base + lane;
-            const int t = s < S ? units_of(tiles_of(p.context_lens[s], pre_lane(s), max_ctx)) * H : 0;
-            const int incl = wave_inclusive_scan(t, lane);
+            const int ci = base / kWave;
+            int n = 0, t = 0;
+            if (ci < kScanChunks) {
+#pragma unroll
+                for (int c = 0; c < kScanChunks; ++c)
+                    if (c == ci) n = n_c[c], t = u_c[c];
+            } else if (s < S) {
+                n = p.context_lens[s];
+                t = units_of(tiles_of(n, pre_lane(s), max_ctx)) * H;
+            }
+            const int incl = wave_inclusive_scan(t);
             const int64_t lo = before + incl - t;
             const unsigned long long hit = __ballot(t > 0 && lo <= a && a < before + incl);
             if (hit) {
                 const int L = __ffsll(hit) - 1;
                 cs = base + L;
+                cs_n = __builtin_amdgcn_readlane(n, L);
                 seq_base = before + __builtin_amdgcn_readlane(incl - t, L);
                 break;
             }
@@ -368,7 +427,7 @@ void paged_decode_kernel(DecodeParams p) {
     Cursor cc;  // the tile being computed
     cc.s = cs;
     cc.pre = pre_uniform(cs);
-    cc.n = uniform_read(p.context_lens, cs);
+    cc.n = cs_n;
     cc.nb = tiles_of(cc.n, cc.pre, max_ctx);
     cc.n -= cc.pre * kBlock;
     if (cc.nb == 0) return;  // cannot happen: unit a lies in a non-empty sequence

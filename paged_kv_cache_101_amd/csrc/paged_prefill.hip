@@ -41,6 +41,8 @@
 // decode (see the end of this file): a prefix group's member sequences take
 // the place of a chunk's tokens, every row sees every key of its part of the
 // shared prefix, and the result is merged with the suffix pass's.
+#include <mutex>
+
 #include "pkv_internal.h"
 #include "pkv_tile.h"
 
@@ -115,6 +117,11 @@ struct PrefillParams {
     float* slots;                 // [kPrefixSlots][prefix_slot_floats(D)]
     const float* res_o;           // suffix results [S][H_q][D] and [S][H_q]
     const float* res_lse;
+    // prefix pass running beside the suffix pass: every group's partials go
+    // to slots (none is merged with the suffix results here), and the chunk
+    // count aims at pf_target workgroups (0: kPrefixTargetWorkgroups)
+    int all_slots;
+    int pf_target;
 };
 
 // Row tiles of kGroupRows rows of a sequence (0 for an invalid chunk).
@@ -188,10 +195,10 @@ __device__ __forceinline__ void prefill_seq_shape(const PrefillParams& p, int s,
 // and rb_total row blocks of 16 (per KV head): about kPrefixTargetWorkgroups
 // workgroups, and the chunked rows' 16-row partials within kPrefixSlots. The
 // attention kernel and the merge launch derive it the same way.
-__device__ __forceinline__ int prefix_chunks(int H, int rt_total, int rb_total) {
+__device__ __forceinline__ int prefix_chunks(int H, int rt_total, int rb_total, int target) {
+    if (target <= 0) target = kPrefixTargetWorkgroups;
     const int per_chunk = H * rt_total;
-    const int cg = per_chunk >= kPrefixTargetWorkgroups
-                       ? 1 : (kPrefixTargetWorkgroups + per_chunk - 1) / per_chunk;
+    const int cg = per_chunk >= target ? 1 : (target + per_chunk - 1) / per_chunk;
     return min(cg, max(1, kPrefixSlots / (H * rb_total)));
 }
 
@@ -255,7 +262,7 @@ void paged_prefill_kernel(PrefillParams p) {
             rt_total += wave_sum_int((rows + kGroupRows - 1) / kGroupRows);
         }
         if (rt_total == 0) return;
-        const int cg = prefix_chunks(H, rt_total, rb_total);
+        const int cg = prefix_chunks(H, rt_total, rb_total, p.pf_target);
         // the group holding this workgroup (wave-uniform)
         const int task = blockIdx.x;
         int wg_before = 0;
@@ -267,8 +274,8 @@ void paged_prefill_kernel(PrefillParams p) {
             const int cj = j < ng ? min(p.group_prefix[j], cg) : 0;
             const int rts = (rows + kGroupRows - 1) / kGroupRows, rbs = (rows + 15) / 16;
             const int wgs = H * rts * cj;
-            const int incl = wave_inclusive_scan(wgs, lane);
-            const int tincl = wave_inclusive_scan(H * rbs * cj, lane);
+            const int incl = wave_inclusive_scan(wgs);
+            const int tincl = wave_inclusive_scan(H * rbs * cj);
             const unsigned long long hit =
                 __ballot(wgs > 0 && wg_before + incl - wgs <= task && task < wg_before + incl);
             if (hit) {
@@ -307,7 +314,7 @@ void paged_prefill_kernel(PrefillParams p) {
                 rt_total += wave_sum_int(rts);
                 rb_total += wave_sum_int(rbs);
             }
-            if (rt_total > 0) cg = prefix_chunks(H, rt_total, rb_total);
+            if (rt_total > 0) cg = prefix_chunks(H, rt_total, rb_total, p.pf_target);
         }
         const int task = blockIdx.x;
         int s = -1, local = 0;
@@ -319,8 +326,8 @@ void paged_prefill_kernel(PrefillParams p) {
             if (ss < S) prefill_seq_shape(p, ss, rts, rbs, tmin);
             const int cs = min(cg, max(tmin, 1));
             const int cnt = rts * H * cs;
-            const int incl = wave_inclusive_scan(cnt, lane);
-            const int tincl = wave_inclusive_scan(H * rbs * cs, lane);
+            const int incl = wave_inclusive_scan(cnt);
+            const int tincl = wave_inclusive_scan(H * rbs * cs);
             const unsigned long long hit = __ballot(cnt > 0 && before + incl - cnt <= task &&
                                                     task < before + incl);
             if (hit) {
@@ -835,9 +842,10 @@ void paged_prefill_kernel(PrefillParams p) {
         lt += lane_fetch(x32, lt);  // weight sum of row t (over this chunk of keys)
         const int row = r0 + t;
         const size_t orow = (size_t)(q0 + min(row, nrows - 1) / G) * Hq + g * G + min(row, nrows - 1) % G;
-        if (pf_chunks > 1) {
-            // one chunk of several: the partial goes to its 16-row slot and
-            // the merge launch that follows combines the chunks
+        if (pf_chunks > 1 || (PFX && p.all_slots)) {
+            // one chunk of several (or a prefix pass running beside the
+            // suffix pass): the partial goes to its 16-row slot and the
+            // merge launch that follows combines the chunks
             const int64_t f = pf_task16 + (int64_t)(r0 / 16) * (H * pf_chunks) + g * pf_chunks + pf_chunk;
             float* slotp = p.slots + (size_t)f * SLOT;
 #pragma unroll
@@ -925,8 +933,9 @@ __global__ __launch_bounds__(kMergeThreads) void chunk_merge_kernel(PrefillParam
         rb_total += wave_sum_int(rbs);
     }
     if (rt_total == 0) return;
-    const int cg = prefix_chunks(H, rt_total, rb_total);
-    if (cg == 1) return;  // nothing was split: the attention kernel wrote every row
+    const int cg = prefix_chunks(H, rt_total, rb_total, p.pf_target);
+    const bool all_slots = PFX && p.all_slots;  // every group left slots
+    if (cg == 1 && !all_slots) return;  // nothing was split: the attention kernel wrote every row
     const int g = blockIdx.x % H;
     const int rbg = blockIdx.x / H;  // 16-row block over all units
     if (rbg >= rb_total) return;
@@ -938,8 +947,8 @@ __global__ __launch_bounds__(kMergeThreads) void chunk_merge_kernel(PrefillParam
         int rows = 0, rts = 0, rbs = 0, cmax = 0;
         if (j < nu) shape(j, rows, rts, rbs, cmax);
         const int cj = min(cmax, cg);
-        const int rincl = wave_inclusive_scan(rbs, lane);
-        const int tincl = wave_inclusive_scan(H * rbs * cj, lane);
+        const int rincl = wave_inclusive_scan(rbs);
+        const int tincl = wave_inclusive_scan(H * rbs * cj);
         const unsigned long long hit =
             __ballot(rbs > 0 && rb_before + rincl - rbs <= rbg && rbg < rb_before + rincl);
         if (hit) {
@@ -954,7 +963,7 @@ __global__ __launch_bounds__(kMergeThreads) void chunk_merge_kernel(PrefillParam
         t16_before += __builtin_amdgcn_readlane(tincl, kWave - 1);
     }
     if (jj < 0) return;  // not reached for rbg < rb_total
-    if (C <= 1) return;  // merged by the attention kernel
+    if (C <= 1 && !all_slots) return;  // merged by the attention kernel
     const int r = threadIdx.x >> 4, e0 = (threadIdx.x & 15) * EPT;
     const int row = rb16 * 16 + r;
     if (row >= nrows) return;
@@ -1075,8 +1084,13 @@ hipError_t launch_paged_prefill(const PrefillArgs& a) {
 // chunk partials (16-row slots) are merged by a third launch, by the
 // log-sum-exp rule, together with the suffix result.
 
+// Beside the suffix pass, the prefix pass aims at fewer workgroups (its work
+// hides under the suffix pass's stream, and fewer chunks leave fewer partials
+// for the merge launch to read).
+constexpr int kPrefixBesideTarget = 256;
+
 template <int KT, int QT, int D>
-static hipError_t launch_prefix_typed(const DecodeArgs& a) {
+static hipError_t launch_prefix_typed(const DecodeArgs& a, bool beside, hipStream_t stream) {
     PrefillParams p{};
     p.q = static_cast<const uint8_t*>(a.q);
     p.k_cache = static_cast<const uint8_t*>(a.k_cache);
@@ -1097,11 +1111,32 @@ static hipError_t launch_prefix_typed(const DecodeArgs& a) {
     p.slots = a.prefix_slots;
     p.res_o = a.res_o;
     p.res_lse = a.res_lse;
+    p.all_slots = beside ? 1 : 0;
+    p.pf_target = beside ? kPrefixBesideTarget : kPrefixTargetWorkgroups;
     const int64_t grid = prefix_workgroup_bound(a.num_seqs, a.group, a.num_kv_heads, a.num_groups);
     auto kernel = paged_prefill_kernel<KT, QT, D, true>;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kPrefillThreads), 0, a.stream, p);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kPrefillThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int QT, int D>
+static hipError_t launch_prefix_merge(const DecodeArgs& a, bool beside) {
+    PrefillParams p{};
+    p.num_seqs = a.num_seqs;
+    p.num_q_heads = a.num_q_heads;
+    p.num_kv_heads = a.num_kv_heads;
+    p.group = a.group;
+    p.max_blocks_per_seq = a.max_blocks_per_seq;
+    p.v_scale = a.kv_dtype == PKV_FP8_E4M3 ? a.v_scale : 1.f;
+    p.out = a.out;
+    p.num_groups = a.num_groups;
+    p.group_starts = a.group_starts;
+    p.group_prefix = a.group_prefix;
+    p.slots = a.prefix_slots;
+    p.res_o = a.res_o;
+    p.res_lse = a.res_lse;
+    p.all_slots = beside ? 1 : 0;
+    p.pf_target = beside ? kPrefixBesideTarget : kPrefixTargetWorkgroups;
     const int64_t merge_grid =
         (int64_t)a.num_kv_heads * prefix_row_blocks_bound(a.num_seqs, a.group, a.num_groups);
     auto merge = chunk_merge_kernel<QT, D, true>;
@@ -1110,19 +1145,81 @@ static hipError_t launch_prefix_typed(const DecodeArgs& a) {
 }
 
 template <int KT, int QT>
-static hipError_t launch_prefix_dim(const DecodeArgs& a) {
-    return a.head_dim == 64 ? launch_prefix_typed<KT, QT, 64>(a) : launch_prefix_typed<KT, QT, 128>(a);
+static hipError_t launch_prefix_pass(const DecodeArgs& a, bool beside, hipStream_t stream) {
+    return a.head_dim == 64 ? launch_prefix_typed<KT, QT, 64>(a, beside, stream)
+                            : launch_prefix_typed<KT, QT, 128>(a, beside, stream);
 }
 
+static hipError_t prefix_pass(const DecodeArgs& a, bool beside, hipStream_t stream) {
+    if (a.kv_dtype == PKV_F32) return launch_prefix_pass<PKV_F32, PKV_F32>(a, beside, stream);
+    if (a.kv_dtype == PKV_F16) return launch_prefix_pass<PKV_F16, PKV_F16>(a, beside, stream);
+    if (a.kv_dtype == PKV_BF16) return launch_prefix_pass<PKV_BF16, PKV_BF16>(a, beside, stream);
+    if (a.q_dtype == PKV_F16) return launch_prefix_pass<PKV_FP8_E4M3, PKV_F16>(a, beside, stream);
+    return launch_prefix_pass<PKV_FP8_E4M3, PKV_BF16>(a, beside, stream);
+}
+
+static hipError_t prefix_merge(const DecodeArgs& a, bool beside) {
+    const int q = a.kv_dtype == PKV_FP8_E4M3 ? a.q_dtype : a.kv_dtype;
+    const bool d64 = a.head_dim == 64;
+    if (q == PKV_F32) return d64 ? launch_prefix_merge<PKV_F32, 64>(a, beside) : launch_prefix_merge<PKV_F32, 128>(a, beside);
+    if (q == PKV_F16) return d64 ? launch_prefix_merge<PKV_F16, 64>(a, beside) : launch_prefix_merge<PKV_F16, 128>(a, beside);
+    return d64 ? launch_prefix_merge<PKV_BF16, 64>(a, beside) : launch_prefix_merge<PKV_BF16, 128>(a, beside);
+}
+
+// A second stream per device on which the prefix pass runs beside the suffix
+// pass, with the events that fork it from and join it back to the caller's
+// stream (created on the first call on the device; default priority). Each
+// call records, waits and launches under the device's lock, so calls from
+// several host threads cannot interleave their fork and join.
+struct SideStream {
+    std::mutex mu;
+    bool tried = false;
+    bool ok = false;
+    hipStream_t stream = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxSideDevices = 64;
+static SideStream g_side[kMaxSideDevices];
+
 hipError_t launch_shared_prefix(const DecodeArgs& a) {
-    // the suffix pass (decode kernel, result mode), then the prefix pass
+    // The prefix pass can run beside the suffix pass when it needs none of
+    // the suffix results, i.e. when every 16-row block of every group can
+    // leave its partial in a slot for the merge launch.
+    const bool fits = (int64_t)a.num_kv_heads *
+                          prefix_row_blocks_bound(a.num_seqs, a.group, a.num_groups) <=
+                      kPrefixSlots;
+    int dev = -1;
+    SideStream* side = nullptr;
+    if (fits && hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxSideDevices)
+        side = &g_side[dev];
+    if (side != nullptr) {
+        std::lock_guard<std::mutex> lock(side->mu);
+        if (!side->tried) {
+            side->tried = true;
+            side->ok = hipStreamCreateWithFlags(&side->stream, hipStreamNonBlocking) == hipSuccess &&
+                       hipEventCreateWithFlags(&side->fork, hipEventDisableTiming) == hipSuccess &&
+                       hipEventCreateWithFlags(&side->join, hipEventDisableTiming) == hipSuccess;
+        }
+        if (side->ok) {
+            // fork: the side stream starts after the caller's earlier work
+            hipError_t err = hipEventRecord(side->fork, a.stream);
+            if (err == hipSuccess) err = hipStreamWaitEvent(side->stream, side->fork, 0);
+            if (err == hipSuccess) err = prefix_pass(a, true, side->stream);
+            if (err == hipSuccess) err = hipEventRecord(side->join, side->stream);
+            // the suffix pass on the caller's stream, meanwhile
+            if (err == hipSuccess) err = launch_paged_decode(a);
+            // join, then merge both passes' results
+            if (err == hipSuccess) err = hipStreamWaitEvent(a.stream, side->join, 0);
+            if (err == hipSuccess) err = prefix_merge(a, true);
+            return err;
+        }
+    }
+    // one stream: the suffix pass, then the prefix pass (which merges
+    // one-chunk groups with the suffix results itself), then the merge
     hipError_t err = launch_paged_decode(a);
-    if (err != hipSuccess) return err;
-    if (a.kv_dtype == PKV_F32) return launch_prefix_dim<PKV_F32, PKV_F32>(a);
-    if (a.kv_dtype == PKV_F16) return launch_prefix_dim<PKV_F16, PKV_F16>(a);
-    if (a.kv_dtype == PKV_BF16) return launch_prefix_dim<PKV_BF16, PKV_BF16>(a);
-    if (a.q_dtype == PKV_F16) return launch_prefix_dim<PKV_FP8_E4M3, PKV_F16>(a);
-    return launch_prefix_dim<PKV_FP8_E4M3, PKV_BF16>(a);
+    if (err == hipSuccess) err = prefix_pass(a, false, a.stream);
+    if (err == hipSuccess) err = prefix_merge(a, false);
+    return err;
 }
 
 }  // namespace pkv

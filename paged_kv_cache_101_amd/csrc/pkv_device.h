@@ -114,11 +114,19 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
+// The four 16-lane rows' results (every lane of a row holding its row's),
+// combined into one wave-uniform value: lanes 0, 16, 32 and 48 are read into
+// scalar registers rather than exchanged through the LDS crossbar.
+template <typename Op>
+__device__ __forceinline__ float combine_rows(float v, Op op) {
+    auto rd = [&](int l) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+    };
+    return op(op(rd(0), rd(16)), op(rd(32), rd(48)));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-    v = group_sum<16>(v);
-    v += __shfl_xor(v, 16, kWave);
-    v += __shfl_xor(v, 32, kWave);
-    return v;
+    return combine_rows(group_sum<16>(v), [](float x, float y) { return x + y; });
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -126,9 +134,7 @@ __device__ __forceinline__ float wave_max(float v) {
     v = fmaxf(v, dpp<kDppQuadXor2>(v));
     v = fmaxf(v, dpp<kDppRowHalfMirror>(v));
     v = fmaxf(v, dpp<kDppRowMirror>(v));
-    v = fmaxf(v, __shfl_xor(v, 16, kWave));
-    v = fmaxf(v, __shfl_xor(v, 32, kWave));
-    return v;
+    return combine_rows(v, [](float x, float y) { return fmaxf(x, y); });
 }
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }

@@ -283,19 +283,37 @@ __device__ __forceinline__ float lane_fetch(int addr, float v) {
 // refill in other registers and copy it back at the loop latch).
 __device__ __forceinline__ void settle(f32x4_t& v) { asm volatile("" : "+v"(v) : : "memory"); }
 
-// Sum over the wave, returned as a wave-uniform (scalar) value.
+// Integer DPP move of v within 16-lane rows (rows outside ROW_MASK, and
+// lanes whose source lies outside their row, read 0).
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_int(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+}
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142;  // lane 15 of each row into the next row
+constexpr int kDppRowBcast31 = 0x143;  // lane 31 into rows 2 and 3
+
+// Sum over the wave, returned as a wave-uniform (scalar) value: a DPP sum
+// within each 16-lane row, then the four rows' sums read into scalars.
 __device__ __forceinline__ int wave_sum_int(int v) {
-#pragma unroll
-    for (int sh = 1; sh < kWave; sh <<= 1) v += __shfl_xor(v, sh, kWave);
-    return __builtin_amdgcn_readfirstlane(v);
+    v += dpp_int<kDppQuadXor1>(v);
+    v += dpp_int<kDppQuadXor2>(v);
+    v += dpp_int<kDppRowHalfMirror>(v);
+    v += dpp_int<kDppRowMirror>(v);
+    return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+           (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
 }
 
-__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int u = __shfl_up(v, d, kWave);
-        if (lane >= d) v += u;
-    }
+// Inclusive prefix sum over the lanes: shifts by 1, 2, 4 and 8 inside each
+// 16-lane row, then lane 15's sum into row 1 (and lane 47's into row 3) and
+// lane 31's into rows 2 and 3. (Checked on the GPU against a host scan.)
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+    v += dpp_int<kDppRowShr1>(v);
+    v += dpp_int<kDppRowShr2>(v);
+    v += dpp_int<kDppRowShr4>(v);
+    v += dpp_int<kDppRowShr8>(v);
+    v += dpp_int<kDppRowBcast15, 0xA>(v);
+    v += dpp_int<kDppRowBcast31, 0xC>(v);
     return v;
 }
 
