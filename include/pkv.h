@@ -20,10 +20,11 @@
  *  - Every function returns an int status: PKV_OK or a negative PKV_ERR_*.
  *    pkv_status_string() names it.
  *  - All buffers are caller-owned, contiguous, row-major device memory
- *    unless a parameter says "host". The library allocates nothing and keeps
- *    no state between calls beyond constants of the device it reads once (the
- *    compute-unit count per device, each decode kernel's occupancy), and is
- *    safe to call from several host threads.
+ *    unless a parameter says "host". The library allocates no memory and
+ *    keeps no state between calls beyond what it sets up once per device
+ *    (the compute-unit count, each decode kernel's occupancy, and for the
+ *    shared-prefix decode a second stream with two events), and is safe to
+ *    call from several host threads.
  *  - Work is enqueued on the given HIP stream (NULL = the null stream) and
  *    never synchronised: results are visible after the stream reaches the
  *    point of the call. No call issues a memset, a copy or a host
@@ -313,15 +314,21 @@ size_t pkv_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  * outside [0, max_blocks_per_seq], it is ignored and every sequence is
  * decoded plainly (still the same result).
  *
- * How: three launches on the stream. The suffix pass is the decode kernel
- * over each member's blocks after its group's prefix; it leaves the members'
- * rows as float32 (normalised output, log2-sum-exp) in the workspace. The
- * prefix pass stacks the (member, query head) rows of a group 128 to a
- * workgroup against the shared tiles, read once per workgroup through LDS,
- * and splits the prefix into chunks when there are few rows. A group with
- * one chunk is merged with its suffix results at once; otherwise the chunk
- * partials go to the workspace and the merge launch combines them with the
- * suffix results by the log-sum-exp rule into out.
+ * How: three launches. The suffix pass is the decode kernel over each
+ * member's blocks after its group's prefix; it leaves the members' rows as
+ * float32 (normalised output, log2-sum-exp) in the workspace. The prefix
+ * pass stacks the (member, query head) rows of a group 128 to a workgroup
+ * against the shared tiles, read once per workgroup through LDS, and splits
+ * the prefix into chunks when there are few rows. When every 16-row block of
+ * the batch can hold a partial slot (num_kv_heads * (ceil(num_seqs * G / 16)
+ * + num_groups) <= 4096), the prefix pass leaves all its partials in the
+ * workspace and runs beside the suffix pass: on a second stream the library
+ * keeps per device (default priority, created on the first such call),
+ * forked from and joined back to `stream` with events, which a graph capture
+ * of `stream` records as well. Otherwise it runs after the suffix pass on
+ * `stream`, merging one-chunk groups with their suffix results itself. The
+ * merge launch on `stream` then combines the chunk partials with the suffix
+ * results by the log-sum-exp rule into out.
  *
  *  num_groups   0..num_seqs (0: plain decode; the arrays may then be NULL)
  *  workspace    at least pkv_shared_prefix_workspace_bytes(...) bytes,
