@@ -23,6 +23,29 @@ SOURCES = ["pkv_api.hip", "kv_append.hip", "paged_decode.hip",
 HOST_SOURCES = ["block_manager.cpp"]  # plain host C++ (g++)
 CXX = os.environ.get("CXX", "g++")
 HOST_CFLAGS = ["-O2", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", f"-I{INCLUDE}"]
+# PKV_SANITIZE=1: the host C++ (the block manager) is built with gcc's
+# AddressSanitizer and UndefinedBehaviorSanitizer, and the library links their
+# runtimes; the device code is unchanged. Load it in a process that preloads
+# the runtimes (see sanitizer_env()); rebuild without the variable before any
+# GPU run.
+SANITIZE = os.environ.get("PKV_SANITIZE", "") == "1"
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+             "-fno-omit-frame-pointer", "-g"]
+
+
+def sanitizer_runtimes():
+    """gcc's ASan and UBSan runtime libraries (paths)."""
+    return [subprocess.run([CXX, f"-print-file-name={n}"], capture_output=True, text=True,
+                           check=True).stdout.strip() for n in ("libasan.so", "libubsan.so")]
+
+
+def sanitizer_env() -> dict:
+    """Environment for a Python process that loads sanitized builds."""
+    env = dict(os.environ)
+    env["LD_PRELOAD"] = ":".join(sanitizer_runtimes())
+    env["ASAN_OPTIONS"] = "detect_leaks=0:abort_on_error=1"
+    env["UBSAN_OPTIONS"] = "print_stacktrace=1:halt_on_error=1"
+    return env
 
 CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-fvisibility=hidden",
@@ -51,7 +74,8 @@ def _compile(src: str, verbose: bool) -> str:
 
 def _compile_host(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [CXX, *HOST_CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [CXX, *HOST_CFLAGS, *(SAN_FLAGS if SANITIZE else []), "-c", os.path.join(CSRC, src),
+           "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -70,6 +94,8 @@ def build(verbose: bool = False) -> str:
         objs = [j.result() for j in jobs]
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
+    if SANITIZE:
+        cmd += sanitizer_runtimes()  # the instrumented host objects need them
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
@@ -77,5 +103,24 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def sanitized_cpu_tests() -> int:
+    """Build libpkv.so and the oracle with the sanitizers, run the CPU test
+    suite (pytest -m "not gpu") in a process that preloads their runtimes,
+    then rebuild both without them. Returns pytest's exit status."""
+    env = dict(os.environ, PKV_SANITIZE="1")
+    for mod in ("paged_kv_cache_101_amd.build", "oracle.build"):
+        subprocess.run([sys.executable, "-c", f"import {mod} as b; b.build()"], cwd=ROOT, env=env,
+                       check=True)
+    rc = subprocess.run([sys.executable, "-m", "pytest", "tests", "-m", "not gpu", "-q",
+                         "-p", "no:cacheprovider"], cwd=ROOT, env=sanitizer_env()).returncode
+    for mod in ("paged_kv_cache_101_amd.build", "oracle.build"):
+        subprocess.run([sys.executable, "-c", f"import {mod} as b; b.build()"], cwd=ROOT,
+                       env={k: v for k, v in os.environ.items() if k != "PKV_SANITIZE"},
+                       check=True)
+    return rc
+
+
 if __name__ == "__main__":
+    if "--sanitized-cpu-tests" in sys.argv:
+        sys.exit(sanitized_cpu_tests())
     print(build(verbose="-v" in sys.argv))
