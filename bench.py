@@ -107,11 +107,12 @@ def parse():
 
 
 def kernel_hash() -> str:
-    """Hash of the decode kernel sources: counter figures are valid only for
-    the build they were taken on."""
+    """Hash of the attention kernel sources (decode, and the prefix pass of
+    the shared-prefix call): counter figures are valid only for the build
+    they were taken on."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("paged_decode.hip", "pkv_tile.h", "pkv_device.h"):
+    for f in ("paged_decode.hip", "paged_prefill.hip", "pkv_tile.h", "pkv_device.h"):
         with open(os.path.join(ROOT, "paged_kv_cache_101_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
