@@ -556,7 +556,8 @@ def summary(workload: str, dev, steps: int, warmup: int, partition_sizes=(0,),
                "frac": round(nb / (t["decode_avg_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                "step_us": round(t["ms_per_step"] * 1e3, 2),
                "decode_seqs_per_s": round(b0.num_seqs / (t["ms_per_step"] * 1e-3), 1),
-               "kv_bytes_per_launch": nb}
+               "kv_bytes_per_launch": nb,
+               "traffic": load_traffic(workload if P == 0 else f"{workload}_p{P}")}
         if "append_avg_ms" in t:
             rec["append_avg_us"] = round(t["append_avg_ms"] * 1e3, 2)
         if cold:
