@@ -451,6 +451,13 @@ void paged_prefill_kernel(PrefillParams p) {
     bool pc_b[kWavePieces], pc_v[kWavePieces];
     bool pc_ok[kWavePieces];  // the wave carries piece i (the last may be absent)
     const int my_pieces = (kStepPieces - wv + kPrefillWaves - 1) / kPrefillWaves;
+    // When a tile's K (and its V) splits into a multiple of four pieces, every
+    // wave carries the same roles in the same order (piece i of the wave:
+    // tile (4 i) / kPieces, K or V by (4 i) % kPieces), known at compile
+    // time, so issuing a step selects no resource at run time.
+    constexpr bool kFixedRoles = kPieces % (2 * kPrefillWaves) == 0;
+    auto fixed_b = [](int i) { return (kPrefillWaves * i) / kPieces == 1; };
+    auto fixed_v = [](int i) { return (kPrefillWaves * i) % kPieces >= kPieces / 2; };
 #pragma unroll
     for (int i = 0; i < kWavePieces; ++i) {
         const int c2 = min(wv + i * kPrefillWaves, kStepPieces - 1);
@@ -484,22 +491,40 @@ void paged_prefill_kernel(PrefillParams p) {
         }
         return id;
     };
+    // Byte offset of tile (block id, KV head g): the product (id * H + g)
+    // fits 32 bits (num_blocks * H < 2^31); the byte offset may not.
+    auto tile_bytes_at = [&](int id) -> size_t {
+        return (size_t)(uint32_t)(id * H + g) * kTileBytes;
+    };
     auto issue = [&](int sp, int ia, int ib) {
         const uint32_t st = (uint32_t)(sp % kRing) * kStepBytes;
-        const size_t off_a = tile_elem_offset(checked(ia), g, H, D) * KB;
-        const size_t off_b = tile_elem_offset(checked(ib), g, H, D) * KB;
+        const size_t off_a = tile_bytes_at(checked(ia));
+        const size_t off_b = tile_bytes_at(checked(ib));
         const __amdgpu_buffer_rsrc_t rka = make_rsrc(p.k_cache + off_a, kTileBytes);
         const __amdgpu_buffer_rsrc_t rva = make_rsrc(p.v_cache + off_a, kTileBytes);
         const __amdgpu_buffer_rsrc_t rkb = make_rsrc(p.k_cache + off_b, kTileBytes);
         const __amdgpu_buffer_rsrc_t rvb = make_rsrc(p.v_cache + off_b, kTileBytes);
 #pragma unroll
-        for (int i = 0; i < kWavePieces; ++i)
-            if (pc_ok[i])
+        for (int i = 0; i < kWavePieces; ++i) {
+            if constexpr (kFixedRoles) {
+                load_to_lds(fixed_v(i) ? (fixed_b(i) ? rvb : rva) : (fixed_b(i) ? rkb : rka),
+                            pc_src[i], lds + st + pc_dst[i]);
+            } else if (pc_ok[i]) {
                 load_to_lds(pc_v[i] ? (pc_b[i] ? rvb : rva) : (pc_b[i] ? rkb : rka), pc_src[i],
                             lds + st + pc_dst[i]);
+            }
+        }
     };
     // wait until at most `later` steps' loads of this wave are in flight
-    auto wait_steps = [&](int later) { wait_vmcnt(later * my_pieces); };
+    auto wait_steps = [&](int later) {
+        if constexpr (kFixedRoles) {
+            // the steady state (kRing - 3 steps still in flight) as one immediate
+            if (later == kRing - 3) __builtin_amdgcn_s_waitcnt(vmcnt_wait((kRing - 3) * kWavePieces));
+            else wait_vmcnt(later * kWavePieces);
+        } else {
+            wait_vmcnt(later * my_pieces);
+        }
+    };
 
     const uint32_t k_off = (uint32_t)((g4 * kBlock + t) * 8 * KB);
     const uint32_t v_off = (uint32_t)((t * 4 + g4) * 8 * KB);
