@@ -42,6 +42,7 @@
 // the place of a chunk's tokens, every row sees every key of its part of the
 // shared prefix, and the result is merged with the suffix pass's.
 #include <mutex>
+#include <type_traits>
 
 #include "pkv_internal.h"
 #include "pkv_tile.h"
@@ -65,9 +66,18 @@ constexpr int vmcnt_wait(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 // byte voff of the buffer, land at lds_base + l * 16 (lds_base is the same
 // for the whole wave). The address is a uniform resource plus a 32-bit lane
 // offset, so no 64-bit per-lane address is kept.
-__device__ __forceinline__ void load_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint8_t* lds_base) {
+__device__ __forceinline__ void load_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint8_t* lds_base,
+                                            uint32_t soff = 0) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16,
-                                             voff, 0, 0, 0);
+                                             voff, (int)soff, 0, 0);
+}
+
+// Eight consecutive block-table entries, read as one scalar load (a
+// wave-uniform address; the loads of the scalar unit need only 4-byte
+// alignment).
+typedef int32_t i32x8_t __attribute__((ext_vector_type(8), aligned(4)));
+__device__ __forceinline__ i32x8_t uniform_read8(const int32_t* p) {
+    return *(const __attribute__((address_space(4))) i32x8_t*)p;
 }
 
 // Wait until at most n (0..16, wave-uniform; larger n waits for 16) of this
@@ -122,6 +132,9 @@ struct PrefillParams {
     // count aims at pf_target workgroups (0: kPrefixTargetWorkgroups)
     int all_slots;
     int pf_target;
+    // every tile's byte offset in the K and V caches fits 32 bits
+    // (num_blocks * num_kv_heads * tile bytes < 2^32)
+    int offsets32;
 };
 
 // Row tiles of kGroupRows rows of a sequence (0 for an invalid chunk).
@@ -138,6 +151,15 @@ __device__ __forceinline__ int row_tiles(const PrefillParams& p, int s) {
 template <int KT, int D>
 constexpr int ring_depth() {
     return 4 * kBlock * D * Elem<KT>::bytes <= 16384 ? 4 : 3;
+}
+
+// Waves per SIMD the attention kernel aims at: two workgroups of four waves
+// share a CU when two rings fit its 160 KiB of LDS (every 16-bit and fp8
+// shape, and float32 at d = 64); float32 at d = 128 (three 32 KiB stages)
+// runs one workgroup per CU and may use every register.
+template <int KT, int D>
+constexpr int prefill_waves_per_simd() {
+    return 2 * ring_depth<KT, D>() * 4 * kBlock * D * Elem<KT>::bytes <= 160 * 1024 ? 2 : 1;
 }
 
 // The 16-bit compute type of a query type (f32 queries never use it).
@@ -210,7 +232,7 @@ __device__ __forceinline__ int prefix_chunks(int H, int rt_total, int rb_total, 
 // workgroup, every row seeing every key of the chunk, the partial merged with
 // the suffix results.
 template <int KT, int QT, int D, bool PFX>
-__global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(prefill_waves_per_simd<KT, D>())))
 void paged_prefill_kernel(PrefillParams p) {
     using TM = TileMath<KT, QT, D>;
     constexpr int NK = TM::NK, NV = TM::NV, NVL = TM::NVL, KW = TM::KW, VLW = TM::VLW;
@@ -480,7 +502,7 @@ void paged_prefill_kernel(PrefillParams p) {
         ib = 2 * sp + 1 < tiles ? uniform_read(p.block_tables, bt_row + tile0 + 2 * sp + 1) : 0;
     };
     auto checked = [&](int id) -> int {
-        if (id < 0 || id >= p.num_blocks) {
+        if ((uint32_t)id >= (uint32_t)p.num_blocks) {  // negative ids too
             bad = true;  // its rows become NaN; the null block is read instead
             return 0;
         }
@@ -707,59 +729,114 @@ void paged_prefill_kernel(PrefillParams p) {
         }
     };
 
-    int nia = 0, nib = 0;  // blocks of the next step to issue
+    // ---- the steady steps ----
+    // Most steps need no causal select, no mask and no end-of-chunk check.
+    // For 16-bit 128-wide tiles (four ring stages, every wave carrying the
+    // same pieces) over caches whose tile offsets fit 32 bits, they run in
+    // groups of four with the ring stages fixed at compile time, the block
+    // ids of four steps read by one scalar load, and every tile addressed
+    // through one K and one V resource plus a 32-bit offset: a handful of
+    // scalar instructions per step instead of the general step's checks,
+    // look-ups and resource set-up. The block ids of the workgroup's chunk
+    // are checked once, here (any id out of range: the general steps, which
+    // flag the rows, take the whole chunk).
+    constexpr bool kQuadShape = kDirectV && kFixedRoles && kRing == 4;
+    int quads = 0;  // groups of four steady steps, from step 0
+    if constexpr (kQuadShape) {
+        if (p.offsets32) {
+            bool ids_ok = true;
+            for (int b0 = 0; b0 < tiles && ids_ok; b0 += kWave) {
+                const int i = b0 + lane;
+                const int id = i < tiles ? p.block_tables[bt_row + tile0 + i] : 0;
+                ids_ok = !__any((uint32_t)id >= (uint32_t)p.num_blocks);
+            }
+            int min_sel = INT32_MAX;
+#pragma unroll
+            for (int rb = 0; rb < kRowBlocks; ++rb) min_sel = min(min_sel, sel_from[rb]);
+            // step sp needs no select while 32 sp + 31 <= min_sel, and the
+            // step it issues (sp + 3) has both tiles while sp + 3 <= steps - 2
+            const int sel_end = min_sel < 2 * kBlock - 1 ? 0 : (min_sel - (2 * kBlock - 1)) / (2 * kBlock) + 1;
+            if (ids_ok) quads = max(0, min(sel_end, steps - kRing)) / 4;
+        }
+    }
+    const __amdgpu_buffer_rsrc_t rk_all = make_rsrc(p.k_cache, 0xFFFFFFFFu);
+    const __amdgpu_buffer_rsrc_t rv_all = make_rsrc(p.v_cache, 0xFFFFFFFFu);
+    const uint32_t tile_mul = (uint32_t)H * kTileBytes, tile_add = (uint32_t)g * kTileBytes;
+    auto issue_quad = [&](uint32_t st, int ia, int ib) {
+        const uint32_t oa = (uint32_t)ia * tile_mul + tile_add, ob = (uint32_t)ib * tile_mul + tile_add;
+#pragma unroll
+        for (int i = 0; i < kWavePieces; ++i)
+            load_to_lds(fixed_v(i) ? rv_all : rk_all, pc_src[i], lds + st + pc_dst[i], fixed_b(i) ? ob : oa);
+    };
+
     for (int sp = 0; sp < kRing - 1 && sp < steps; ++sp) {
         int ia, ib;
         step_ids(sp, ia, ib);
         issue(sp, ia, ib);
     }
-    if (kRing - 1 < steps) step_ids(kRing - 1, nia, nib);
     wait_steps(min(kRing - 2, steps - 1));
     workgroup_barrier();
     // The scores of the step being computed and of the next one alternate
-    // between two register sets (the loop is unrolled by two), so the next
-    // step's products never have to be copied into the current step's set.
+    // between two register sets (the loops take two or four steps at a
+    // time), so the next step's products never have to be copied into the
+    // current step's set.
     f32x4_t s_cur[2][kRowBlocks], s_alt[2][kRowBlocks];
     scores(0, s_cur);
+    int nia = 0, nib = 0;  // block ids of the next step a general step issues
 
-    auto step = [&](int sp, f32x4_t (&s_now)[2][kRowBlocks], f32x4_t (&s_nxt)[2][kRowBlocks])
-                    __attribute__((always_inline)) {
-            const bool has_next = sp + 1 < steps;
-            if (has_next) {
+    // One step of the loop. kLast: the workgroup's last step, the only one
+    // with no next step, and the only one whose keys can reach past n (the
+    // unused rows of a sequence's last block) or whose tile B can be absent
+    // (an odd tile count): chunk lengths put every other step's 32 keys
+    // below n.
+    // kQ >= 0: a steady step, the kQ-th of its group of four (ring stage
+    // kQ; ia, ib: the block ids of the step it issues); -1: a general step.
+    auto step = [&](auto last_c, auto quad_c, int sp, f32x4_t (&s_now)[2][kRowBlocks],
+                    f32x4_t (&s_nxt)[2][kRowBlocks], int ia, int ib) __attribute__((always_inline)) {
+            constexpr bool kLast = decltype(last_c)::value;
+            constexpr int kQ = decltype(quad_c)::value;
+            constexpr bool kSteady = kQ >= 0;
+            if constexpr (kSteady) {
+                __builtin_amdgcn_s_waitcnt(vmcnt_wait((kRing - 3) * kWavePieces));
+                workgroup_barrier();
+                issue_quad((uint32_t)((kQ + kRing - 1) % kRing) * kStepBytes, ia, ib);
+            } else if constexpr (!kLast) {
                 // step sp + 1 in LDS for every wave; stage (sp - 1) % kRing free
                 wait_steps(min(kRing - 3, steps - 2 - sp));
                 workgroup_barrier();
                 if (sp + kRing - 1 < steps) issue(sp + kRing - 1, nia, nib);
             }
-            const uint32_t st = (uint32_t)(sp % kRing) * kStepBytes;
-            const uint32_t st_next = (uint32_t)((sp + 1) % kRing) * kStepBytes;
+            const uint32_t st = kSteady ? (uint32_t)kQ * kStepBytes : (uint32_t)(sp % kRing) * kStepBytes;
+            const uint32_t st_next = kSteady ? (uint32_t)((kQ + 1) % kRing) * kStepBytes
+                                             : (uint32_t)((sp + 1) % kRing) * kStepBytes;
             const int key0 = 2 * sp * kBlock;  // first key of tile A; tile B starts at key0 + 16
             const bool has_b = 2 * sp + 1 < tiles;
             if constexpr (!TM::kF32) {
-                if (wave_last >= key0) {  // else every row of the wave is complete
-                    // One straight-line block per step, so the compiler can
-                    // interleave the next step's QK products with this step's
-                    // weights, and so the accumulators have one definition per
-                    // step: the next step's K reads and QK products, this step's
-                    // maximum (the rare rescale first), weights, V reads and
-                    // P . V. On the last step the next-step reads see a stage no
-                    // load targets and their products are never used.
+                if (kSteady || wave_last >= key0) {  // else every row of the wave is complete
+                    // The next step's K reads, this step's maximum (the rare
+                    // rescale first), then one straight-line stretch (no branch:
+                    // the compiler may overlap the next step's QK products with
+                    // this step's weights, and the accumulators have one
+                    // definition per step): QK products, weights, V reads and
+                    // P . V.
                     // Diagonal steps replace the scores of keys past a row's
-                    // position by -inf. Keys at or past n (the unused rows of the
-                    // last block) and a tile B past the workgroup's last tile
-                    // (which the causal limit, not n, can end) are seen by no row:
-                    // their V elements are zeroed too, so that whatever those rows
-                    // hold cannot reach P . V.
+                    // position by -inf. On the last step, keys at or past n and
+                    // an absent tile B (past the workgroup's last tile, which
+                    // the causal limit, not n, can end) are seen by no row:
+                    // their V elements are zeroed too, so that whatever those
+                    // rows hold cannot reach P . V.
                     uint32_t kr[2][NK][KW];
-                    read_k(st_next, kr[0]);
-                    read_k(st_next + kKTileB, kr[1]);
+                    if constexpr (!kLast) {
+                        read_k(st_next, kr[0]);
+                        read_k(st_next + kKTileB, kr[1]);
+                    }
                     float x[kRowBlocks][8], xm[kRowBlocks];
                     bool trig = false;
 #pragma unroll
                     for (int rb = 0; rb < kRowBlocks; ++rb) {
                         // raw scores: tile A keys key0 + 4 g4 + e, tile B keys key0 + 16 + 4 g4 + e
                         // (selected in place, so that they keep their registers)
-                        if (key0 + 2 * kBlock - 1 > sel_from[rb]) {
+                        if (!kSteady && key0 + 2 * kBlock - 1 > sel_from[rb]) {
                             const int lim = pos[rb] - key0 - 4 * g4;  // visible: key offsets up to lim
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
@@ -779,7 +856,7 @@ void paged_prefill_kernel(PrefillParams p) {
 #pragma unroll
                         for (int rb = 0; rb < kRowBlocks; ++rb) rescale(rb, xm[rb]);
                     }
-                    qk_products(kr, s_nxt);
+                    if constexpr (!kLast) qk_products(kr, s_nxt);
                     V8 pk[kRowBlocks];
 #pragma unroll
                     for (int rb = 0; rb < kRowBlocks; ++rb) pk[rb] = weights16(rb, x[rb], m_use[rb]);
@@ -788,7 +865,7 @@ void paged_prefill_kernel(PrefillParams p) {
                     u32x4_t vop[NV];
                     uint32_t va[NVL][VLW], vb[NVL][VLW];
                     read_vops(st, vop, va, vb);
-                    if (key0 + 2 * kBlock > n || !has_b) {
+                    if constexpr (kLast) {
                         const int na = n - key0 - 4 * g4;        // live keys among this lane's four of tile A
                         const int nb = has_b ? na - kBlock : 0;  // and of tile B (the null block: none)
                         mask_vops(na, nb, vop, va, vb);
@@ -806,7 +883,7 @@ void paged_prefill_kernel(PrefillParams p) {
                 read_vops(st, vop, va, vb);
                 const int na = n - key0 - 4 * g4;          // live keys among this lane's four of tile A
                 const int nb = has_b ? na - kBlock : 0;  // and of tile B (the null block: none)
-                if (key0 + 2 * kBlock > n || !has_b) mask_vops(na, nb, vop, va, vb);
+                if (kLast) mask_vops(na, nb, vop, va, vb);
 #pragma unroll
                 for (int rb = 0; rb < kRowBlocks; ++rb) {
                     if (rb_last[rb] < key0) continue;  // no row of the block sees this step
@@ -843,13 +920,41 @@ void paged_prefill_kernel(PrefillParams p) {
                         }
                     l_run[rb] += ((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7]));
                 }
-                if (has_next && wave_last >= key0 + 2 * kBlock) scores(st_next, s_nxt);
+                if (!kLast && wave_last >= key0 + 2 * kBlock) scores(st_next, s_nxt);
             }
-            if (sp + kRing < steps) step_ids(sp + kRing, nia, nib);
+            if constexpr (!kLast && !kSteady)
+                if (sp + kRing < steps) step_ids(sp + kRing, nia, nib);
     };
-    for (int sp = 0; sp < steps; sp += 2) {
-        step(sp, s_cur, s_alt);
-        if (sp + 1 < steps) step(sp + 1, s_alt, s_cur);
+    using General = std::integral_constant<int, -1>;
+    int sp = 0;
+    if constexpr (kQuadShape) {
+        if (quads > 0) {
+            // the ids of the steps issued by group q: tiles 8 q + 6 .. 8 q + 13
+            const int32_t* idp = p.block_tables + bt_row + tile0 + 2 * (kRing - 1);
+            i32x8_t ids = uniform_read8(idp);
+            for (int q = 0; q < quads; ++q, sp += 4) {
+                i32x8_t nxt = ids;
+                if (q + 1 < quads) nxt = uniform_read8(idp + 8 * (q + 1));
+                step(std::false_type{}, std::integral_constant<int, 0>{}, sp, s_cur, s_alt, ids[0], ids[1]);
+                step(std::false_type{}, std::integral_constant<int, 1>{}, sp + 1, s_alt, s_cur, ids[2], ids[3]);
+                step(std::false_type{}, std::integral_constant<int, 2>{}, sp + 2, s_cur, s_alt, ids[4], ids[5]);
+                step(std::false_type{}, std::integral_constant<int, 3>{}, sp + 3, s_alt, s_cur, ids[6], ids[7]);
+                ids = nxt;
+            }
+        }
+    }
+    // the general steps: the rest in pairs (the two score sets alternate),
+    // then the last one
+    if (sp + kRing - 1 < steps) step_ids(sp + kRing - 1, nia, nib);
+    for (; sp + 2 < steps; sp += 2) {
+        step(std::false_type{}, General{}, sp, s_cur, s_alt, 0, 0);
+        step(std::false_type{}, General{}, sp + 1, s_alt, s_cur, 0, 0);
+    }
+    if (sp + 1 < steps) {
+        step(std::false_type{}, General{}, sp, s_cur, s_alt, 0, 0);
+        step(std::true_type{}, General{}, sp + 1, s_alt, s_cur, 0, 0);
+    } else if (sp < steps) {
+        step(std::true_type{}, General{}, sp, s_cur, s_alt, 0, 0);
     }
 
     __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));  // no load into LDS outlives the workgroup
@@ -1037,6 +1142,14 @@ int64_t prefill_task_bound(int num_seqs, int num_tokens, int group, int num_kv_h
     return (int64_t)num_kv_heads * (((int64_t)num_tokens * group) / kGroupRows + num_seqs);
 }
 
+// Whether every (block, KV head) tile of a cache lies below 4 GiB from its
+// start, so that the attention kernel may address tiles by 32-bit offsets.
+template <int KT, int D>
+static int tile_offsets_fit_32(int num_blocks, int num_kv_heads) {
+    const uint64_t bytes = (uint64_t)num_blocks * (uint64_t)num_kv_heads * kBlock * D * Elem<KT>::bytes;
+    return bytes <= 0xFFFFFFFFull ? 1 : 0;
+}
+
 template <int KT, int QT, int D>
 static hipError_t launch_prefill_typed(const PrefillArgs& a) {
     PrefillParams p{};
@@ -1056,6 +1169,7 @@ static hipError_t launch_prefill_typed(const PrefillArgs& a) {
     p.qk_scale_log2 = a.scale * (KT == PKV_FP8_E4M3 ? a.k_scale : 1.f) * 1.44269504088896340736f;
     p.v_scale = KT == PKV_FP8_E4M3 ? a.v_scale : 1.f;
     p.out = a.out;
+    p.offsets32 = tile_offsets_fit_32<KT, D>(a.num_blocks, a.num_kv_heads);
     // The keys are split only when the row tiles (at least T * G / 128 per KV
     // head) fall short of the workgroup target; otherwise the workspace is
     // not touched and no merge launch is needed.
@@ -1136,6 +1250,7 @@ static hipError_t launch_prefix_typed(const DecodeArgs& a, bool beside, hipStrea
     p.res_lse = a.res_lse;
     p.all_slots = beside ? 1 : 0;
     p.pf_target = beside ? kPrefixBesideTarget : kPrefixTargetWorkgroups;
+    p.offsets32 = tile_offsets_fit_32<KT, D>(a.num_blocks, a.num_kv_heads);
     const int64_t grid = prefix_workgroup_bound(a.num_seqs, a.group, a.num_kv_heads, a.num_groups);
     auto kernel = paged_prefill_kernel<KT, QT, D, true>;
     hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kPrefillThreads), 0, stream, p);
