@@ -813,12 +813,13 @@ void paged_prefill_kernel(PrefillParams p) {
             const bool has_b = 2 * sp + 1 < tiles;
             if constexpr (!TM::kF32) {
                 if (kSteady || wave_last >= key0) {  // else every row of the wave is complete
-                    // The next step's K reads, this step's maximum (the rare
-                    // rescale first), then one straight-line stretch (no branch:
+                    // The next step's K reads and this step's V reads (their
+                    // LDS latency passes under the maximum), this step's
+                    // maximum (the rare rescale first), then one straight-line
+                    // stretch (no branch:
                     // the compiler may overlap the next step's QK products with
                     // this step's weights, and the accumulators have one
-                    // definition per step): QK products, weights, V reads and
-                    // P . V.
+                    // definition per step): QK products, weights and P . V.
                     // Diagonal steps replace the scores of keys past a row's
                     // position by -inf. On the last step, keys at or past n and
                     // an absent tile B (past the workgroup's last tile, which
@@ -830,6 +831,9 @@ void paged_prefill_kernel(PrefillParams p) {
                         read_k(st_next, kr[0]);
                         read_k(st_next + kKTileB, kr[1]);
                     }
+                    u32x4_t vop[NV];
+                    uint32_t va[NVL][VLW], vb[NVL][VLW];
+                    read_vops(st, vop, va, vb);
                     float x[kRowBlocks][8], xm[kRowBlocks];
                     bool trig = false;
 #pragma unroll
@@ -860,11 +864,6 @@ void paged_prefill_kernel(PrefillParams p) {
                     V8 pk[kRowBlocks];
 #pragma unroll
                     for (int rb = 0; rb < kRowBlocks; ++rb) pk[rb] = weights16(rb, x[rb], m_use[rb]);
-                    // V is read once the K operands are consumed (their registers
-                    // are reused)
-                    u32x4_t vop[NV];
-                    uint32_t va[NVL][VLW], vb[NVL][VLW];
-                    read_vops(st, vop, va, vb);
                     if constexpr (kLast) {
                         const int na = n - key0 - 4 * g4;        // live keys among this lane's four of tile A
                         const int nb = has_b ? na - kBlock : 0;  // and of tile B (the null block: none)
