@@ -94,11 +94,18 @@ __device__ __forceinline__ void wait_vmcnt_from(int n) {
 }
 __device__ __forceinline__ void wait_vmcnt(int n) { wait_vmcnt_from<0>(n); }
 
-// All waves of the workgroup reach this point. A compiler barrier on both
-// sides keeps memory accesses from moving across it; unlike __syncthreads()
-// it does not wait for this wave's outstanding loads.
+// All waves of the workgroup reach this point, each with its LDS reads
+// complete. A compiler barrier on both sides keeps memory accesses from
+// moving across it; unlike __syncthreads() it does not wait for this wave's
+// outstanding buffer loads into LDS (the ring's own waits count those).
+// Waiting for the LDS reads matters because the compiler may move the
+// products that consume a step's operands past the next step's barrier:
+// the reads of a ring stage must be done before any wave, once past the
+// barrier, issues the loads that refill that stage.
 __device__ __forceinline__ void workgroup_barrier() {
     asm volatile("" ::: "memory");
+    // lgkmcnt(0), vmcnt and expcnt left at their maxima (gfx9 encoding)
+    __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
