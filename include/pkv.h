@@ -421,7 +421,7 @@ int pkv_debug_gather(const void *k_cache, const void *v_cache, const pkv_cache_d
  * device memory at `src` once as a plain stream of 16-byte nontemporal
  * loads (the decode kernel's load width and cache policy), spread over
  * num_workgroups workgroups of 256 threads (0 = one per compute unit), and XOR
- * every 32-bit word into *sink (device; one atomic per wave) so that no read
+ * every 32-bit word into *sink (device; one atomic per workgroup) so that no read
  * can be dropped. Timed by the caller, it gives the read bandwidth this
  * device delivers to a streaming kernel: the yardstick beside the published
  * HBM peak ([ttlab] section 1 judges decode by the fraction of the rated

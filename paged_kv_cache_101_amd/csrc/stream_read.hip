@@ -7,8 +7,8 @@
 // The buffer is read once as 32 KiB chunks, chunk c by workgroup c mod the
 // grid, each of the 256 threads issuing eight 16-byte nontemporal loads per
 // chunk (the decode kernel's load width and cache policy). Every word is
-// XORed into one value per wave, and each wave XORs its value into *sink,
-// so no load can be dropped. One workgroup per compute unit is the default:
+// XORed into one value per workgroup, and each workgroup XORs its value
+// into *sink, so no load can be dropped. One workgroup per compute unit is the default:
 // a sweep on MI355X over 1..4 workgroups per CU, 4..16 loads per thread,
 // contiguous or interleaved chunks and cached loads found this the fastest
 // (7.09 TB/s over 1.34 GB; two workgroups 6.8, four 6.2-6.3, cached loads
@@ -45,7 +45,18 @@ __global__ __launch_bounds__(kStreamThreads) void stream_read_kernel(const uint8
     }
 #pragma unroll
     for (int sh = 1; sh < kWave; sh <<= 1) acc ^= (uint32_t)__shfl_xor((int)acc, sh, kWave);
-    if ((threadIdx.x & (kWave - 1)) == 0) atomicXor(sink, acc);
+    // one atomic per workgroup: atomics on one address are serialised, and
+    // one per wave cost ~10 ns each on MI355X (1024 of them, the default
+    // grid's waves, added up to ~10 us to a 147 MB read)
+    __shared__ uint32_t wave_acc[kStreamThreads / kWave];
+    if ((threadIdx.x & (kWave - 1)) == 0) wave_acc[threadIdx.x / kWave] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t x = 0;
+#pragma unroll
+        for (int i = 0; i < kStreamThreads / kWave; ++i) x ^= wave_acc[i];
+        atomicXor(sink, x);
+    }
 }
 
 }  // namespace
