@@ -283,15 +283,77 @@ void paged_decode_kernel(DecodeParams p) {
     const int max_ctx = mb * kBlock;
     const int pt = PART ? p.part_tiles : 1;  // tiles per partition (PART)
     const float nan = __builtin_nanf("");
-    // prefix groups (suffix pass only; an unusable description counts as none)
-    const int ng = PFX ? usable_groups(p.group_starts, p.group_prefix, p.num_groups, S, mb, lane) : 0;
+    // The lengths of the first kScanChunks * 64 sequences, read once (one
+    // memory round, with the prefix groups' description) and kept in
+    // registers: the scan, the sequences with no tiles and every segment
+    // change of the tile stream take them from here.
+    constexpr int kScanChunks = 4;
+    constexpr int kCached = kScanChunks * kWave;
+    int n_c[kScanChunks], u_c[kScanChunks];  // length and units of sequence c * 64 + lane
+#pragma unroll
+    for (int c = 0; c < kScanChunks; ++c) {
+        const int s = c * kWave + lane;
+        n_c[c] = s < S ? p.context_lens[s] : 0;
+    }
+    // Prefix groups (suffix pass only; an unusable description counts as
+    // none). Up to 64 groups are held one per lane, start, end and shared
+    // blocks of group `lane`, so that finding a sequence's group takes no
+    // memory round; more are searched in memory.
+    int ng = 0, g_a = 0, g_b = 0, g_p = 0;
+    if constexpr (PFX) {
+        const int ngd = p.num_groups;
+        if (ngd > 0 && ngd <= kWave) {
+            bool ok = true;
+            if (lane < ngd) {
+                g_a = p.group_starts[lane];
+                g_b = p.group_starts[lane + 1];
+                g_p = p.group_prefix[lane];
+                ok = g_a >= 0 && g_a <= g_b && g_b <= S && g_p >= 0 && g_p <= mb;
+            }
+            ng = __ballot(!ok) == 0 ? ngd : 0;
+            if (ng == 0) g_a = g_b = 0;  // no group matches any sequence
+        } else {
+            ng = usable_groups(p.group_starts, p.group_prefix, ngd, S, mb, lane);
+        }
+    }
+    const bool grp_lanes = PFX && ng > 0 && ng <= kWave;
+    // shared blocks of sequence s: wave-uniform s, and s per lane
     auto pre_uniform = [&](int s) -> int {
-        if constexpr (PFX) return prefix_blocks_of<true>(p.group_starts, p.group_prefix, ng, s);
-        else return 0;
+        if constexpr (PFX) {
+            if (grp_lanes) {
+                const unsigned long long hit = __ballot(g_a <= s && s < g_b);
+                return hit ? __builtin_amdgcn_readlane(g_p, __ffsll(hit) - 1) : 0;
+            }
+            return prefix_blocks_of<true>(p.group_starts, p.group_prefix, ng, s);
+        } else {
+            return 0;
+        }
     };
     auto pre_lane = [&](int s) -> int {
-        if constexpr (PFX) return prefix_blocks_of<false>(p.group_starts, p.group_prefix, ng, s);
-        else return 0;
+        if constexpr (PFX) {
+            if (grp_lanes) {
+                int pre = 0;
+                for (int j = 0; j < ng; ++j) {
+                    const int a = __builtin_amdgcn_readlane(g_a, j), b = __builtin_amdgcn_readlane(g_b, j);
+                    pre = (a <= s && s < b) ? __builtin_amdgcn_readlane(g_p, j) : pre;
+                }
+                return pre;
+            }
+            return prefix_blocks_of<false>(p.group_starts, p.group_prefix, ng, s);
+        } else {
+            return 0;
+        }
+    };
+    // length of sequence s (wave-uniform)
+    auto len_uniform = [&](int s) -> int {
+        if (s < kCached) {
+            int n = 0;
+#pragma unroll
+            for (int c = 0; c < kScanChunks; ++c)
+                if ((s >> 6) == c) n = __builtin_amdgcn_readlane(n_c[c], s & (kWave - 1));
+            return n;
+        }
+        return uniform_read(p.context_lens, s);
     };
     // Units of work a segment of nb tiles holds: its tiles (balanced split),
     // or its partitions of pt tiles (PART).
@@ -305,7 +367,7 @@ void paged_decode_kernel(DecodeParams p) {
     // suffix tiles gets an empty result (n == 16 * pre) or a NaN one (its
     // length does not hold its group's prefix). One wave writes each.
     for (int s = w; s < S; s += nw_launch) {
-        const int n = p.context_lens[s];
+        const int n = len_uniform(s);
         const int pre = pre_uniform(s);
         if (tiles_of(n, pre, max_ctx) > 0) continue;
         if (PFX && pre > 0) {
@@ -318,16 +380,7 @@ void paged_decode_kernel(DecodeParams p) {
     }
 
     // Total units T and this wave's slice [a, b) of them. Units are numbered
-    // like the tiles: sequence-major, then KV head, then position. The
-    // lengths of the first kScanChunks * 64 sequences are read once, in one
-    // memory round, and kept in registers for the second pass.
-    constexpr int kScanChunks = 4;
-    int n_c[kScanChunks], u_c[kScanChunks];  // length and units of sequence c * 64 + lane
-#pragma unroll
-    for (int c = 0; c < kScanChunks; ++c) {
-        const int s = c * kWave + lane;
-        n_c[c] = s < S ? p.context_lens[s] : 0;
-    }
+    // like the tiles: sequence-major, then KV head, then position.
     int64_t total = 0;
 #pragma unroll
     for (int c = 0; c < kScanChunks; ++c) {
@@ -405,7 +458,7 @@ void paged_decode_kernel(DecodeParams p) {
         } else {
             int s = c.s + 1, n = 0, pre = 0, nb = 0;
             for (; s < S; ++s) {
-                n = uniform_read(p.context_lens, s);
+                n = len_uniform(s);
                 pre = pre_uniform(s);
                 nb = tiles_of(n, pre, max_ctx);
                 if (nb > 0) break;
