@@ -106,15 +106,20 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_hash() -> str:
+def kernel_hash(root: str = None) -> str:
     """Hash of the attention kernel sources (decode, and the prefix pass of
-    the shared-prefix call): counter figures are valid only for the build
-    they were taken on."""
+    the shared-prefix call) with comments and white space removed: counter
+    figures are valid only for the code they were taken on, and a comment
+    does not change it."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in ("paged_decode.hip", "paged_prefill.hip", "pkv_tile.h", "pkv_device.h"):
-        with open(os.path.join(ROOT, "paged_kv_cache_101_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(root or ROOT, "paged_kv_cache_101_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)  # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                # line comments
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -25,9 +25,13 @@
 //     P^T . V contracts both tiles of a step in one 16x16x32 MFMA per 16
 //     output columns. Tiles wholly before a row block's first position need
 //     no mask; the diagonal tiles mask key k > p per row by select; steps
-//     after the last position of all the wave's rows are skipped. Every step
-//     runs one straight-line body, so the compiler overlaps the next step's
-//     QK products with this step's softmax.
+//     after the last position of all the wave's rows are skipped. A step's
+//     products and weights form one straight-line stretch; only the
+//     workgroup's last step (peeled off the loop) masks V.
+//   * The steady steps (no select, no mask, no end check: most of them) run
+//     in groups of four with fixed ring stages and a handful of scalar
+//     instructions each: block ids eight at a time, tiles addressed by one
+//     K and one V resource plus a 32-bit offset.
 //   * Workgroup index -> (sequence, row tile, KV head) with the KV head fastest,
 //     so the workgroups of one head land on one XCD (workgroups are dealt to
 //     the 8 XCDs round-robin) and share its L2; within a sequence the row
