@@ -81,7 +81,7 @@ PREFILL_MIN_WARMUP_S = 0.25  # untimed warm-up of the prefill workloads, at leas
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gqa40",
                     choices=["gqa40", "gqa40_tp8", "qwen", "prefix", "prefix_shared", "fp8", "tiny",
@@ -99,7 +99,7 @@ def parse():
                     help="also time decode launches that each follow a 1 GiB device write, "
                          "which evicts the L2 caches and the 256 MB MALL (the timed launch then "
                          "reads its KV from HBM)")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (for counter scaling)")

@@ -137,10 +137,14 @@ uint8_t oracle_fp8_e4m3_encode(double x, double c)
 
 /* The same rounding applied to a quotient taken in float32: y = x / c as one
  * IEEE single-precision division (round to nearest even), then the nearest
- * code of y as above. This is the precision in which a quantising append
- * decides each code (the library's kernel divides in float32), so both sides
- * decide in the same arithmetic; with c a power of two it equals
- * oracle_fp8_e4m3_encode(x, c). */
+ * code of y as above. The pages give fp8 storage with a per-tensor scale
+ * but no precision for the division; a code is an integer decided by
+ * floating point, so both the checked side and this one must take it in one
+ * stated precision, and float32 is the narrowest IEEE type that holds every
+ * incoming element (16-bit or float32 rows) and the scale exactly. Only a
+ * quotient within rounding of a midpoint between two codes can differ from
+ * the exact one; with c a power of two the quotient is exact and this
+ * equals oracle_fp8_e4m3_encode(x, c). */
 uint8_t oracle_fp8_e4m3_encode_f32(float x, float c)
 {
     volatile float y = x / c;
