@@ -6,7 +6,8 @@ checked as a one-token chunk with the context up to its own position (the
 same definition). Cases: chunks of 1, 15, 16, 17 tokens and several row tiles
 of 128 rows, chunks shorter than their context, empty chunks, every cache type,
 G = 1..8 and d 64/128, one-token chunks equal to decode, a prompt fed whole or
-in chunks, and invalid chunks (skipped) or block ids (NaN rows)."""
+in chunks, and invalid chunks (skipped) or block ids (NaN rows), also where a
+long 16-bit chunk would otherwise run its steps in groups of four."""
 import numpy as np
 import pytest
 import torch
@@ -132,6 +133,31 @@ def test_invalid_chunks_and_blocks(gpu):
     got = out_to_f64(out)
     assert np.isnan(got[10:20]).all() and np.isnan(got[20:30]).all()
     assert_close(got[:10], oracle_rows(b, q, qs)[:10], "bf16", "valid sequence")
+
+
+@pytest.mark.parametrize("kv", ["f16", "bf16"])
+def test_invalid_block_among_steady_steps(gpu, kv):
+    """d 128, 16-bit tiles: long chunks run most of their steps in groups of
+    four, with the block ids checked once before the loop. A block outside the
+    pool (and a negative id) in that range must still turn the sequence's rows
+    into NaN, through the general steps, and leave the other sequence's rows
+    equal to the oracle's."""
+    ctx = [1100, 900]       # 69 and 57 tiles of keys: several groups of four steps
+    q_lens = [40, 30]
+    b, q, qs = make(71 if kv == "f16" else 72, ctx, q_lens, kv, kv, 16, 4, 128, gpu)
+    bt = b.block_tables.clone()
+    bt[0, 9] = b.num_blocks + 2
+    bt[0, 10] = -1
+    out = torch.empty_like(q)
+    kc, vc = device_caches(b)
+    B.pkv_paged_attention_prefill(q, kc, vc, desc(b), bt, b.context_lens, qs, b.scale, out)
+    torch.cuda.synchronize()
+    got = out_to_f64(out)
+    print(f"[case] {kv}: rows of sequence 0 NaN: {np.isnan(got[:40]).all()}", flush=True)
+    assert np.isnan(got[:40]).all()
+    ref = oracle_rows(b, q, qs)
+    e = assert_close(got[40:], ref[40:], kv, "sequence with valid blocks")
+    print(f"[parity] {kv} valid sequence: {e}", flush=True)
 
 
 def test_no_tokens_is_a_no_op(gpu):
