@@ -694,8 +694,12 @@ void paged_decode_kernel(DecodeParams p) {
                 }
             } else if constexpr (PART) {
                 // partition j of a split segment: unnormalised accumulator,
-                // max, sum to its own slot, plain stores; the merge launch
-                // that follows (the kernel boundary orders them) reduces them
+                // max, sum to its own slot, plain nontemporal stores; the
+                // merge launch that follows (the kernel boundary orders them)
+                // reduces them. (The stores hold up the in-order wait for the
+                // next tiles until they complete; nontemporal ones complete
+                // sooner: 220 -> 215 us for 16 x 32768 fp8 in 512-token
+                // partitions.)
                 float* slotp = p.slots +
                                ((size_t)(cc.s * H + cc.g) * p.part_stride + clo / pt) * SLOT;
 #pragma unroll
@@ -703,12 +707,13 @@ void paged_decode_kernel(DecodeParams p) {
                     const int hh = 4 * g4 + r;
                     if (hh < GM) {
 #pragma unroll
-                        for (int j = 0; j < NV; ++j) slotp[hh * D + 16 * j + t] = o[j][r];
+                        for (int j = 0; j < NV; ++j)
+                            __builtin_nontemporal_store(o[j][r], slotp + hh * D + 16 * j + t);
                     }
                 }
                 if (lane < GM) {
-                    slotp[GM * D + lane] = piece_bad ? nan : m_run;
-                    slotp[GM * D + GM + lane] = piece_bad ? nan : lt;
+                    __builtin_nontemporal_store(piece_bad ? nan : m_run, slotp + GM * D + lane);
+                    __builtin_nontemporal_store(piece_bad ? nan : lt, slotp + GM * D + GM + lane);
                 }
             } else {
                 // partial of a split segment: unnormalised accumulator, max, sum
