@@ -300,6 +300,8 @@ def bench_prefill(args):
         kh, vh = W.to_numpy(b.k_cache), W.to_numpy(b.v_cache)
         bt, cl = b.block_tables.cpu().numpy(), b.context_lens.cpu().numpy()
         qh = W.to_numpy(q)
+        # grow the sample until one run takes about cpu_seconds: each next
+        # size from the rate just measured (at most 8x at a time)
         k = 1
         while True:
             rows = np.arange(T - chunk, T - chunk + k)
@@ -309,9 +311,9 @@ def bench_prefill(args):
                                  np.ascontiguousarray(bt[[S - 1] * k]), (pos + 1).astype(np.int32),
                                  np.arange(k + 1, dtype=np.int32), b.scale)
             el = time.perf_counter() - t0
-            if el > args.cpu_seconds / 4 or k >= chunk:
+            if el >= 0.7 * args.cpu_seconds or k >= chunk:
                 break
-            k = min(chunk, k * 4)
+            k = min(chunk, max(k + 1, min(8 * k, int(k * args.cpu_seconds / max(el, 1e-3)))))
         sample_flops = 4 * d * Hq * int((pos + 1).sum())
         cpu = {"value": round(sample_flops / el / 1e12, 6), "unit": "TFLOP/s",
                "cores": oracle.num_threads(), "kind": "oracle",
