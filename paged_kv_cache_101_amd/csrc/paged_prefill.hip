@@ -455,14 +455,21 @@ void paged_prefill_kernel(PrefillParams p) {
     static_assert(kTileBytes % 1024 == 0, "piece split");
     static_assert((kRing - 2) * kWavePieces <= 16, "wait count");
     // V pieces are stored permuted so that the V operand reads are
-    // lane-contiguous: a lane's V load i (tokens 4 * g4 .. + 3 of its element
+    // conflict-free: a lane's V load i (tokens 4 * g4 .. + 3 of its element
     // columns, kVChunks 16-byte chunks) sits at chunk 4 * t + g4 (times
-    // kVChunks) of its region of the tile, so the piece's lane L fetches the
-    // chunk that reading lane L needs. fp8 V loads are 8 bytes per lane and
-    // are stored as they are.
+    // kVChunks) of its region of the tile, and the piece's lane L fetches the
+    // chunk that the lane reading 16-byte slot L needs. Float32 tiles: lane
+    // (t, g4) reads slot 16 g4 + t. 16-bit tiles: slot v_slot(t, g4) below,
+    // read as two 8-byte halves. fp8 V loads are 8 bytes per lane and are
+    // stored as they are.
     constexpr int kVChunks = VLW / 4;
     auto v_piece_src = [&](int pc) -> uint32_t {
-        if constexpr (kVChunks > 0) {
+        if constexpr (kDirectV) {
+            // the inverse of v_slot: slot L = 16 g4 + r is read by column t
+            const int g4l = lane >> 4, r = lane & 15;
+            const int tl = (r & 7) + 8 * ((r >> 3) ^ (g4l & 1));
+            return (uint32_t)(pc * 1024 + (4 * tl + g4l) * 16);
+        } else if constexpr (kVChunks > 0) {
             const int i = pc / kVChunks, h = pc % kVChunks;
             const int sigma = 4 * (lane & 15) + (lane >> 4);  // 4 * t + g4 of reading lane L
             return (uint32_t)(i * 1024 * kVChunks + (kVChunks * sigma + h) * 16);
@@ -642,18 +649,24 @@ void paged_prefill_kernel(PrefillParams p) {
     // V of the step in stage st: for 16-bit caches the P . V operands
     // themselves (operand j = tile A's 4 tokens of element column 16 j + t,
     // then tile B's), else the loads. A lane's 16-byte chunk of each tile
-    // holds two operands' halves; the compiler reads each chunk whole
-    // (conflict-free 16-byte reads at a 16-byte lane stride) and pairs the
-    // halves in registers. Reading the two 8-byte halves separately, each
-    // straight into its operand, left a 16-byte lane stride for 8-byte
-    // reads, a two-way bank conflict: 4% slower over the step (610 against
-    // 589 us, same box), with LDS bank-conflict stalls in 19% of the cycles.
+    // holds two operands' halves (element columns 32 i + t and 32 i + 16 + t),
+    // read as two 8-byte halves, each straight into its operand. The lanes of
+    // columns t >= 8 take the halves the other way round (their operand 2 i
+    // is column 32 i + 16 + t, and o[.][2 i], o[.][2 i + 1] trade places for
+    // those output elements until the loop ends), and the chunk of lane
+    // (t, g4) sits at slot v_slot(t, g4): together these make both 8-byte
+    // reads conflict-free (any 16 or 32 consecutive lanes hit distinct
+    // banks). Reading the chunk whole and pairing the halves in registers
+    // took about 24 register moves per step; reading the halves at a 16-byte
+    // lane stride had two-way bank conflicts.
+    const int v_first = (t >> 3) * 8;  // byte of the chunk that operand 2 i takes
+    const uint32_t v_slot = (uint32_t)(16 * g4 + (t & 7) + 8 * ((g4 & 1) ^ (t >> 3))) * 16;
     auto read_vops = [&](uint32_t st, u32x4_t (&vop)[NV], uint32_t (&va)[NVL][VLW],
                          uint32_t (&vb)[NVL][VLW]) {
         if constexpr (kDirectV) {
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
-                const uint8_t* la = lds + st + 2 * kTileBytes + lane * 16 + hh * 8;
+                const uint8_t* la = lds + st + 2 * kTileBytes + v_slot + (hh == 0 ? v_first : 8 - v_first);
 #pragma unroll
                 for (int i = 0; i < NVL; ++i) {
                     const u32x2_t a2 = *reinterpret_cast<const u32x2_t*>(la + 2 * i * 1024);
@@ -968,6 +981,19 @@ void paged_prefill_kernel(PrefillParams p) {
     }
 
     __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));  // no load into LDS outlives the workgroup
+    if constexpr (kDirectV) {
+        // output elements 4 g4 .. + 3 with 4 g4 >= 8 (columns t >= 8 of the
+        // V operands) were accumulated with each pair of operands swapped
+        const bool sw = g4 >= 2;
+#pragma unroll
+        for (int rb = 0; rb < kRowBlocks; ++rb)
+#pragma unroll
+            for (int i = 0; i < NV / 2; ++i) {
+                const f32x4_t a = o[rb][2 * i], b = o[rb][2 * i + 1];
+                o[rb][2 * i] = sw ? b : a;
+                o[rb][2 * i + 1] = sw ? a : b;
+            }
+    }
 
     // ---- lane (t, g4) holds elements 16 j + 4 g4 .. + 3 of row t ----
     const float nan = __builtin_nanf("");
