@@ -106,15 +106,20 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_hash(root: str = None) -> str:
-    """Hash of the attention kernel sources (decode, and the prefix pass of
-    the shared-prefix call) with comments and white space removed: counter
-    figures are valid only for the code they were taken on, and a comment
-    does not change it."""
+def kernel_hash(workload: str = None, root: str = None) -> str:
+    """Hash of the sources of the attention kernels a decode workload
+    launches (the decode kernel and its merge; the shared-prefix call also
+    runs the prefix pass and its merge from paged_prefill.hip), with comments
+    and white space removed: counter figures are valid only for the code they
+    were taken on, and a comment does not change it. workload None: every
+    attention source."""
     import hashlib
     import re
     h = hashlib.sha256()
-    for f in ("paged_decode.hip", "paged_prefill.hip", "pkv_tile.h", "pkv_device.h"):
+    files = ["paged_decode.hip", "pkv_tile.h", "pkv_device.h"]
+    if workload in (None, "prefix_shared"):
+        files.insert(1, "paged_prefill.hip")
+    for f in files:
         with open(os.path.join(root or ROOT, "paged_kv_cache_101_amd", "csrc", f)) as fh:
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)  # block comments
@@ -134,7 +139,7 @@ def load_traffic(workload: str):
         for line in fh:
             if line.startswith("{"):
                 rec = json.loads(line)
-    if rec is None or rec.get("kernel_hash") != kernel_hash():
+    if rec is None or rec.get("kernel_hash") != kernel_hash(workload.split(":")[0]):
         return None
     return rec.get("traffic_bytes_per_launch", {}).get("total")
 
