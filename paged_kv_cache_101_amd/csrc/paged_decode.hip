@@ -896,8 +896,12 @@ static hipError_t launch_typed(const DecodeArgs& a) {
         // over 2..16 per CU): more concurrent streams lower the bandwidth the
         // memory system delivers and widen the spread between waves. fp8
         // tiles carry half the bytes, and the 16 x 32768 fp8 shape runs 27%
-        // faster at 6 per CU than at 3.
-        nw = (per_cu < kTarget ? per_cu : kTarget) * cus * kWavesPerGroup;
+        // faster at 6 per CU than at 3. The suffix pass of the shared-prefix
+        // call (short segments, the prefix pass running beside it) takes one
+        // more: 256 sequences with 64..512-token suffixes, 96.0 us per call
+        // at 4 per CU against 98.6 at 3 (2, 5, 6 and 8 per CU were slower).
+        constexpr int kWant = PFX ? (kTarget + 1 > 8 ? 8 : kTarget + 1) : kTarget;
+        nw = (per_cu < kWant ? per_cu : kWant) * cus * kWavesPerGroup;
         if (nw > kMaxWorkers) nw = kMaxWorkers;
         if (PART) {
             // whole partitions per wave: the nearest whole number k of them
