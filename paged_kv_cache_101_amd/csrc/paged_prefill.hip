@@ -1258,9 +1258,12 @@ hipError_t launch_paged_prefill(const PrefillArgs& a) {
 // log-sum-exp rule, together with the suffix result.
 
 // Beside the suffix pass, the prefix pass aims at fewer workgroups (its work
-// hides under the suffix pass's stream, and fewer chunks leave fewer partials
-// for the merge launch to read).
-constexpr int kPrefixBesideTarget = 256;
+// hides under the suffix pass's stream, fewer of its workgroups take CUs from
+// that stream, and fewer chunks leave fewer partials for the merge launch to
+// read). 256 sequences sharing a 2048-token prefix, 32 / 8 heads: 106 us per
+// call at a target of 64 (one chunk), 93 at 96 and 128 (two), 93.7 at 192,
+// 96 at 256 and 106 at 384.
+constexpr int kPrefixBesideTarget = 128;
 
 template <int KT, int QT, int D>
 static hipError_t launch_prefix_typed(const DecodeArgs& a, bool beside, hipStream_t stream) {
