@@ -66,9 +66,13 @@ inline size_t tail_offset(size_t ws_bytes, size_t bytes) { return (ws_bytes & ~(
 
 // ---- shared-prefix decode ----------------------------------------------------
 // The prefix pass runs workgroups of 128 (member, query head) rows of one
-// prefix group and KV head over one chunk of the prefix blocks; the chunk
-// count aims at this many workgroups.
-constexpr int kPrefixTargetWorkgroups = 512;
+// prefix group and KV head over one chunk of the prefix blocks, and a
+// prefill with few query rows splits each row tile's keys the same way; the
+// chunk count aims at this many workgroups: one per CU of an MI355X. Eight
+// 16-token chunks over 8192-token contexts (32 / 8 heads) take 52.8 us at
+// 256 (four chunks per row tile), 56.3 at 512, 59-61 at 192, 320 and 384,
+// and 65-79 at 128, 768 and 1024.
+constexpr int kPrefixTargetWorkgroups = 256;
 // Partial slots of 16 rows in the workspace. The chunk count is capped so
 // that the slots of chunked groups fit; an unchunked group needs none.
 constexpr int kPrefixSlots = 4096;
