@@ -465,7 +465,7 @@ void paged_prefill_kernel(PrefillParams p) {
     constexpr int kVChunks = VLW / 4;
     auto v_piece_src = [&](int pc) -> uint32_t {
         if constexpr (kDirectV) {
-            // the inverse of v_slot: slot L = 16 g4 + r is read by column t
+            // the inverse of v_slot: slot L = 16 g4 + r is read by lane (tl, g4)
             const int g4l = lane >> 4, r = lane & 15;
             const int tl = (r & 7) + 8 * ((r >> 3) ^ (g4l & 1));
             return (uint32_t)(pc * 1024 + (4 * tl + g4l) * 16);
