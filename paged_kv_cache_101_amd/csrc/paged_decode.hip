@@ -823,21 +823,51 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void partition_merge_kernel(Pa
     const int np = (nb + p.part_tiles - 1) / p.part_tiles;
     if (np <= 1) return;
     const float* base = p.slots + (size_t)(s * p.num_kv_heads + g) * p.part_stride * SLOT;
+    // Lane j holds partition j0 + j's maximum and sum (partitions 64 at a
+    // time; lanes past the last re-read it and drop it), so the weights cost
+    // one memory round; the accumulators then follow with 16 partitions'
+    // loads in flight, each weight taken from its lane. (Reading each
+    // partition's maximum and sum in the accumulator loop, 8 partitions in
+    // flight, cost about 3 us more per call for 16 x 32768 tokens at 64
+    // query heads; 32 in flight was no faster than 16.)
     float M = -INFINITY;
-    for (int j0 = 0; j0 < np; j0 += kWave) {
-        const int j = j0 + lane;
-        M = fmaxf(M, wave_max(j < np ? base[(size_t)j * SLOT + GM * D + hh] : -INFINITY));
+    if (np > kWave) {
+        for (int j0 = 0; j0 < np; j0 += kWave) {
+            const float m = base[(size_t)min(j0 + lane, np - 1) * SLOT + GM * D + hh];
+            M = fmaxf(M, wave_max(j0 + lane < np ? m : -INFINITY));
+        }
     }
     float L = 0.f, acc[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-#pragma unroll 8
-    for (int j = 0; j < np; ++j) {
-        const float* sj = base + (size_t)j * SLOT;
-        const float wj = __builtin_amdgcn_exp2f(sj[GM * D + hh] - M);
-        L = fmaf(wj, sj[GM * D + GM + hh], L);
+    for (int j0 = 0; j0 < np; j0 += kWave) {
+        const bool live = j0 + lane < np;
+        const float* sl = base + (size_t)min(j0 + lane, np - 1) * SLOT;
+        const float m = sl[GM * D + hh], l = sl[GM * D + GM + hh];
+        if (np <= kWave) M = wave_max(live ? m : -INFINITY);
+        const float w = live ? __builtin_amdgcn_exp2f(m - M) : 0.f;
+        L += wave_sum(w * l);
+        const int cnt = min(kWave, np - j0);
+        constexpr int kBatch = 16;
+        for (int jb = 0; jb < cnt; jb += kBatch) {
+            // a batch of partitions' accumulators, loaded unconditionally
+            // (past the last: the last again, with weight zero)
+            float a[kBatch][EPL];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] = fmaf(wj, sj[hh * D + lane * EPL + e], acc[e]);
+            for (int u = 0; u < kBatch; ++u) {
+                const float* sj = base + (size_t)(j0 + min(jb + u, cnt - 1)) * SLOT;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) a[u][e] = sj[hh * D + lane * EPL + e];
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const float wu = __builtin_bit_cast(
+                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), min(jb + u, kWave - 1)));
+                const float wj = jb + u < cnt ? wu : 0.f;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) acc[e] = fmaf(wj, a[u][e], acc[e]);
+            }
+        }
     }
     const float sc = p.v_scale / L;
     const size_t orow = (size_t)s * p.num_q_heads + h;
