@@ -1135,6 +1135,51 @@ __global__ __launch_bounds__(kMergeThreads) void chunk_merge_kernel(PrefillParam
     const size_t orow = (size_t)(start + row / G) * Hq + g * G + row % G;
     const float* slot0 = p.slots + (size_t)(t16 + (int64_t)rb16 * (H * C) + g * C) * SLOT;
     const float lse = PFX ? p.res_lse[orow] : -INFINITY;
+    float acc[EPT];
+    f32x4_t so[EPT / 4];
+#pragma unroll
+    for (int i = 0; i < EPT; i += 4) {
+        so[i / 4] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if constexpr (PFX) so[i / 4] = *reinterpret_cast<const f32x4_t*>(p.res_o + orow * D + e0 + i);
+    }
+    constexpr int kPre = 8;
+    if (C <= kPre) {
+        // Every load of up to kPre chunks in one memory round (past the
+        // last chunk: the last again, with weight zero), then the maximum,
+        // the weights and the sums in chunk order.
+        float mc[kPre], lc[kPre];
+        f32x4_t ac[kPre][EPT / 4];
+#pragma unroll
+        for (int cc = 0; cc < kPre; ++cc) {
+            const float* sl = slot0 + (size_t)min(cc, C - 1) * SLOT;
+            mc[cc] = sl[16 * D + r];
+            lc[cc] = sl[16 * D + 16 + r];
+#pragma unroll
+            for (int i = 0; i < EPT; i += 4) ac[cc][i / 4] = *reinterpret_cast<const f32x4_t*>(sl + r * D + e0 + i);
+        }
+        float M = lse;
+#pragma unroll
+        for (int cc = 0; cc < kPre; ++cc)
+            if (cc < C) M = fmaxf(M, mc[cc]);
+        const float ws = PFX ? __builtin_amdgcn_exp2f(lse - M) : 0.f;
+        float L = ws;
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) acc[i] = ws * so[i / 4][i % 4];
+#pragma unroll
+        for (int cc = 0; cc < kPre; ++cc) {
+            // a chunk where the row saw no key holds m = -inf, l = 0 and zeros
+            const float w = cc >= C || mc[cc] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc[cc] - M);
+            L += w * lc[cc];
+#pragma unroll
+            for (int i = 0; i < EPT; ++i) acc[i] = fmaf(w, ac[cc][i / 4][i % 4], acc[i]);
+        }
+        const float sc = p.v_scale / L;
+#pragma unroll
+        for (int i = 0; i < EPT; i += 4)
+            store4_as<QT>(p.out, orow * D + e0 + i, acc[i] * sc, acc[i + 1] * sc, acc[i + 2] * sc,
+                          acc[i + 3] * sc);
+        return;
+    }
     float M = lse;
     // eight chunks' loads in flight at a time (a loop that is not unrolled
     // waits for each load before issuing the next)
@@ -1142,14 +1187,8 @@ __global__ __launch_bounds__(kMergeThreads) void chunk_merge_kernel(PrefillParam
     for (int cc = 0; cc < C; ++cc) M = fmaxf(M, slot0[(size_t)cc * SLOT + 16 * D + r]);
     const float ws = PFX ? __builtin_amdgcn_exp2f(lse - M) : 0.f;
     float L = ws;
-    float acc[EPT];
 #pragma unroll
-    for (int i = 0; i < EPT; i += 4) {
-        f32x4_t so = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (PFX) so = *reinterpret_cast<const f32x4_t*>(p.res_o + orow * D + e0 + i);
-#pragma unroll
-        for (int x = 0; x < 4; ++x) acc[i + x] = ws * so[x];
-    }
+    for (int i = 0; i < EPT; ++i) acc[i] = ws * so[i / 4][i % 4];
 #pragma unroll 8
     for (int cc = 0; cc < C; ++cc) {
         const float* sl = slot0 + (size_t)cc * SLOT;
