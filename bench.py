@@ -116,7 +116,7 @@ def kernel_hash(workload: str = None, root: str = None) -> str:
     import hashlib
     import re
     h = hashlib.sha256()
-    files = ["paged_decode.hip", "pkv_tile.h", "pkv_device.h"]
+    files = ["paged_decode.hip", "decode_wave.h", "pkv_tile.h", "pkv_device.h"]
     if workload in (None, "prefix_shared"):
         files.insert(1, "paged_prefill.hip")
     for f in files:

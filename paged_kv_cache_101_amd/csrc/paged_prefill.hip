@@ -45,9 +45,9 @@
 // decode (see the end of this file): a prefix group's member sequences take
 // the place of a chunk's tokens, every row sees every key of its part of the
 // shared prefix, and the result is merged with the suffix pass's.
-#include <mutex>
 #include <type_traits>
 
+#include "decode_wave.h"
 #include "pkv_internal.h"
 #include "pkv_tile.h"
 
@@ -242,9 +242,10 @@ __device__ __forceinline__ int prefix_chunks(int H, int rt_total, int rb_total, 
 // -- one (prefix group, row tile, KV head, chunk of the prefix blocks) per
 // workgroup, every row seeing every key of the chunk, the partial merged with
 // the suffix results.
+// One workgroup's task: task_id in [0, the grid's upper bound on tasks);
+// workgroups past the last task return at once.
 template <int KT, int QT, int D, bool PFX>
-__global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(prefill_waves_per_simd<KT, D>())))
-void paged_prefill_kernel(PrefillParams p) {
+__device__ __forceinline__ void prefill_workgroup(const PrefillParams& p, int task_id) {
     using TM = TileMath<KT, QT, D>;
     constexpr int NK = TM::NK, NV = TM::NV, NVL = TM::NVL, KW = TM::KW, VLW = TM::VLW;
     constexpr int VW = TM::VW;
@@ -296,7 +297,7 @@ void paged_prefill_kernel(PrefillParams p) {
         if (rt_total == 0) return;
         const int cg = prefix_chunks(H, rt_total, rb_total, p.pf_target);
         // the group holding this workgroup (wave-uniform)
-        const int task = blockIdx.x;
+        const int task = task_id;
         int wg_before = 0;
         int64_t t16_before = 0;
         int jj = -1, local = 0;
@@ -348,7 +349,7 @@ void paged_prefill_kernel(PrefillParams p) {
             }
             if (rt_total > 0) cg = prefix_chunks(H, rt_total, rb_total, p.pf_target);
         }
-        const int task = blockIdx.x;
+        const int task = task_id;
         int s = -1, local = 0;
         int before = 0;
         int64_t t16_before = 0;
@@ -1049,6 +1050,12 @@ void paged_prefill_kernel(PrefillParams p) {
     }
 }
 
+template <int KT, int QT, int D, bool PFX>
+__global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(prefill_waves_per_simd<KT, D>())))
+void paged_prefill_kernel(PrefillParams p) {
+    prefill_workgroup<KT, QT, D, PFX>(p, (int)blockIdx.x);
+}
+
 // The merge launch: one workgroup of 256 threads per (16-row block, KV head)
 // of the rows whose keys were split into chunks (prefix groups in the prefix
 // pass, PFX; prefill sequences with few rows otherwise). Thread i takes row
@@ -1304,8 +1311,9 @@ hipError_t launch_paged_prefill(const PrefillArgs& a) {
 // 96 at 256 and 106 at 384.
 constexpr int kPrefixBesideTarget = 128;
 
-template <int KT, int QT, int D>
-static hipError_t launch_prefix_typed(const DecodeArgs& a, bool beside, hipStream_t stream) {
+// The prefix pass's parameters (beside: running beside the suffix pass).
+template <int KT, int D>
+static PrefillParams prefix_params(const DecodeArgs& a, bool beside) {
     PrefillParams p{};
     p.q = static_cast<const uint8_t*>(a.q);
     p.k_cache = static_cast<const uint8_t*>(a.k_cache);
@@ -1329,10 +1337,83 @@ static hipError_t launch_prefix_typed(const DecodeArgs& a, bool beside, hipStrea
     p.all_slots = beside ? 1 : 0;
     p.pf_target = beside ? kPrefixBesideTarget : kPrefixTargetWorkgroups;
     p.offsets32 = tile_offsets_fit_32<KT, D>(a.num_blocks, a.num_kv_heads);
+    return p;
+}
+
+template <int KT, int QT, int D>
+static hipError_t launch_prefix_typed(const DecodeArgs& a, bool beside, hipStream_t stream) {
+    const PrefillParams p = prefix_params<KT, D>(a, beside);
     const int64_t grid = prefix_workgroup_bound(a.num_seqs, a.group, a.num_kv_heads, a.num_groups);
     auto kernel = paged_prefill_kernel<KT, QT, D, true>;
     hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kPrefillThreads), 0, stream, p);
     return hipGetLastError();
+}
+
+// ---- the suffix and prefix passes in one launch --------------------------------
+//
+// Workgroups [0, suffix_wgs) run the suffix pass's worker waves, four to a
+// workgroup (decode_wave in result mode), the rest the prefix pass's tasks
+// (prefill_workgroup in prefix mode, partials to slots). The two passes need
+// nothing from each other, so they share the device from the start of the
+// launch, with no second stream and no cross-stream events; the merge
+// launch follows on the same stream. (On a second stream with a fork and a
+// join, the merge started about 6 us after the suffix pass ended, and the
+// suffix pass at times 11-14 us after the prefix pass began.)
+template <int KT, int QT, int D, int GM>
+__global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(prefill_waves_per_simd<KT, D>())))
+void shared_prefix_kernel(DecodeParams dp, PrefillParams pp, int suffix_wgs) {
+    if ((int)blockIdx.x < suffix_wgs)
+        decode_wave<KT, QT, D, GM, true, false>(
+            dp, __builtin_amdgcn_readfirstlane((int)blockIdx.x * kPrefillWaves + wave_id()));
+    else
+        prefill_workgroup<KT, QT, D, true>(pp, (int)blockIdx.x - suffix_wgs);
+}
+
+template <int KT, int QT, int D, int GM>
+static hipError_t launch_fused_typed(const DecodeArgs& a) {
+    // the suffix pass's worker waves: as the decode launch would take them
+    int nw = a.num_workers;
+    if (nw == 0) {
+        const int cus = device_cus();
+        if (cus <= 0) return hipErrorInvalidDevice;
+        nw = decode_waves_per_cu<KT, D, true>() * cus;
+        if (nw > kMaxWorkers) nw = kMaxWorkers;
+    }
+    const int64_t unit_bound = (int64_t)a.num_seqs * a.num_kv_heads * a.max_blocks_per_seq;
+    if (nw > unit_bound) nw = (int)unit_bound;
+    if (nw < 1) nw = 1;
+    const DecodeParams dp = decode_params<KT>(a, nw, 1, false, true);
+    const PrefillParams pp = prefix_params<KT, D>(a, true);
+    const int suffix_wgs = (nw + kPrefillWaves - 1) / kPrefillWaves;
+    const int64_t grid =
+        suffix_wgs + prefix_workgroup_bound(a.num_seqs, a.group, a.num_kv_heads, a.num_groups);
+    hipLaunchKernelGGL((shared_prefix_kernel<KT, QT, D, GM>), dim3((unsigned)grid), dim3(kPrefillThreads),
+                       0, a.stream, dp, pp, suffix_wgs);
+    return hipGetLastError();
+}
+
+template <int KT, int QT, int D>
+static hipError_t launch_fused_group(const DecodeArgs& a) {
+    switch (padded_group(a.group)) {
+    case 1: return launch_fused_typed<KT, QT, D, 1>(a);
+    case 2: return launch_fused_typed<KT, QT, D, 2>(a);
+    case 4: return launch_fused_typed<KT, QT, D, 4>(a);
+    case 6: return launch_fused_typed<KT, QT, D, 6>(a);
+    default: return launch_fused_typed<KT, QT, D, 8>(a);
+    }
+}
+
+template <int KT, int QT>
+static hipError_t launch_fused_dim(const DecodeArgs& a) {
+    return a.head_dim == 64 ? launch_fused_group<KT, QT, 64>(a) : launch_fused_group<KT, QT, 128>(a);
+}
+
+static hipError_t launch_fused(const DecodeArgs& a) {
+    if (a.kv_dtype == PKV_F32) return launch_fused_dim<PKV_F32, PKV_F32>(a);
+    if (a.kv_dtype == PKV_F16) return launch_fused_dim<PKV_F16, PKV_F16>(a);
+    if (a.kv_dtype == PKV_BF16) return launch_fused_dim<PKV_BF16, PKV_BF16>(a);
+    if (a.q_dtype == PKV_F16) return launch_fused_dim<PKV_FP8_E4M3, PKV_F16>(a);
+    return launch_fused_dim<PKV_FP8_E4M3, PKV_BF16>(a);
 }
 
 template <int QT, int D>
@@ -1382,56 +1463,22 @@ static hipError_t prefix_merge(const DecodeArgs& a, bool beside) {
     return d64 ? launch_prefix_merge<PKV_BF16, 64>(a, beside) : launch_prefix_merge<PKV_BF16, 128>(a, beside);
 }
 
-// A second stream per device on which the prefix pass runs beside the suffix
-// pass, with the events that fork it from and join it back to the caller's
-// stream (created on the first call on the device; default priority). Each
-// call records, waits and launches under the device's lock, so calls from
-// several host threads cannot interleave their fork and join.
-struct SideStream {
-    std::mutex mu;
-    bool tried = false;
-    bool ok = false;
-    hipStream_t stream = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
-};
-constexpr int kMaxSideDevices = 64;
-static SideStream g_side[kMaxSideDevices];
-
 hipError_t launch_shared_prefix(const DecodeArgs& a) {
     // The prefix pass can run beside the suffix pass when it needs none of
     // the suffix results, i.e. when every 16-row block of every group can
-    // leave its partial in a slot for the merge launch.
+    // leave its partial in a slot for the merge launch: then both passes are
+    // one launch, and the merge follows.
     const bool fits = (int64_t)a.num_kv_heads *
                           prefix_row_blocks_bound(a.num_seqs, a.group, a.num_groups) <=
                       kPrefixSlots;
-    int dev = -1;
-    SideStream* side = nullptr;
-    if (fits && hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxSideDevices)
-        side = &g_side[dev];
-    if (side != nullptr) {
-        std::lock_guard<std::mutex> lock(side->mu);
-        if (!side->tried) {
-            side->tried = true;
-            side->ok = hipStreamCreateWithFlags(&side->stream, hipStreamNonBlocking) == hipSuccess &&
-                       hipEventCreateWithFlags(&side->fork, hipEventDisableTiming) == hipSuccess &&
-                       hipEventCreateWithFlags(&side->join, hipEventDisableTiming) == hipSuccess;
-        }
-        if (side->ok) {
-            // fork: the side stream starts after the caller's earlier work
-            hipError_t err = hipEventRecord(side->fork, a.stream);
-            if (err == hipSuccess) err = hipStreamWaitEvent(side->stream, side->fork, 0);
-            if (err == hipSuccess) err = prefix_pass(a, true, side->stream);
-            if (err == hipSuccess) err = hipEventRecord(side->join, side->stream);
-            // the suffix pass on the caller's stream, meanwhile
-            if (err == hipSuccess) err = launch_paged_decode(a);
-            // join, then merge both passes' results
-            if (err == hipSuccess) err = hipStreamWaitEvent(a.stream, side->join, 0);
-            if (err == hipSuccess) err = prefix_merge(a, true);
-            return err;
-        }
+    if (fits) {
+        hipError_t err = launch_fused(a);
+        if (err == hipSuccess) err = prefix_merge(a, true);
+        return err;
     }
-    // one stream: the suffix pass, then the prefix pass (which merges
-    // one-chunk groups with the suffix results itself), then the merge
+    // otherwise one after the other: the suffix pass, then the prefix pass
+    // (which merges one-chunk groups with the suffix results itself), then
+    // the merge
     hipError_t err = launch_paged_decode(a);
     if (err == hipSuccess) err = prefix_pass(a, false, a.stream);
     if (err == hipSuccess) err = prefix_merge(a, false);
