@@ -22,9 +22,8 @@
  *  - All buffers are caller-owned, contiguous, row-major device memory
  *    unless a parameter says "host". The library allocates no memory and
  *    keeps no state between calls beyond what it sets up once per device
- *    (the compute-unit count, each decode kernel's occupancy, and for the
- *    shared-prefix decode a second stream with two events), and is safe to
- *    call from several host threads.
+ *    (the compute-unit count and each decode kernel's occupancy), and is
+ *    safe to call from several host threads.
  *  - Work is enqueued on the given HIP stream (NULL = the null stream) and
  *    never synchronised: results are visible after the stream reaches the
  *    point of the call. No call issues a memset, a copy or a host
@@ -322,10 +321,8 @@ size_t pkv_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  * the prefix into chunks when there are few rows. When every 16-row block of
  * the batch can hold a partial slot (num_kv_heads * (ceil(num_seqs * G / 16)
  * + num_groups) <= 4096), the prefix pass leaves all its partials in the
- * workspace and runs beside the suffix pass: on a second stream the library
- * keeps per device (default priority, created on the first such call),
- * forked from and joined back to `stream` with events, which a graph capture
- * of `stream` records as well. Otherwise it runs after the suffix pass on
+ * workspace and runs beside the suffix pass: one launch on `stream` whose
+ * workgroups take either pass. Otherwise it runs after the suffix pass on
  * `stream`, merging one-chunk groups with their suffix results itself. The
  * merge launch on `stream` then combines the chunk partials with the suffix
  * results by the log-sum-exp rule into out.
