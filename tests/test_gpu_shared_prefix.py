@@ -84,9 +84,10 @@ def test_prefix_workload_reduced(gpu):
 
 
 def test_one_chunk_merge_path(gpu):
-    """A large group (300 members x 8 heads per KV head, split into chunks that
-    the merge launch combines) beside a P = 1 group, which cannot be split and
-    is merged from registers by the prefix kernel."""
+    """A large group (300 members x 8 heads per KV head, split into chunks)
+    beside a P = 1 group, which cannot be split. The batch's row blocks fit the
+    partial slots, so both passes share one launch and the merge launch
+    combines the chunk partials of both groups with their suffix results."""
     rng = np.random.default_rng(54)
     groups = [(0, 300, 3), (300, 310, 1)]
     ctx = grouped_lengths(rng, 310, groups, 1, 40)
@@ -98,8 +99,9 @@ def test_one_chunk_merge_path(gpu):
 
 def test_no_group_is_chunked(gpu):
     """1024 members x 8 heads per KV head fill 64 row tiles per head, 512
-    workgroups at one chunk each: every row is merged from registers and the
-    merge launch has nothing to do."""
+    workgroups at one chunk each. The row blocks exceed the partial slots, so
+    the passes run one after the other: every row is merged from registers by
+    the prefix pass and the merge launch has nothing to do."""
     rng = np.random.default_rng(57)
     groups = [(0, 1024, 2)]
     ctx = grouped_lengths(rng, 1024, groups, 1, 24)
