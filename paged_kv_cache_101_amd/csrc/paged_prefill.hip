@@ -242,10 +242,30 @@ __device__ __forceinline__ int prefix_chunks(int H, int rt_total, int rb_total, 
 // -- one (prefix group, row tile, KV head, chunk of the prefix blocks) per
 // workgroup, every row seeing every key of the chunk, the partial merged with
 // the suffix results.
-// One workgroup's task: task_id in [0, the grid's upper bound on tasks);
+// One workgroup per task: task in [0, the grid's upper bound on tasks);
 // workgroups past the last task return at once.
-template <int KT, int QT, int D, bool PFX>
-__device__ __forceinline__ void prefill_workgroup(const PrefillParams& p, int task_id) {
+// FGM > 0 (prefix mode only): the shared-prefix call's single launch for both
+// passes. Workgroups [0, suffix_wgs) run the suffix pass's worker waves, four
+// to a workgroup (decode_wave in result mode, query heads padded to FGM), the
+// rest the prefix pass's tasks (partials to slots). The two passes need
+// nothing from each other, so they share the device from the start of the
+// launch, with no second stream and no cross-stream events; the merge launch
+// follows on the same stream. (On a second stream with a fork and a join, the
+// merge started about 6 us after the suffix pass ended, and the suffix pass
+// at times 11-14 us after the prefix pass began.)
+template <int KT, int QT, int D, bool PFX, int FGM>
+__global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(prefill_waves_per_simd<KT, D>())))
+void paged_prefill_kernel(PrefillParams p, DecodeParams dp, int suffix_wgs) {
+    static_assert(FGM == 0 || PFX, "only the prefix pass shares a launch");
+    int task_id = (int)blockIdx.x;
+    if constexpr (FGM > 0) {
+        if (task_id < suffix_wgs) {
+            decode_wave<KT, QT, D, FGM, true, false>(
+                dp, __builtin_amdgcn_readfirstlane(task_id * kPrefillWaves + wave_id()));
+            return;
+        }
+        task_id -= suffix_wgs;
+    }
     using TM = TileMath<KT, QT, D>;
     constexpr int NK = TM::NK, NV = TM::NV, NVL = TM::NVL, KW = TM::KW, VLW = TM::VLW;
     constexpr int VW = TM::VW;
@@ -1050,12 +1070,6 @@ __device__ __forceinline__ void prefill_workgroup(const PrefillParams& p, int ta
     }
 }
 
-template <int KT, int QT, int D, bool PFX>
-__global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(prefill_waves_per_simd<KT, D>())))
-void paged_prefill_kernel(PrefillParams p) {
-    prefill_workgroup<KT, QT, D, PFX>(p, (int)blockIdx.x);
-}
-
 // The merge launch: one workgroup of 256 threads per (16-row block, KV head)
 // of the rows whose keys were split into chunks (prefix groups in the prefix
 // pass, PFX; prefill sequences with few rows otherwise). Thread i takes row
@@ -1263,8 +1277,8 @@ static hipError_t launch_prefill_typed(const PrefillArgs& a) {
     const int64_t grid = prefill_task_bound(a.num_seqs, a.num_tokens, a.group, a.num_kv_heads) +
                          (may_split ? kPrefixTargetWorkgroups : 0);
     if (grid <= 0) return hipSuccess;
-    auto kernel = paged_prefill_kernel<KT, QT, D, false>;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kPrefillThreads), 0, a.stream, p);
+    auto kernel = paged_prefill_kernel<KT, QT, D, false, 0>;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kPrefillThreads), 0, a.stream, p, DecodeParams{}, 0);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || !may_split) return err;
     // the merge of split sequences (16-row blocks: at most T * G / 16 + S per KV head)
@@ -1344,30 +1358,12 @@ template <int KT, int QT, int D>
 static hipError_t launch_prefix_typed(const DecodeArgs& a, bool beside, hipStream_t stream) {
     const PrefillParams p = prefix_params<KT, D>(a, beside);
     const int64_t grid = prefix_workgroup_bound(a.num_seqs, a.group, a.num_kv_heads, a.num_groups);
-    auto kernel = paged_prefill_kernel<KT, QT, D, true>;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kPrefillThreads), 0, stream, p);
+    auto kernel = paged_prefill_kernel<KT, QT, D, true, 0>;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kPrefillThreads), 0, stream, p, DecodeParams{}, 0);
     return hipGetLastError();
 }
 
-// ---- the suffix and prefix passes in one launch --------------------------------
-//
-// Workgroups [0, suffix_wgs) run the suffix pass's worker waves, four to a
-// workgroup (decode_wave in result mode), the rest the prefix pass's tasks
-// (prefill_workgroup in prefix mode, partials to slots). The two passes need
-// nothing from each other, so they share the device from the start of the
-// launch, with no second stream and no cross-stream events; the merge
-// launch follows on the same stream. (On a second stream with a fork and a
-// join, the merge started about 6 us after the suffix pass ended, and the
-// suffix pass at times 11-14 us after the prefix pass began.)
-template <int KT, int QT, int D, int GM>
-__global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(prefill_waves_per_simd<KT, D>())))
-void shared_prefix_kernel(DecodeParams dp, PrefillParams pp, int suffix_wgs) {
-    if ((int)blockIdx.x < suffix_wgs)
-        decode_wave<KT, QT, D, GM, true, false>(
-            dp, __builtin_amdgcn_readfirstlane((int)blockIdx.x * kPrefillWaves + wave_id()));
-    else
-        prefill_workgroup<KT, QT, D, true>(pp, (int)blockIdx.x - suffix_wgs);
-}
+// ---- the suffix and prefix passes in one launch (paged_prefill_kernel, FGM > 0) ----
 
 template <int KT, int QT, int D, int GM>
 static hipError_t launch_fused_typed(const DecodeArgs& a) {
@@ -1387,8 +1383,8 @@ static hipError_t launch_fused_typed(const DecodeArgs& a) {
     const int suffix_wgs = (nw + kPrefillWaves - 1) / kPrefillWaves;
     const int64_t grid =
         suffix_wgs + prefix_workgroup_bound(a.num_seqs, a.group, a.num_kv_heads, a.num_groups);
-    hipLaunchKernelGGL((shared_prefix_kernel<KT, QT, D, GM>), dim3((unsigned)grid), dim3(kPrefillThreads),
-                       0, a.stream, dp, pp, suffix_wgs);
+    hipLaunchKernelGGL((paged_prefill_kernel<KT, QT, D, true, GM>), dim3((unsigned)grid),
+                       dim3(kPrefillThreads), 0, a.stream, pp, dp, suffix_wgs);
     return hipGetLastError();
 }
 
