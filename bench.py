@@ -618,8 +618,8 @@ def main():
     achieved = kv_bytes_launch / (decode_avg_ms * 1e-3) / 1e9
     traffic = load_traffic(args.workload if args.partition_size == 0 else
                            f"{args.workload}_p{args.partition_size}")
-    kernel = ("paged_decode_kernel suffix pass + paged_prefill_kernel prefix mode + chunk_merge_kernel "
-              "(pkv_paged_attention_decode_shared_prefix)" if shared else
+    kernel = ("paged_prefill_kernel (suffix-pass and prefix-pass workgroups in one launch) + "
+              "chunk_merge_kernel (pkv_paged_attention_decode_shared_prefix)" if shared else
               "paged_decode_kernel + partition_merge_kernel (pkv_paged_attention_decode, fixed "
               f"{args.partition_size}-token partitions)" if args.partition_size else
               "paged_decode_kernel (one launch per pkv_paged_attention_decode call)")
