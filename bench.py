@@ -106,19 +106,26 @@ def parse():
     return ap.parse_args()
 
 
+PREFILL_WORKLOADS = ("prefill", "prefill_small")
+
+
 def kernel_hash(workload: str = None, root: str = None) -> str:
-    """Hash of the sources of the attention kernels a decode workload
-    launches (the decode kernel and its merge; the shared-prefix call also
-    runs the prefix pass and its merge from paged_prefill.hip), with comments
-    and white space removed: counter figures are valid only for the code they
-    were taken on, and a comment does not change it. workload None: every
-    attention source."""
+    """Hash of the sources of the attention kernels a workload launches (a
+    decode workload: the decode kernel and its merge, and for the
+    shared-prefix call also the prefix pass and its merge from
+    paged_prefill.hip; a prefill workload: paged_prefill.hip with what it
+    includes, and the split's chunk target), with comments and white space
+    removed: counter figures are valid only for the code they were taken on,
+    and a comment does not change it. workload None: every attention source
+    of the decode workloads."""
     import hashlib
     import re
     h = hashlib.sha256()
     files = ["paged_decode.hip", "decode_wave.h", "pkv_tile.h", "pkv_device.h"]
     if workload in (None, "prefix_shared"):
         files.insert(1, "paged_prefill.hip")
+    if workload in PREFILL_WORKLOADS:
+        files = ["paged_prefill.hip", "decode_wave.h", "pkv_tile.h", "pkv_device.h", "pkv_internal.h"]
     for f in files:
         with open(os.path.join(root or ROOT, "paged_kv_cache_101_amd", "csrc", f)) as fh:
             text = fh.read()
@@ -128,10 +135,20 @@ def kernel_hash(workload: str = None, root: str = None) -> str:
     return h.hexdigest()[:16]
 
 
+def counter_file(workload: str) -> str:
+    """The committed counter summary of a workload (decode workloads: the
+    workload's name, with the partition size for fixed partitions)."""
+    if workload == "prefill":
+        return "prefill_step_counters.txt"
+    if workload == "prefill_small":
+        return "prefill_small_counters.txt"
+    return f"decode_{workload}_counters.txt"
+
+
 def load_traffic(workload: str):
-    """HBM traffic per decode launch from the committed counter summary, or
-    None if it was taken on other kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"decode_{workload}_counters.txt")
+    """HBM traffic per call from the committed counter summary, or None if it
+    was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", counter_file(workload))
     if not os.path.exists(path):
         return None
     rec = None
@@ -339,15 +356,19 @@ def bench_prefill(args):
         # below the ridge (few query rows per key): bound by reading the KV once
         gbs = kv_bytes / (avg * 1e-3) / 1e9
         line["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                            "traffic": load_traffic(args.workload),
                             "kernel": "paged_prefill_kernel (split keys) + chunk_merge_kernel",
+                            "algorithmic_bytes_per_launch": kv_bytes,
                             "launch_avg_us": round(avg * 1e3, 2)}
         line["unsplit_avg_us"] = round(timed(None) * 1e3, 2)  # the same call without a workspace
     else:
         line["roofline"] = {"bound": "mfma", "achieved": round(tflops, 1),
                             "peak": MFMA_PEAK_TFLOPS[dt], "unit": "TFLOP/s",
-                            "frac": round(tflops / MFMA_PEAK_TFLOPS[dt], 4), "traffic": None,
+                            "frac": round(tflops / MFMA_PEAK_TFLOPS[dt], 4),
+                            "traffic": load_traffic(args.workload),
                             "kernel": "paged_prefill_kernel (one launch per call)",
+                            "algorithmic_bytes_per_launch": kv_bytes,
                             "launch_avg_us": round(avg * 1e3, 2)}
     print(json.dumps(line), flush=True)
 
