@@ -559,6 +559,7 @@ class DecodeRun:
         cavg = statistics.fmean(cms)
         nb = self.kv_bytes_per_launch()
         return {"launch_avg_us": round(cavg * 1e3, 2),
+                "launch_median_us": round(statistics.median(cms) * 1e3, 2),
                 "launch_p10_us": round(cms[len(cms) // 10] * 1e3, 2),
                 "launch_p90_us": round(cms[(9 * len(cms)) // 10] * 1e3, 2),
                 "achieved_gbps": round(nb / (cavg * 1e-3) / 1e9, 1),
@@ -583,6 +584,7 @@ def summary(workload: str, dev, steps: int, warmup: int, partition_sizes=(0,),
         nb = run.kv_bytes_per_launch()
         b0 = run.layers[0]
         rec = {"decode_avg_us": round(t["decode_avg_ms"] * 1e3, 2),
+               "decode_median_us": round(statistics.median(t["decode_ms"]) * 1e3, 2),
                "decode_p10_us": round(t["decode_ms"][len(t["decode_ms"]) // 10] * 1e3, 2),
                "decode_p90_us": round(t["decode_ms"][(9 * len(t["decode_ms"])) // 10] * 1e3, 2),
                "achieved_gbps": round(nb / (t["decode_avg_ms"] * 1e-3) / 1e9, 1),
@@ -649,6 +651,7 @@ def main():
         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
         "algorithmic_bytes_per_launch": kv_bytes_launch,
         "launch_avg_us": round(decode_avg_ms * 1e3, 2),
+        "launch_median_us": round(statistics.median(decode_ms) * 1e3, 2),
         "launch_p10_us": round(decode_ms[len(decode_ms) // 10] * 1e3, 2),
         "launch_p90_us": round(decode_ms[(9 * len(decode_ms)) // 10] * 1e3, 2),
     }
