@@ -387,3 +387,51 @@ def test_binding_gather_and_copy_reject_mismatch():
     with pytest.raises(ValueError, match="pool needs"):
         B.pkv_copy_blocks(kc, kc.clone(), B.cache_desc(32, 2, 64, "f32"),
                           torch.zeros((1, 2), dtype=torch.int32))
+
+
+C_CALLER = r"""
+#include "pkv.h"
+#include "pkv_blocks.h"
+#include <stdio.h>
+
+int main(void) {
+    /* sizing and the block manager run on the host */
+    size_t ws = pkv_decode_workspace_bytes(40, 32, 8, 128, 512, 0, 0);
+    size_t kv = pkv_kv_bytes_per_token(40, 8, 128, PKV_F16);
+    pkv_block_manager *bm = pkv_bm_create(64, 1);
+    if (bm == NULL) return 2;
+    int64_t prompt[20];
+    for (int i = 0; i < 20; ++i) prompt[i] = 100 + i;
+    int32_t cached = -1, ncopies = -1, copies[1][2];
+    int64_t slots[20];
+    int rc = pkv_bm_add_request(bm, 7, prompt, 20, 0, &cached);
+    rc |= pkv_bm_append(bm, 7, 20, NULL, slots, copies, &ncopies);
+    int32_t nblocks = pkv_bm_num_blocks(bm, 7), free_blocks = pkv_bm_num_free_blocks(bm);
+    pkv_bm_destroy(bm);
+    printf("%zu %zu %d %d %d %d %d\n", ws, kv, rc, cached, ncopies, nblocks, free_blocks);
+    return 0;
+}
+"""
+
+
+def test_headers_serve_a_plain_c_caller(tmp_path):
+    """include/pkv.h and include/pkv_blocks.h compile as strict C99 (no HIP
+    header needed), and a C program links libpkv.so and calls its host
+    entry points."""
+    import shutil
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    B.lib()  # raises if the library has not been built
+    src, exe = tmp_path / "caller.c", tmp_path / "caller"
+    src.write_text(C_CALLER)
+    libdir = os.path.dirname(B.LIB_PATH)
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                    f"-I{os.path.join(ROOT, 'include')}", str(src), f"-L{libdir}", "-lpkv",
+                    f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()
+    ws, kv, rc, cached, ncopies, nblocks, free_blocks = map(int, out)
+    assert ws == B.pkv_decode_workspace_bytes(40, 32, 8, 128, 512, 0, 0)
+    assert kv == 40 * 2 * 8 * 128 * 2  # the pages' per-token formula, 40 layers, fp16
+    assert (rc, cached, ncopies, nblocks) == (0, 0, 0, 2)
+    assert free_blocks == 63 - 2
