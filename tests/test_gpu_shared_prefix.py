@@ -112,14 +112,13 @@ def test_no_group_is_chunked(gpu):
 
 
 def test_prefix_workload_full_size(gpu):
-    """The 256 x (2048 shared + 64..512) workload: sampled sequences against
-    the oracle, every row against plain decode."""
+    """The 256 x (2048 shared + 64..512) workload as the benchmark runs it:
+    every sequence against the oracle, and every row against plain decode."""
     b = W.prefix_shared(device=gpu, canary=True)
     got = gpu_shared_decode(b)
     plain = gpu_decode(b)
     torch.cuda.synchronize()
-    seqs = np.array([0, 1, 77, 128, 200, 255])
-    assert_close(out_to_f64(got)[seqs], oracle_decode(b, seqs=seqs), "bf16", "full size, sampled")
+    assert_close(out_to_f64(got), oracle_decode(b), "bf16", "full size")
     assert_close(out_to_f64(got), out_to_f64(plain), "bf16", "full size vs plain decode")
 
 
