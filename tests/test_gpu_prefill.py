@@ -263,3 +263,49 @@ def test_random_shapes_match_oracle(gpu, seed):
     got = out_to_f64(gpu_prefill(b, q, qs, workspace=ws))
     e = assert_close(got, oracle_rows(b, q, qs), kv, what)
     print(f"[parity] {what}: {e}", flush=True)
+
+
+def _bench_batch(gpu, small):
+    """A prefill workload of the benchmark, built as bench.py builds it (same
+    batch seeds, query seed, chunking and head shape)."""
+    import bench
+    contexts = bench.PREFILL_SMALL_CONTEXTS if small else bench.PREFILL_CONTEXTS
+    chunk = bench.PREFILL_SMALL_CHUNK if small else bench.PREFILL_CHUNK
+    b = W.make_batch("prefill-small" if small else "prefill-step", 8 if small else 6, contexts,
+                     32, 8, 128, "f16", "f16", device=gpu)
+    T = len(contexts) * chunk
+    g = torch.Generator(device=gpu)
+    g.manual_seed(66)
+    q = torch.randn((T, 32, 128), generator=g, device=gpu).to(torch.float16)
+    qs = torch.arange(0, T + 1, chunk, dtype=torch.int32, device=gpu)
+    return b, q, qs, chunk
+
+
+def test_bench_prefill_step_sampled(gpu):
+    """The benchmark's chunked-prefill step (four 2048-token chunks at
+    contexts 2048..8192, 32/8 heads, d 128, fp16) with its workspace, as timed:
+    sampled rows of every chunk (its first and last rows, row-tile edges and
+    random ones) against the oracle."""
+    b, q, qs, chunk = _bench_batch(gpu, small=False)
+    got = out_to_f64(gpu_prefill(b, q, qs, workspace=B.prefill_workspace(128, gpu)))
+    rng = np.random.default_rng(66)
+    num_chunks = b.context_lens.numel()
+    assert num_chunks == 4
+    rows = []
+    for c in range(num_chunks):
+        base = c * chunk
+        rows += [base + r for r in (0, 1, 31, 32, 127, 128, 1023, chunk - 2, chunk - 1)]
+        rows += list(base + rng.integers(0, chunk, 8))
+    rows = np.unique(np.asarray(rows))
+    assert_close(got[rows], oracle_rows(b, q, qs, rows), "f16", "bench prefill step, sampled rows")
+
+
+def test_bench_prefill_small_every_row(gpu):
+    """The benchmark's few-row prefill (eight 16-token chunks at context 8192)
+    with its workspace (split keys): every row against the oracle, and the
+    unsplit call agrees to rounding."""
+    b, q, qs, _ = _bench_batch(gpu, small=True)
+    got = out_to_f64(gpu_prefill(b, q, qs, workspace=B.prefill_workspace(128, gpu)))
+    assert_close(got, oracle_rows(b, q, qs), "f16", "bench few-row prefill, every row")
+    unsplit = out_to_f64(gpu_prefill(b, q, qs))
+    assert np.abs(unsplit - got).max() <= 2e-3
